@@ -1,0 +1,173 @@
+"""Thin Python entry points with the C ABI's names.
+
+Argument marshalling only: every step of the layer runs in libzgattn's HIP kernels.
+PyTorch supplies device memory (``tensor.data_ptr()``) and the stream
+(``torch.cuda.current_stream()``); outputs are allocated with ``torch.empty`` when the
+caller passes none.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional
+
+import torch
+
+from ._lib import BF16, F32, Desc, check, lib
+
+
+def rotary_dim_for(head_dim: int, ratio: float = 0.33) -> int:
+    """The largest even number of dims not above ``ratio * head_dim`` (42 for 128, 20 for 64)."""
+    return 2 * int(math.floor(ratio * head_dim / 2.0))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def make_desc(*, batch, seq_len, n_q_heads, n_kv_heads, head_dim, window=128,
+              rotary_dim=None, pos_offset=0, rope_base=10000.0, rms_eps=1e-6,
+              softmax_scale=0.0, dtype=BF16) -> Desc:
+    return Desc(batch, seq_len, n_q_heads, n_kv_heads, head_dim, window,
+                rotary_dim_for(head_dim) if rotary_dim is None else rotary_dim,
+                pos_offset, rope_base, rms_eps, softmax_scale, dtype)
+
+
+def _prefill_desc(q, k, window, rotary_dim, pos_offset, rope_base, eps, scale):
+    B, T, Hq, d = q.shape
+    return make_desc(batch=B, seq_len=T, n_q_heads=Hq, n_kv_heads=k.shape[2], head_dim=d,
+                     window=window, rotary_dim=rotary_dim, pos_offset=pos_offset,
+                     rope_base=rope_base, rms_eps=eps, softmax_scale=scale,
+                     dtype=_dtype_code(q))
+
+
+def swa_prefill(q, k, v, g, wq, wk, *, window=128, rotary_dim=None, pos_offset=0,
+                rope_base=10000.0, eps=1e-6, scale=0.0, out=None):
+    """Gated sliding-window layer: [B,T,Hq,d] output of softmax-window attention * sigmoid(g)."""
+    _dev(q, k, v, g, wq, wk, out)
+    if out is None:
+        out = torch.empty_like(q)
+    d = _prefill_desc(q, k, window, rotary_dim, pos_offset, rope_base, eps, scale)
+    check(lib().zgattn_swa_prefill(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                   _ptr(wq), _ptr(wk), _ptr(out), _stream()),
+          "zgattn_swa_prefill")
+    return out
+
+
+def global_prefill_workspace_bytes(q, k, rotary_dim=None) -> int:
+    d = _prefill_desc(q, k, 1, rotary_dim, 0, 10000.0, 1e-6, 0.0)
+    return int(lib().zgattn_global_prefill_workspace_bytes(ctypes.byref(d)))
+
+
+def global_prefill(q, k, v, wq, wk, *, rotary_dim=None, pos_offset=0, rope_base=10000.0,
+                   eps=1e-6, scale=0.0, workspace="auto", out=None):
+    """Ungated full-causal layer. ``workspace``: "auto" allocates the K~ buffer, None runs
+    the fused-K variant, or a caller-owned uint8 CUDA tensor."""
+    _dev(q, k, v, wq, wk, out)
+    if out is None:
+        out = torch.empty_like(q)
+    d = _prefill_desc(q, k, 1, rotary_dim, pos_offset, rope_base, eps, scale)
+    ws_bytes = int(lib().zgattn_global_prefill_workspace_bytes(ctypes.byref(d)))
+    if isinstance(workspace, str):
+        workspace = (torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+                     if ws_bytes > 0 else None)
+    ws_ptr = _ptr(workspace)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(lib().zgattn_global_prefill(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(wq),
+                                      _ptr(wk), ws_ptr, nbytes, _ptr(out), _stream()),
+          "zgattn_global_prefill")
+    return out
+
+
+def _decode_desc(q, k_new, window, rotary_dim, rope_base, eps, scale):
+    B, Hq, dd = q.shape
+    return make_desc(batch=B, seq_len=1, n_q_heads=Hq, n_kv_heads=k_new.shape[1],
+                     head_dim=dd, window=window, rotary_dim=rotary_dim, rope_base=rope_base,
+                     rms_eps=eps, softmax_scale=scale, dtype=_dtype_code(q))
+
+
+def swa_decode(q, k_new, v_new, g, wq, wk, k_ring, v_ring, pos, *, rotary_dim=None,
+               rope_base=10000.0, eps=1e-6, scale=0.0, out=None):
+    """One gated-SWA decode step; the ring size is the window. Updates the ring in place."""
+    _dev(q, k_new, v_new, g, wq, wk, k_ring, v_ring, pos, out)
+    if pos.dtype != torch.int32:
+        raise TypeError("pos must be int32")
+    if out is None:
+        out = torch.empty_like(q)
+    d = _decode_desc(q, k_new, k_ring.shape[2], rotary_dim, rope_base, eps, scale)
+    check(lib().zgattn_swa_decode(ctypes.byref(d), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(g),
+                                  _ptr(wq), _ptr(wk), _ptr(k_ring), _ptr(v_ring), _ptr(pos),
+                                  _ptr(out), _stream()),
+          "zgattn_swa_decode")
+    return out
+
+
+def global_decode_workspace_bytes(q, k_new, capacity: int) -> int:
+    d = _decode_desc(q, k_new, 1, None, 10000.0, 1e-6, 0.0)
+    return int(lib().zgattn_global_decode_workspace_bytes(ctypes.byref(d), capacity))
+
+
+def global_decode(q, k_new, v_new, wq, wk, k_cache, v_cache, pos, *, rotary_dim=None,
+                  rope_base=10000.0, eps=1e-6, scale=0.0, workspace=None, out=None):
+    """One global-layer decode step over a full cache; appends the new token in place."""
+    _dev(q, k_new, v_new, wq, wk, k_cache, v_cache, pos, out)
+    if pos.dtype != torch.int32:
+        raise TypeError("pos must be int32")
+    if out is None:
+        out = torch.empty_like(q)
+    cap = k_cache.shape[2]
+    d = _decode_desc(q, k_new, 1, rotary_dim, rope_base, eps, scale)
+    need = int(lib().zgattn_global_decode_workspace_bytes(ctypes.byref(d), cap))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    check(lib().zgattn_global_decode(ctypes.byref(d), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                     _ptr(wq), _ptr(wk), _ptr(k_cache), _ptr(v_cache), cap,
+                                     _ptr(pos), _ptr(workspace), nbytes, _ptr(out), _stream()),
+          "zgattn_global_decode")
+    return out
+
+
+def qknorm_rope(x, w, *, pos=None, rotary_dim=None, pos_offset=0, rope_base=10000.0,
+                eps=1e-6, out=None):
+    """RMSNorm + partial RoPE of x [B,T,H,d]. ``out`` may be any strided view with the
+    same logical shape (e.g. ``cache.permute(0, 2, 1, 3)[:, :T]``) whose last dim is dense."""
+    _dev(x, w, pos)
+    B, T, H, dd = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    if out.shape != x.shape or out.stride(3) != 1 or out.dtype != x.dtype or not out.is_cuda:
+        raise ValueError("out must match x's shape/dtype with a dense last dim")
+    if pos is not None and pos.dtype != torch.int32:
+        raise TypeError("pos must be int32")
+    d = make_desc(batch=B, seq_len=T, n_q_heads=H, n_kv_heads=H, head_dim=dd, window=1,
+                  rotary_dim=rotary_dim, pos_offset=pos_offset, rope_base=rope_base,
+                  rms_eps=eps, dtype=_dtype_code(x))
+    sb, st, sh, _ = out.stride()
+    check(lib().zgattn_qknorm_rope(ctypes.byref(d), H, _ptr(x), _ptr(w), _ptr(pos),
+                                   _ptr(out), sb, st, sh, _stream()),
+          "zgattn_qknorm_rope")
+    return out

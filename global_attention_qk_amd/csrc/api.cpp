@@ -1,0 +1,291 @@
+// C ABI of libzgattn: host-side argument checks, RoPE frequency tables and launches.
+// Every check happens before anything is launched; see include/zgattn.h for the contract.
+#include "zgattn.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+using namespace zg;
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_desc(const zgattn_desc* d) {
+  if (!d) return ZGATTN_ENULL;
+  if (d->dtype != ZGATTN_F32 && d->dtype != ZGATTN_BF16) return ZGATTN_EDTYPE;
+  if (d->batch < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1) return ZGATTN_EINVAL;
+  if (d->n_q_heads % d->n_kv_heads != 0) return ZGATTN_EINVAL;
+  if (d->head_dim != 64 && d->head_dim != 128) return ZGATTN_EUNSUPPORTED;
+  if (d->rotary_dim < 0 || d->rotary_dim > d->head_dim || (d->rotary_dim & 1)) return ZGATTN_EINVAL;
+  if (!(d->rope_base > 0.0f) || !isfinite(d->rope_base)) return ZGATTN_EINVAL;
+  if (!(d->rms_eps >= 0.0f) || !isfinite(d->rms_eps)) return ZGATTN_EINVAL;
+  if (!isfinite(d->softmax_scale)) return ZGATTN_EINVAL;
+  if (d->pos_offset < 0 || d->pos_offset > ZGATTN_MAX_POSITION) return ZGATTN_ERANGE;
+  return ZGATTN_OK;
+}
+
+float scale_of(const zgattn_desc* d) {
+  return d->softmax_scale > 0.0f ? d->softmax_scale : (float)(1.0 / sqrt((double)d->head_dim));
+}
+
+// f_k = base^(-2k/r) / (2 pi) revolutions per position, as an fp32 head + tail pair.
+RopeFreq rope_freq(int rdim, float base) {
+  RopeFreq f;
+  for (int k = 0; k < kMaxHalfRot; ++k) {
+    f.hi[k] = 0.0f;
+    f.lo[k] = 0.0f;
+  }
+  const int half = rdim / 2;
+  const long double two_pi = 6.283185307179586476925286766559L;
+  for (int k = 0; k < half; ++k) {
+    const long double v = powl((long double)base, -2.0L * k / rdim) / two_pi;
+    const float h = (float)v;
+    f.hi[k] = h;
+    f.lo[k] = (float)(v - (long double)h);
+  }
+  return f;
+}
+
+int prefill_common(const zgattn_desc* d, const void* q, const void* k, const void* v,
+                   const float* wq, const float* wk, void* out) {
+  int st = check_desc(d);
+  if (st) return st;
+  if (d->seq_len < 0) return ZGATTN_EINVAL;
+  if (d->seq_len > 0 && (int64_t)d->pos_offset + d->seq_len - 1 > ZGATTN_MAX_POSITION)
+    return ZGATTN_ERANGE;
+  if (d->seq_len == 0) return ZGATTN_OK;
+  if (!q || !k || !v || !wq || !wk || !out) return ZGATTN_ENULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ZGATTN_EINVAL;
+  return ZGATTN_OK;
+}
+
+PrefillArgs make_prefill(const zgattn_desc* d, const void* q, const void* k, const void* v,
+                         const void* g, const float* wq, const float* wk, void* out, int swa) {
+  PrefillArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.out = out;
+  a.wq = wq;
+  a.wk = wk;
+  a.kt = nullptr;
+  a.B = d->batch;
+  a.T = d->seq_len;
+  a.Hq = d->n_q_heads;
+  a.Hkv = d->n_kv_heads;
+  a.d = d->head_dim;
+  a.window = d->window;
+  a.rdim = d->rotary_dim;
+  a.pos_offset = d->pos_offset;
+  a.swa = swa;
+  a.eps = d->rms_eps;
+  a.scale = scale_of(d);
+  a.fr = rope_freq(d->rotary_dim, d->rope_base);
+  return a;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? ZGATTN_OK : ZGATTN_EHIP; }
+
+int decode_common(const zgattn_desc* d, const void* q, const void* k_new, const void* v_new,
+                  const float* wq, const float* wk, void* kc, void* vc, const int32_t* pos,
+                  void* out) {
+  int st = check_desc(d);
+  if (st) return st;
+  if (!q || !k_new || !v_new || !wq || !wk || !kc || !vc || !pos || !out) return ZGATTN_ENULL;
+  if (d->dtype != ZGATTN_BF16) return ZGATTN_EUNSUPPORTED;
+  const int G = d->n_q_heads / d->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return ZGATTN_EUNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(kc) ||
+      !aligned16(vc) || !aligned16(out))
+    return ZGATTN_EINVAL;
+  return ZGATTN_OK;
+}
+
+DecodeArgs make_decode(const zgattn_desc* d, const void* q, const void* k_new,
+                       const void* v_new, const void* g, const float* wq, const float* wk,
+                       void* kc, void* vc, const int32_t* pos, void* out) {
+  DecodeArgs a;
+  a.q = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.g = g;
+  a.wq = wq;
+  a.wk = wk;
+  a.k_cache = kc;
+  a.v_cache = vc;
+  a.pos = pos;
+  a.out = out;
+  a.ws = nullptr;
+  a.B = d->batch;
+  a.Hq = d->n_q_heads;
+  a.Hkv = d->n_kv_heads;
+  a.d = d->head_dim;
+  a.S = 0;
+  a.rdim = d->rotary_dim;
+  a.window = d->window;
+  a.nsplit = 0;
+  a.chunk = 0;
+  a.eps = d->rms_eps;
+  a.scale = scale_of(d);
+  a.fr = rope_freq(d->rotary_dim, d->rope_base);
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int zgattn_abi_version(void) { return ZGATTN_ABI_VERSION; }
+
+const char* zgattn_strerror(int status) {
+  switch (status) {
+    case ZGATTN_OK: return "ok";
+    case ZGATTN_EINVAL: return "invalid argument (size, parameter or alignment)";
+    case ZGATTN_ENULL: return "required pointer is NULL";
+    case ZGATTN_EDTYPE: return "unknown dtype";
+    case ZGATTN_EUNSUPPORTED: return "unsupported configuration";
+    case ZGATTN_EWORKSPACE: return "workspace missing or too small";
+    case ZGATTN_ERANGE: return "position or capacity out of range";
+    case ZGATTN_EHIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+int zgattn_swa_prefill(const zgattn_desc* d, const void* q, const void* k, const void* v,
+                       const void* g, const float* wq, const float* wk, void* out,
+                       void* stream) {
+  int st = prefill_common(d, q, k, v, wq, wk, out);
+  if (st) return st;
+  if (d->window < 1) return ZGATTN_EINVAL;
+  if (d->seq_len == 0) return ZGATTN_OK;
+  if (!g) return ZGATTN_ENULL;
+  if (!aligned16(g)) return ZGATTN_EINVAL;
+  PrefillArgs a = make_prefill(d, q, k, v, g, wq, wk, out, 1);
+  hipStream_t s = (hipStream_t)stream;
+  if (d->dtype == ZGATTN_F32) return hip_status(launch_prefill_f32(a, s));
+  if (!prefill_bf16_supported(a.d, a.Hq / a.Hkv, a.rdim)) return ZGATTN_EUNSUPPORTED;
+  return hip_status(launch_prefill_bf16(a, s));
+}
+
+size_t zgattn_global_prefill_workspace_bytes(const zgattn_desc* d) {
+  if (check_desc(d) || d->seq_len < 0) return 0;
+  if (d->dtype != ZGATTN_BF16) return 0;
+  return (size_t)d->batch * d->n_kv_heads * (size_t)d->seq_len * d->head_dim * 2;
+}
+
+int zgattn_global_prefill(const zgattn_desc* d, const void* q, const void* k, const void* v,
+                          const float* wq, const float* wk, void* workspace,
+                          size_t workspace_bytes, void* out, void* stream) {
+  int st = prefill_common(d, q, k, v, wq, wk, out);
+  if (st) return st;
+  if (d->seq_len == 0) return ZGATTN_OK;
+  PrefillArgs a = make_prefill(d, q, k, v, nullptr, wq, wk, out, 0);
+  hipStream_t s = (hipStream_t)stream;
+  if (d->dtype == ZGATTN_F32) return hip_status(launch_prefill_f32(a, s));
+  if (!prefill_bf16_supported(a.d, a.Hq / a.Hkv, a.rdim)) return ZGATTN_EUNSUPPORTED;
+  if (workspace) {
+    if (workspace_bytes < zgattn_global_prefill_workspace_bytes(d) || !aligned16(workspace))
+      return ZGATTN_EWORKSPACE;
+    NormRopeArgs n;
+    n.x = k;
+    n.w = wk;
+    n.pos = nullptr;
+    n.y = workspace;
+    n.B = a.B;
+    n.T = a.T;
+    n.H = a.Hkv;
+    n.d = a.d;
+    n.ysb = (int64_t)a.Hkv * a.T * a.d;  // [B][Hkv][T][d]
+    n.yst = a.d;
+    n.ysh = (int64_t)a.T * a.d;
+    n.rdim = a.rdim;
+    n.pos_offset = a.pos_offset;
+    n.is_bf16 = 1;
+    n.eps = a.eps;
+    n.out_scale = 1.0f;
+    n.fr = a.fr;
+    hipError_t e = launch_qknorm_rope(n, s);
+    if (e != hipSuccess) return ZGATTN_EHIP;
+    a.kt = (bf16*)workspace;
+  }
+  return hip_status(launch_prefill_bf16(a, s));
+}
+
+int zgattn_swa_decode(const zgattn_desc* d, const void* q, const void* k_new, const void* v_new,
+                      const void* g, const float* wq, const float* wk, void* k_ring,
+                      void* v_ring, const int32_t* pos, void* out, void* stream) {
+  int st = decode_common(d, q, k_new, v_new, wq, wk, k_ring, v_ring, pos, out);
+  if (st) return st;
+  if (!g) return ZGATTN_ENULL;
+  if (!aligned16(g)) return ZGATTN_EINVAL;
+  if (d->window < 1 || d->window > 4096) return ZGATTN_EINVAL;
+  DecodeArgs a = make_decode(d, q, k_new, v_new, g, wq, wk, k_ring, v_ring, pos, out);
+  return hip_status(launch_swa_decode(a, (hipStream_t)stream));
+}
+
+size_t zgattn_global_decode_workspace_bytes(const zgattn_desc* d, int32_t capacity) {
+  if (check_desc(d) || capacity < 1) return 0;
+  int ns, chunk;
+  size_t bytes;
+  global_decode_geometry(d->batch, d->n_q_heads, d->head_dim, capacity, &ns, &chunk, &bytes);
+  return bytes;
+}
+
+int zgattn_global_decode(const zgattn_desc* d, const void* q, const void* k_new,
+                         const void* v_new, const float* wq, const float* wk, void* k_cache,
+                         void* v_cache, int32_t capacity, const int32_t* pos, void* workspace,
+                         size_t workspace_bytes, void* out, void* stream) {
+  int st = decode_common(d, q, k_new, v_new, wq, wk, k_cache, v_cache, pos, out);
+  if (st) return st;
+  if (capacity < 1 || capacity > ZGATTN_MAX_POSITION + 1) return ZGATTN_ERANGE;
+  if (!workspace || !aligned16(workspace)) return ZGATTN_EWORKSPACE;
+  DecodeArgs a = make_decode(d, q, k_new, v_new, nullptr, wq, wk, k_cache, v_cache, pos, out);
+  size_t need;
+  global_decode_geometry(a.B, a.Hq, a.d, capacity, &a.nsplit, &a.chunk, &need);
+  if (workspace_bytes < need) return ZGATTN_EWORKSPACE;
+  a.S = capacity;
+  a.ws = (float*)workspace;
+  return hip_status(launch_global_decode(a, (hipStream_t)stream));
+}
+
+int zgattn_qknorm_rope(const zgattn_desc* d, int32_t n_heads, const void* x, const float* w,
+                       const int32_t* pos, void* y, int64_t y_stride_b, int64_t y_stride_t,
+                       int64_t y_stride_h, void* stream) {
+  int st = check_desc(d);
+  if (st) return st;
+  if (d->seq_len < 0 || n_heads < 1) return ZGATTN_EINVAL;
+  if (!pos && d->seq_len > 0 && (int64_t)d->pos_offset + d->seq_len - 1 > ZGATTN_MAX_POSITION)
+    return ZGATTN_ERANGE;
+  if (d->seq_len == 0) return ZGATTN_OK;
+  if (!x || !w || !y) return ZGATTN_ENULL;
+  const int esz = d->dtype == ZGATTN_BF16 ? 2 : 4;
+  if (!aligned16(x) || !aligned16(y)) return ZGATTN_EINVAL;
+  if ((y_stride_b * esz) % 16 || (y_stride_t * esz) % 16 || (y_stride_h * esz) % 16)
+    return ZGATTN_EINVAL;
+  if (y_stride_b < 0 || y_stride_t < 0 || y_stride_h < 0) return ZGATTN_EINVAL;
+  NormRopeArgs n;
+  n.x = x;
+  n.w = w;
+  n.pos = pos;
+  n.y = y;
+  n.ysb = y_stride_b;
+  n.yst = y_stride_t;
+  n.ysh = y_stride_h;
+  n.B = d->batch;
+  n.T = d->seq_len;
+  n.H = n_heads;
+  n.d = d->head_dim;
+  n.rdim = d->rotary_dim;
+  n.pos_offset = d->pos_offset;
+  n.is_bf16 = d->dtype == ZGATTN_BF16;
+  n.eps = d->rms_eps;
+  n.out_scale = 1.0f;
+  n.fr = rope_freq(d->rotary_dim, d->rope_base);
+  return hip_status(launch_qknorm_rope(n, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,64 @@
+// Device-side helpers shared by the zgattn kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace zg {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kMaxHalfRot = 64;  // rotary_dim / 2 <= 64 (d <= 128)
+// Positions must be exact in fp32 (|p| < 2^24).
+#define ZGATTN_POS_LIMIT (1 << 24)
+
+// Per-pair RoPE phase step in revolutions per position, f_k = base^(-2k/r) / (2 pi),
+// split into an fp32 head and tail (computed in double on the host) so that the phase
+// p * f_k keeps ~44 significant bits for positions up to 2^24.
+struct RopeFreq {
+  float hi[kMaxHalfRot];
+  float lo[kMaxHalfRot];
+};
+
+__device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(bf16 x) { return (float)x; }
+
+// cos/sin of the angle p * 2 pi * f, with the phase reduced exactly to [-1/2, 1/2]
+// revolutions before the trigonometric evaluation.
+__device__ __forceinline__ void rope_cos_sin(int p, float fhi, float flo, float& c, float& s) {
+  const float pf = (float)p;                  // exact: |p| < 2^24
+  const float a = pf * fhi;
+  const float e = __builtin_fmaf(pf, fhi, -a);  // exact rounding error of pf * fhi
+  const float lo = __builtin_fmaf(pf, flo, e);
+  const float n = __builtin_rintf(a);
+  const float fr = (a - n) + lo;              // a - n is exact (Sterbenz)
+  sincospif(2.0f * fr, &s, &c);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// sigmoid(x) = 1 / (1 + exp(-x)); +inf -> 1, -inf -> 0, no NaN for infinite x.
+__device__ __forceinline__ float sigmoidf_(float x) {
+  return 1.0f / (1.0f + __expf(-x));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+}  // namespace zg

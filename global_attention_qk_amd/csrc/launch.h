@@ -1,0 +1,70 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace zg {
+
+// One prefill call (either layer kind), already validated on the host.
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* g;      // gate pre-activation (SWA) or nullptr (global)
+  void* out;
+  const float* wq;
+  const float* wk;
+  bf16* kt;           // normalised+rotated K, [B][Hkv][T][d] (global with workspace) or nullptr
+  int B, T, Hq, Hkv, d, window, rdim, pos_offset;
+  int swa;            // 1: gated sliding window; 0: ungated full causal
+  float eps;
+  float scale;        // softmax scale (natural-log units)
+  RopeFreq fr;
+};
+
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
+bool prefill_bf16_supported(int d, int group, int rdim);
+
+// Standalone QK-RMSNorm + partial RoPE with strided output.
+struct NormRopeArgs {
+  const void* x;
+  const float* w;
+  const int32_t* pos;  // [B*T] or nullptr
+  void* y;
+  int64_t ysb, yst, ysh;  // output strides in elements
+  int B, T, H, d, rdim, pos_offset, is_bf16;
+  float eps;
+  float out_scale;        // multiplies the result (1 for the public entry point)
+  RopeFreq fr;
+};
+hipError_t launch_qknorm_rope(const NormRopeArgs& a, hipStream_t s);
+
+// One decode step (either layer kind), bf16.
+struct DecodeArgs {
+  const void* q;       // [B][Hq][d]
+  const void* k_new;   // [B][Hkv][d]
+  const void* v_new;
+  const void* g;       // [B][Hq][d] (SWA) or nullptr
+  const float* wq;
+  const float* wk;
+  void* k_cache;       // [B][Hkv][S][d]
+  void* v_cache;
+  const int32_t* pos;  // [B]
+  void* out;           // [B][Hq][d]
+  float* ws;           // global: workspace; SWA: unused
+  int B, Hq, Hkv, d, S, rdim, window, nsplit, chunk;
+  float eps, scale;
+  RopeFreq fr;
+};
+hipError_t launch_swa_decode(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_global_decode(const DecodeArgs& a, hipStream_t s);
+// Split-K geometry and workspace bytes for a global decode call.
+void global_decode_geometry(int B, int Hq, int d, int capacity, int* nsplit, int* chunk,
+                            size_t* ws_bytes);
+
+}  // namespace zg

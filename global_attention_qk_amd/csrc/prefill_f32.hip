@@ -1,0 +1,188 @@
+// fp32 prefill attention (both layer kinds) on the vector ALUs.
+//
+// Same definition as the bf16 MFMA path (hyper.ai summary of arXiv 2609.13356, section
+// 方法; "ZGCM-1-7B 完全解説" explainer, section アーキテクチャ) kept in fp32 end to end,
+// for fp32 tensors. One wave64 workgroup owns 64 consecutive positions of one query
+// head; each lane owns one query row and keeps q~ and its output accumulator in
+// registers. K tiles are normalised+rotated once per visit in LDS, V tiles staged in LDS,
+// and every lane reads both with broadcast LDS loads. Any head group, rotary_dim <= d.
+#include "launch.h"
+
+namespace zg {
+namespace {
+
+constexpr int kT = 64;  // positions per workgroup and keys per tile
+
+struct FArgs {
+  const float* q;
+  const float* k;
+  const float* v;
+  const float* g;
+  float* out;
+  const float* wq;
+  const float* wk;
+  int T, Hq, Hkv, window, rdim, pos_offset, swa, group;
+  float eps, scale;
+  RopeFreq fr;
+};
+
+// RMSNorm + partial RoPE of one LDS row (length D, fp32), written to `dst` (LDS).
+template <int D>
+__device__ void norm_rope_row_f32(const float* raw, float* dst, const float* w, int pos,
+                                  int rdim, float eps, const RopeFreq& fr) {
+  float ss = 0.f;
+#pragma unroll 8
+  for (int c = 0; c < D; ++c) ss = __builtin_fmaf(raw[c], raw[c], ss);
+  const float rn = 1.0f / sqrtf(ss / D + eps);
+  const int half = rdim >> 1;
+  for (int j = 0; j < half; ++j) {
+    float cs, sn;
+    rope_cos_sin(pos, fr.hi[j], fr.lo[j], cs, sn);
+    const float a = raw[j] * rn * w[j];
+    const float b = raw[j + half] * rn * w[j + half];
+    dst[j] = a * cs - b * sn;
+    dst[j + half] = b * cs + a * sn;
+  }
+  for (int c = rdim; c < D; ++c) dst[c] = raw[c] * rn * w[c];
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void prefill_f32_kernel(const FArgs p) {
+  constexpr int RS = D + 1;  // padded LDS row
+  __shared__ float sRaw[kT * RS];
+  __shared__ float sK[kT * RS];
+  __shared__ float sV[kT * RS];
+  __shared__ float sW[2 * D];
+  __shared__ float sS[kT * (kT + 1)];
+
+  const int t = threadIdx.x;
+  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int kvh = h / p.group;
+  const int i0 = tile * kT;
+  const int T = p.T;
+  const int qi = i0 + t;
+  for (int c = t; c < D; c += 64) {
+    sW[c] = p.wq[c];
+    sW[D + c] = p.wk[c];
+  }
+  __syncthreads();
+  // q row -> LDS (thread-per-row), transform into sK (scratch), then to registers.
+  {
+    const float* src = p.q + (((size_t)b * T + qi) * p.Hq + h) * D;
+    for (int c = 0; c < D; c += 4) {
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (qi < T) x = *(const float4*)(src + c);
+      sRaw[t * RS + c] = x.x;
+      sRaw[t * RS + c + 1] = x.y;
+      sRaw[t * RS + c + 2] = x.z;
+      sRaw[t * RS + c + 3] = x.w;
+    }
+    norm_rope_row_f32<D>(sRaw + t * RS, sK + t * RS, sW, p.pos_offset + qi, p.rdim, p.eps, p.fr);
+  }
+  float qv[D];
+#pragma unroll
+  for (int c = 0; c < D; ++c) qv[c] = sK[t * RS + c] * p.scale;
+  float acc[D];
+#pragma unroll
+  for (int c = 0; c < D; ++c) acc[c] = 0.f;
+  float m = -INFINITY, l = 0.f;
+
+  const int last = min(i0 + kT, T) - 1;
+  int kt_lo = 0;
+  if (p.swa) kt_lo = max(0, i0 - p.window + 1) / kT;
+  const int kt_hi = last / kT;
+  __syncthreads();
+  for (int kt = kt_lo; kt <= kt_hi; ++kt) {
+    const int k0 = kt * kT;
+    const int kj = k0 + t;
+    {
+      const size_t off = (((size_t)b * T + kj) * p.Hkv + kvh) * D;
+      for (int c = 0; c < D; c += 4) {
+        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+        float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (kj < T) {
+          x = *(const float4*)(p.k + off + c);
+          y = *(const float4*)(p.v + off + c);
+        }
+        sRaw[t * RS + c] = x.x; sRaw[t * RS + c + 1] = x.y;
+        sRaw[t * RS + c + 2] = x.z; sRaw[t * RS + c + 3] = x.w;
+        sV[t * RS + c] = y.x; sV[t * RS + c + 1] = y.y;
+        sV[t * RS + c + 2] = y.z; sV[t * RS + c + 3] = y.w;
+      }
+      norm_rope_row_f32<D>(sRaw + t * RS, sK + t * RS, sW + D, p.pos_offset + kj, p.rdim,
+                           p.eps, p.fr);
+    }
+    __syncthreads();
+    // scores of this lane's query against the tile (LDS, one row per lane)
+    float mt = -INFINITY;
+    for (int j = 0; j < kT; ++j) {
+      const int key = k0 + j;
+      bool vis = key <= qi;
+      if (p.swa) vis = vis && key > qi - p.window;
+      float d = 0.f;
+#pragma unroll
+      for (int c = 0; c < D; ++c) d = __builtin_fmaf(qv[c], sK[j * RS + c], d);
+      d = vis ? d : -INFINITY;
+      sS[t * (kT + 1) + j] = d;
+      mt = fmaxf(mt, d);
+    }
+    const float mn = fmaxf(m, mt);
+    if (mn != -INFINITY) {
+      const float alpha = (m == -INFINITY) ? 0.f : expf(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int c = 0; c < D; ++c) acc[c] *= alpha;
+      for (int j = 0; j < kT; ++j) {
+        const float pj = expf(sS[t * (kT + 1) + j] - mn);
+        l += pj;
+#pragma unroll
+        for (int c = 0; c < D; ++c) acc[c] = __builtin_fmaf(pj, sV[j * RS + c], acc[c]);
+      }
+      m = mn;
+    }
+    __syncthreads();
+  }
+  if (qi < T) {
+    const size_t off = (((size_t)b * T + qi) * p.Hq + h) * D;
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int c = 0; c < D; ++c) {
+      float o = acc[c] * inv;
+      if (p.swa) o *= 1.0f / (1.0f + expf(-p.g[off + c]));
+      p.out[off + c] = o;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s) {
+  FArgs f;
+  f.q = (const float*)a.q;
+  f.k = (const float*)a.k;
+  f.v = (const float*)a.v;
+  f.g = (const float*)a.g;
+  f.out = (float*)a.out;
+  f.wq = a.wq;
+  f.wk = a.wk;
+  f.T = a.T;
+  f.Hq = a.Hq;
+  f.Hkv = a.Hkv;
+  f.window = a.window;
+  f.rdim = a.rdim;
+  f.pos_offset = a.pos_offset;
+  f.swa = a.swa;
+  f.group = a.Hq / a.Hkv;
+  f.eps = a.eps;
+  f.scale = a.scale;
+  f.fr = a.fr;
+  const dim3 grid((a.T + kT - 1) / kT, a.Hq, a.B);
+  if (grid.x == 0) return hipSuccess;
+  if (a.d == 128)
+    hipLaunchKernelGGL(prefill_f32_kernel<128>, grid, dim3(64), 0, s, f);
+  else
+    hipLaunchKernelGGL(prefill_f32_kernel<64>, grid, dim3(64), 0, s, f);
+  return hipGetLastError();
+}
+
+}  // namespace zg

@@ -1,0 +1,157 @@
+/*
+ * zgattn -- hybrid gated sliding-window / global causal GQA attention on MI355X (gfx950).
+ *
+ * The layer these entry points compute is the one the ZGCM-1 pages state:
+ *   GatedSWA(h) = o_proj( A_SWA(q, k, v) (*) sigmoid(g_proj(h)) )
+ * with q, k, v, g projected in parallel from the normalised hidden state, RMSNorm ("QK
+ * normalisation") and partial RoPE (rotary ratio 0.33) on the q and k branches, a
+ * 128-token sliding window for A_SWA, and ungated full-causal attention in the global
+ * layers (hyper.ai summary of arXiv 2609.13356, section 方法, display equation; the
+ * "ZGCM-1-7B 完全解説" explainer, section アーキテクチャ). The projections and o_proj are
+ * outside this library: the calls take post-projection Q, K, V and the gate
+ * pre-activation G and return the pre-o_proj output.
+ *
+ * Conventions for every call:
+ *  - Tensor pointers are DEVICE pointers owned by the caller. The library never
+ *    allocates, frees or synchronises; every call is asynchronous on `stream`
+ *    (a hipStream_t; NULL = the default stream). Inputs are never modified. Only `out`,
+ *    the caches (decode appends the new token) and `workspace` are written.
+ *  - Layouts are dense and contiguous, d fastest: Q, G, O are [B, T, Hq, d]; K, V are
+ *    [B, T, Hkv, d]; decode caches are [B, Hkv, S, d]. Q, K, V, G, O and caches share
+ *    one element type (`dtype`); RMSNorm weights are always fp32 [d].
+ *  - Query head h reads KV head h / (Hq / Hkv).
+ *  - Key j is visible to query i iff j <= i (global) and additionally i - window < j
+ *    (SWA): the window counts the query itself (the jaehun.me review's worked example,
+ *    section 게이트형 SWA의 동작: with window 4 the 4th token sees 4 tokens).
+ *  - RMSNorm is per head over d: x / sqrt(mean(x^2) + rms_eps) * w. RoPE then rotates
+ *    the leading rotary_dim dims in pairs (k, k + rotary_dim/2) by the angle
+ *    pos * rope_base^(-2k/rotary_dim); dims [rotary_dim, d) pass through.
+ *  - Scores are softmax_scale * q~ . k~ (softmax_scale <= 0 selects 1/sqrt(d)).
+ *  - The gate is elementwise: O = A * 1/(1 + exp(-G)), G with O's shape.
+ *  - Errors: every call returns a zgattn_status. Arguments are checked on the host
+ *    before anything is launched; on error nothing is launched and the outputs are
+ *    untouched. A failed launch returns ZGATTN_EHIP. No call prints or aborts.
+ *  - Thread-safe: no mutable global state except a per-device property cache.
+ */
+#ifndef ZGATTN_H
+#define ZGATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ZGATTN_ABI_VERSION 1
+
+typedef enum {
+  ZGATTN_OK = 0,
+  ZGATTN_EINVAL = -1,       /* a size or parameter is out of range                     */
+  ZGATTN_ENULL = -2,        /* a required pointer is NULL                              */
+  ZGATTN_EDTYPE = -3,       /* unknown dtype                                           */
+  ZGATTN_EUNSUPPORTED = -4, /* valid but not implemented (e.g. d not in {64, 128})     */
+  ZGATTN_EWORKSPACE = -5,   /* workspace missing or smaller than the queried size      */
+  ZGATTN_ERANGE = -6,       /* a position or capacity is out of range                  */
+  ZGATTN_EHIP = -7          /* the HIP runtime reported an error at launch             */
+} zgattn_status;
+
+typedef enum { ZGATTN_F32 = 0, ZGATTN_BF16 = 1 } zgattn_dtype;
+
+typedef struct {
+  int32_t batch;        /* B >= 1                                                       */
+  int32_t seq_len;      /* T >= 0 (prefill); ignored by decode                          */
+  int32_t n_q_heads;    /* Hq >= 1                                                      */
+  int32_t n_kv_heads;   /* Hkv >= 1, Hq % Hkv == 0                                       */
+  int32_t head_dim;     /* d in {64, 128}                                               */
+  int32_t window;       /* SWA window W >= 1 (128 in the model); ignored by global calls */
+  int32_t rotary_dim;   /* even, 0 <= r <= d (2*floor(0.33*d/2) in the model: 42 or 20) */
+  int32_t pos_offset;   /* absolute position of prefill row 0 (>= 0)                    */
+  float rope_base;      /* > 0 (10000 in the workloads)                                 */
+  float rms_eps;        /* >= 0 (1e-6 in the workloads)                                 */
+  float softmax_scale;  /* <= 0 selects 1/sqrt(d)                                       */
+  int32_t dtype;        /* zgattn_dtype                                                 */
+} zgattn_desc;
+
+/* Positions (pos_offset + T - 1, decode pos) must stay below 2^24 so that they are exact
+ * in fp32; larger values return ZGATTN_ERANGE. */
+#define ZGATTN_MAX_POSITION ((1 << 24) - 1)
+
+int zgattn_abi_version(void);
+const char* zgattn_strerror(int status);
+
+/*
+ * Gated SWA prefill (hyper.ai summary, section 方法: GatedSWA equation without o_proj).
+ *   q, g, out: [B, T, Hq, d];  k, v: [B, T, Hkv, d];  wq, wk: fp32 [d].
+ *   out = softmax over the window of (q~ . k~) applied to v, times sigmoid(g).
+ * QK-RMSNorm and partial RoPE are applied on the fly as Q and K tiles are loaded.
+ * T == 0 is a no-op. out must not alias any input.
+ */
+int zgattn_swa_prefill(const zgattn_desc* desc, const void* q, const void* k, const void* v,
+                       const void* g, const float* wq, const float* wk, void* out,
+                       void* stream);
+
+/*
+ * Global (full-causal, ungated) prefill (explainer, section アーキテクチャ: the global
+ * layers attend to the whole context and carry no gate).
+ *   q, out: [B, T, Hq, d];  k, v: [B, T, Hkv, d];  wq, wk: fp32 [d].
+ * `workspace` (device, >= zgattn_global_prefill_workspace_bytes(desc) bytes, 256-byte
+ * aligned) receives normalised+rotated K once before the attention kernel reads it; with
+ * workspace == NULL the K transform is instead fused into every K-tile load (slower for
+ * long sequences, where each K tile is visited by many query tiles).
+ */
+int zgattn_global_prefill(const zgattn_desc* desc, const void* q, const void* k,
+                          const void* v, const float* wq, const float* wk, void* workspace,
+                          size_t workspace_bytes, void* out, void* stream);
+size_t zgattn_global_prefill_workspace_bytes(const zgattn_desc* desc);
+
+/*
+ * Gated SWA decode: one new token per sequence against a ring of `window` entries
+ * (explainer, section アーキテクチャ: the SWA layers keep only a fixed 128 tokens).
+ *   q, g, out: [B, Hq, d];  k_new, v_new: [B, Hkv, d] (raw, before norm/RoPE);
+ *   k_ring, v_ring: [B, Hkv, window, d] holding post-norm, post-RoPE K and raw V;
+ *   pos: device int32 [B], absolute position of the new token.
+ * Position p lives in ring slot p % window. The call writes k~_new and v_new into slot
+ * pos % window, then attends over positions max(0, pos-window+1) .. pos. A sequence
+ * whose pos is negative or above ZGATTN_MAX_POSITION gets NaN outputs and an untouched
+ * ring (checked on the device, since pos lives there).
+ */
+int zgattn_swa_decode(const zgattn_desc* desc, const void* q, const void* k_new,
+                      const void* v_new, const void* g, const float* wq, const float* wk,
+                      void* k_ring, void* v_ring, const int32_t* pos, void* out,
+                      void* stream);
+
+/*
+ * Global decode with split-K over the cache (explainer, section アーキテクチャ: decode is
+ * memory-bandwidth-bound and the global layers keep the whole sequence).
+ *   q, out: [B, Hq, d];  k_new, v_new: [B, Hkv, d];  caches [B, Hkv, capacity, d]
+ *   (post-norm, post-RoPE K; raw V) valid for indices < pos[b];  pos: device int32 [B].
+ * The call writes k~_new, v_new at cache index pos[b], then attends over 0 .. pos[b].
+ * `workspace` (device, >= zgattn_global_decode_workspace_bytes(desc, capacity) bytes)
+ * holds per-split partial results. A sequence with pos outside [0, capacity) gets NaN
+ * outputs and an untouched cache.
+ */
+int zgattn_global_decode(const zgattn_desc* desc, const void* q, const void* k_new,
+                         const void* v_new, const float* wq, const float* wk,
+                         void* k_cache, void* v_cache, int32_t capacity,
+                         const int32_t* pos, void* workspace, size_t workspace_bytes,
+                         void* out, void* stream);
+size_t zgattn_global_decode_workspace_bytes(const zgattn_desc* desc, int32_t capacity);
+
+/*
+ * Standalone QK-RMSNorm + partial RoPE (the q/k-branch transform of both layer kinds).
+ *   x: [B, T, n_heads, d] contiguous (desc->dtype);  w: fp32 [d];
+ *   pos: device int32 [B*T] absolute positions, or NULL for pos_offset + t;
+ *   y: same dtype, element (b, t, h, c) stored at
+ *      y + b*y_stride_b + t*y_stride_t + h*y_stride_h + c   (strides in elements),
+ *   so it can write straight into a [B, Hkv, S, d] cache. y must not overlap x.
+ */
+int zgattn_qknorm_rope(const zgattn_desc* desc, int32_t n_heads, const void* x,
+                       const float* w, const int32_t* pos, void* y, int64_t y_stride_b,
+                       int64_t y_stride_t, int64_t y_stride_h, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZGATTN_H */

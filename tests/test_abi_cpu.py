@@ -1,0 +1,116 @@
+"""The C-ABI library loads and exports what include/zgattn.h declares; host-side argument
+checks return their status codes before anything touches a GPU."""
+
+import ctypes
+import os
+
+import pytest
+
+from global_attention_qk_amd import _lib as L
+from global_attention_qk_amd.api import make_desc
+
+pytestmark = pytest.mark.skipif(not os.path.exists(L.LIB_PATH),
+                                reason="libzgattn.so not built (run __graft_entry__.build())")
+
+FAKE = ctypes.c_void_p(4096)  # never dereferenced: every call below fails validation first
+
+
+def test_exports_every_declared_symbol():
+    lib = L.lib()
+    declared = L.header_symbols()
+    assert len(declared) == 9
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(declared) == set(L.SIGNATURES)
+
+
+def test_version_and_strerror():
+    lib = L.lib()
+    assert lib.zgattn_abi_version() == 1
+    for code in L.STATUS:
+        assert lib.zgattn_strerror(code)
+    assert lib.zgattn_strerror(12345) == b"unknown status"
+
+
+def _d(**kw):
+    base = dict(batch=1, seq_len=16, n_q_heads=4, n_kv_heads=1, head_dim=128, window=128,
+                rotary_dim=42, dtype=L.BF16)
+    base.update(kw)
+    return make_desc(**base)
+
+
+def _swa(d, q=FAKE, g=FAKE, out=FAKE):
+    return L.lib().zgattn_swa_prefill(ctypes.byref(d), q, FAKE, FAKE, g, FAKE, FAKE, out, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_q_heads=6, n_kv_heads=4), L.STATUS and -1),
+    (dict(head_dim=96), -4),
+    (dict(rotary_dim=43), -1),
+    (dict(rotary_dim=130), -1),
+    (dict(dtype=7), -3),
+    (dict(window=0), -1),
+    (dict(batch=0), -1),
+    (dict(seq_len=-1), -1),
+    (dict(pos_offset=-3), -6),
+    (dict(pos_offset=(1 << 24) - 8, seq_len=16), -6),
+    (dict(rope_base=-1.0), -1),
+    (dict(rms_eps=float("nan")), -1),
+])
+def test_prefill_rejects(kw, code):
+    assert _swa(_d(**kw)) == code
+
+
+def test_nulls_and_alignment():
+    assert _swa(_d(), q=None) == -2
+    assert _swa(_d(), g=None) == -2
+    assert _swa(_d(), out=ctypes.c_void_p(4100)) == -1
+    assert L.lib().zgattn_swa_prefill(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -2
+    # empty sequence is a no-op that touches nothing
+    assert _swa(_d(seq_len=0), q=None, g=None, out=None) == 0
+
+
+def test_bf16_mfma_path_limits():
+    # rotary_dim above 64 and head groups the 256-row tile cannot split are refused
+    assert _swa(_d(rotary_dim=80)) == -4
+    assert _swa(_d(n_q_heads=3, n_kv_heads=1)) == -4
+
+
+def test_global_prefill_workspace():
+    lib = L.lib()
+    d = _d(batch=2, seq_len=1000, n_q_heads=32, n_kv_heads=8)
+    need = lib.zgattn_global_prefill_workspace_bytes(ctypes.byref(d))
+    assert need == 2 * 8 * 1000 * 128 * 2
+    st = lib.zgattn_global_prefill(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   need - 1, FAKE, None)
+    assert st == -5
+
+
+def test_decode_checks():
+    lib = L.lib()
+    d = _d(batch=4, seq_len=1, n_q_heads=32, n_kv_heads=8)
+    cap = 262144
+    need = lib.zgattn_global_decode_workspace_bytes(ctypes.byref(d), cap)
+    assert need >= 4 * 32 * 128 * 4
+    call = lambda **kw: lib.zgattn_global_decode(
+        ctypes.byref(kw.get("d", d)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+        kw.get("cap", cap), kw.get("pos", FAKE), kw.get("ws", FAKE), kw.get("nb", need),
+        FAKE, None)
+    assert call(ws=None) == -5
+    assert call(nb=need - 1) == -5
+    assert call(cap=0) == -6
+    assert call(pos=None) == -2
+    assert call(d=_d(dtype=L.F32, n_q_heads=32, n_kv_heads=8)) == -4
+    assert call(d=_d(n_q_heads=48, n_kv_heads=3)) == -4   # head group 16
+    st = lib.zgattn_swa_decode(ctypes.byref(_d(window=0, n_q_heads=32, n_kv_heads=8)), FAKE,
+                               FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == -1
+
+
+def test_qknorm_rope_checks():
+    lib = L.lib()
+    d = _d()
+    ok_strides = (16 * 128, 128, 128 * 16)
+    assert lib.zgattn_qknorm_rope(ctypes.byref(d), 0, FAKE, FAKE, None, FAKE, *ok_strides, None) == -1
+    assert lib.zgattn_qknorm_rope(ctypes.byref(d), 4, FAKE, FAKE, None, FAKE, 16 * 128, 127, 128 * 16, None) == -1
+    assert lib.zgattn_qknorm_rope(ctypes.byref(d), 4, None, FAKE, None, FAKE, *ok_strides, None) == -2
