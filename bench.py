@@ -1,0 +1,251 @@
+"""Benchmark: attention tokens/s at 256K context on one MI355X.
+
+One step = the whole hot path over one batch of seeded synthetic input:
+  * prefill pair at T = 262,144 (B = 1, Hq = 32, Hkv = 8, d = 128, bf16): one gated-SWA
+    layer (W = 128) and one full-causal global layer over the same Q/K/V;
+  * one decode step for B = 32 sequences at context 262,144: a global layer over a full
+    [32, 8, 262144, 128] cache and a gated-SWA layer over a 128-entry ring.
+value = (prefill tokens + decode tokens) / step time, inputs resident in HBM.
+
+Prints ONE JSON line (rank 0). Per-kernel times come from HIP events recorded on the
+stream the library launches on (torch's current stream).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="approximate CPU time budget of the oracle sample")
+    return ap.parse_args()
+
+
+def alg_counts(T, B, Hq, Hkv, d, W, Bdec, S):
+    """Algorithmic FLOPs (QK^T + PV on visible pairs) and bytes (each tensor once)."""
+    swa_pairs = W * (W + 1) // 2 + (T - W) * W if T >= W else T * (T + 1) // 2
+    glob_pairs = T * (T + 1) // 2
+    el = 2  # bf16
+    return {
+        "swa_flops": 4 * d * swa_pairs * B * Hq,
+        "glob_flops": 4 * d * glob_pairs * B * Hq,
+        # Q, K, V, G read + O written
+        "swa_bytes": B * T * d * el * (3 * Hq + 2 * Hkv),
+        "glob_bytes": B * T * d * el * (2 * Hq + 2 * Hkv),
+        # K and V cache over [0, pos] + q, k_new, v_new, out
+        "gdec_bytes": Bdec * Hkv * S * d * el * 2 + Bdec * d * el * (2 * Hq + 2 * Hkv),
+        "sdec_bytes": Bdec * Hkv * W * d * el * 2 + Bdec * d * el * (3 * Hq + 2 * Hkv),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
+              "multi-GPU path. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import global_attention_qk_amd as zg
+    from workloads import C4, C5, decode_inputs, prefill_inputs
+
+    dev = "cuda"
+    torch.cuda.init()
+    T, B, Hq, Hkv, d, W = C4.T, C4.B, C4.Hq, C4.Hkv, C4.d, C4.window
+    r = C4.rotary_dim
+    # ---- inputs (seeded, generated on the device, outside the timed region) -----------
+    q, k, v, g, wq, wk = prefill_inputs(C4, device=dev)
+    out_s = torch.empty_like(q)
+    out_g = torch.empty_like(q)
+    ws_bytes = zg.global_prefill_workspace_bytes(q, k, rotary_dim=r)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    dec = decode_inputs(C5, device=dev)
+    Bd, S = C5.B, C5.T
+    pos = torch.full((Bd,), S - 1, dtype=torch.int32, device=dev)
+    dws = torch.empty(zg.global_decode_workspace_bytes(dec["q"], dec["k_new"], S),
+                      dtype=torch.uint8, device=dev)
+    out_gd = torch.empty_like(dec["q"])
+    out_sd = torch.empty_like(dec["q"])
+    torch.cuda.synchronize()
+
+    names = ["swa_prefill", "global_prefill", "global_decode", "swa_decode"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        zg.swa_prefill(q, k, v, g, wq, wk, window=W, rotary_dim=r, out=out_s)
+        mark(1)
+        zg.global_prefill(q, k, v, wq, wk, rotary_dim=r, workspace=ws, out=out_g)
+        mark(2)
+        zg.global_decode(dec["q"], dec["k_new"], dec["v_new"], dec["wq"], dec["wk"],
+                         dec["k_cache"], dec["v_cache"], pos, rotary_dim=r, workspace=dws,
+                         out=out_gd)
+        mark(3)
+        zg.swa_decode(dec["q"], dec["k_new"], dec["v_new"], dec["g"], dec["wq"], dec["wk"],
+                      dec["k_ring"], dec["v_ring"], pos, rotary_dim=r, out=out_sd)
+        mark(4)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        print(f"[bench] warmup step {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {n: [] for n in names}
+    for ev in events:
+        for j, n in enumerate(names):
+            per[n].append(ev[j].elapsed_time(ev[j + 1]))
+    ms = {n: sum(x) / len(x) for n, x in per.items()}
+    ms_step = wall * 1e3 / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms_step:.2f} ms/step "
+          + " ".join(f"{n}={ms[n]:.3f}ms" for n in names), file=sys.stderr, flush=True)
+
+    cnt = alg_counts(T, B, Hq, Hkv, d, W, Bd, S)
+    tokens = B * T + Bd
+    value = tokens / (ms_step / 1e3)
+    glob_tflops = cnt["glob_flops"] / (ms["global_prefill"] / 1e3) / 1e12
+    breakdown = {
+        n: {"ms": round(ms[n], 4)} for n in names
+    }
+    breakdown["swa_prefill"].update(
+        tokens_per_s=B * T / (ms["swa_prefill"] / 1e3),
+        hbm_GBs=cnt["swa_bytes"] / (ms["swa_prefill"] / 1e3) / 1e9)
+    breakdown["swa_prefill"]["hbm_frac"] = breakdown["swa_prefill"]["hbm_GBs"] / PEAK_HBM_GBS
+    breakdown["global_prefill"].update(
+        tokens_per_s=B * T / (ms["global_prefill"] / 1e3), tflops=glob_tflops,
+        mfma_frac=glob_tflops / PEAK_BF16_TFLOPS)
+    breakdown["global_decode"].update(
+        tokens_per_s=Bd / (ms["global_decode"] / 1e3),
+        hbm_GBs=cnt["gdec_bytes"] / (ms["global_decode"] / 1e3) / 1e9)
+    breakdown["global_decode"]["hbm_frac"] = breakdown["global_decode"]["hbm_GBs"] / PEAK_HBM_GBS
+    breakdown["swa_decode"].update(
+        tokens_per_s=Bd / (ms["swa_decode"] / 1e3),
+        hbm_GBs=cnt["sdec_bytes"] / (ms["swa_decode"] / 1e3) / 1e9)
+    breakdown["prefill_pair_tokens_per_s"] = B * T / ((ms["swa_prefill"] + ms["global_prefill"]) / 1e3)
+    breakdown["decode_tokens_per_s"] = Bd / ((ms["global_decode"] + ms["swa_decode"]) / 1e3)
+
+    rec = {
+        "metric": "attention tokens/s at 256K ctx (SWA+global prefill, decode); % MFMA/HBM peak",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V/G and caches generated on the device)",
+        "config": {
+            "workload": "prefill pair (gated SWA W=128 + global causal) B=1 T=262144 "
+                        "Hq=32 Hkv=8 d=128 rotary 42 + decode step B=32 ctx=262144",
+            "prefill": {"B": B, "T": T, "Hq": Hq, "Hkv": Hkv, "d": d, "window": W,
+                        "rotary_dim": r},
+            "decode": {"B": Bd, "context": S, "Hq": Hq, "Hkv": Hkv, "d": d, "ring": W},
+            "tokens_per_step": tokens,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "kernel": "global prefill (causal bf16 MFMA attention, T=262144)",
+            "bound": "mfma",
+            "achieved": glob_tflops,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": glob_tflops / PEAK_BF16_TFLOPS,
+            "traffic": None,
+            "alg_flops_per_launch": cnt["glob_flops"],
+        },
+        "breakdown": breakdown,
+    }
+    if args.cpu_baseline == "on":
+        del q, k, v, g, out_s, out_g, ws
+        rec["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(budget_s: float):
+    """The fp64 oracle on a bounded sample of the same workload, scaled to tokens/s.
+
+    Sample: n stratified query rows of the T=262144 prefill pair (all 32 heads, both
+    layers: the oracle's global rows read all keys up to the row, SWA rows their window)
+    and one decode sequence of each kind at context 262144. CPU seconds per step =
+    T * (global + SWA seconds per row) + 32 * (decode seconds per sequence).
+    """
+    import numpy as np
+    import torch
+
+    from oracle import attn as O
+    from workloads import C4, C5, decode_inputs, prefill_inputs, stratified_rows
+
+    cores = len(os.sched_getaffinity(0))
+    T = C4.T
+    q, k, v, g, wq, wk = prefill_inputs(C4, device="cuda")
+    f = lambda t: t.float().cpu().numpy()
+    n_rows = 24
+    rows = np.sort(np.random.default_rng(7).choice(T, size=n_rows, replace=False))
+    kh, vh = f(k), f(v)
+    qh, gh = f(q[:, rows]), f(g[:, rows])
+    wqh, wkh = f(wq), f(wk)
+    del q, k, v, g
+    t0 = time.perf_counter()
+    O.prefill_rows(qh, kh, vh, None, wqh, wkh, rows, rotary_dim=C4.rotary_dim,
+                   threads=cores)
+    t_glob = (time.perf_counter() - t0) / n_rows
+    t0 = time.perf_counter()
+    O.prefill_rows(qh, kh, vh, gh, wqh, wkh, rows, window=C4.window,
+                   rotary_dim=C4.rotary_dim, threads=cores)
+    t_swa = (time.perf_counter() - t0) / n_rows
+    del kh, vh
+    dec = decode_inputs(C5, device="cuda", B=1)
+    dh = {n: f(t) for n, t in dec.items()}
+    S = C5.T
+    t0 = time.perf_counter()
+    O.decode_global(dh["q"], dh["k_new"], dh["v_new"], dh["wq"], dh["wk"], dh["k_cache"],
+                    dh["v_cache"], np.array([S - 1]), rotary_dim=C5.rotary_dim)
+    t_gd = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    O.decode_swa(dh["q"], dh["k_new"], dh["v_new"], dh["g"], dh["wq"], dh["wk"], dh["k_ring"],
+                 dh["v_ring"], np.array([S - 1]), window=C5.window, rotary_dim=C5.rotary_dim)
+    t_sd = time.perf_counter() - t0
+    step_s = T * (t_glob + t_swa) + C5.B * (t_gd + t_sd)
+    return {
+        "value": (T + C5.B) / step_s,
+        "unit": "tokens/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"{n_rows} uniformly drawn query rows of the T=262144 prefill pair (all 32 "
+                  f"heads; global {t_glob:.3f} s/row, SWA {t_swa:.3f} s/row) and one decode "
+                  f"sequence per layer kind at context 262144 (global {t_gd:.2f} s, SWA "
+                  f"{t_sd:.4f} s), scaled to one step of 262144 prefill + 32 decode tokens",
+        "seconds_per_step_estimate": step_s,
+    }
+
+
+if __name__ == "__main__":
+    main()

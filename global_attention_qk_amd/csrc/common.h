@@ -34,6 +34,9 @@ __device__ __forceinline__ float bf16_to_f32(bf16 x) { return (float)x; }
 // cos/sin of the angle p * 2 pi * f, with the phase reduced exactly to [-1/2, 1/2]
 // revolutions before the trigonometric evaluation.
 __device__ __forceinline__ void rope_cos_sin(int p, float fhi, float flo, float& c, float& s) {
+  // No contraction here: fusing (pf * fhi) - n into one FMA would count the product's
+  // rounding error twice (it is added back through `lo`).
+#pragma clang fp contract(off)
   const float pf = (float)p;                  // exact: |p| < 2^24
   const float a = pf * fhi;
   const float e = __builtin_fmaf(pf, fhi, -a);  // exact rounding error of pf * fhi

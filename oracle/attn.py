@@ -173,7 +173,9 @@ def prefill_rows(q, k, v, g, wq, wk, rows, *, window=None, rotary_dim=None,
 
     jobs = [(b, kv) for b in range(B) for kv in range(Hkv)]
     if threads > 1:
-        with ThreadPoolExecutor(threads) as ex:
+        # one BLAS thread per worker: the workers already cover the cores
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1), ThreadPoolExecutor(threads) as ex:
             list(ex.map(lambda a: one(*a), jobs))
     else:
         for a in jobs:

@@ -118,6 +118,14 @@ def test_bf16_position_offset_large():
     _check("global", q, k, v, None, wq, wk, pos_offset=262144 - 300, tol=TOL_BF16)
 
 
+@pytest.mark.parametrize("kind", ["swa", "global"])
+def test_fp32_position_offset_large(kind):
+    # the fp32 tolerance resolves RoPE phase errors of ~1e-5 rad at positions near 2.6e5
+    q, k, v, g, wq, wk = _inputs(1, 130, 4, 1, 128, "f32", 650)
+    _check(kind, q, k, v, g, wq, wk, window=128, rdim=42, pos_offset=262144 - 130,
+           tol=TOL_F32)
+
+
 def test_tiny_sequences():
     for T in (1, 2, 31, 33, 64, 65):
         q, k, v, g, wq, wk = _inputs(1, T, 8, 2, 128, "bf16", 800 + T)
