@@ -36,6 +36,9 @@ def hipcc() -> str:
 def common_flags():
     return ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMAs issued through builtins write VGPRs (scores feed the VALU softmax);
+            # the output accumulators are pinned to AGPRs explicitly.
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-I", INCLUDE, "-I", CSRC, "-Wno-unused-command-line-argument"]
 
 

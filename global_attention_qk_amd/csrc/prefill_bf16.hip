@@ -15,37 +15,47 @@
 //     B-operand layout of O^T += V^T . P^T, so no cross-lane shuffle is needed between
 //     the two products and the softmax row statistics are per-lane scalars.
 //   * V is transposed into LDS with the keys of each 16-key group permuted so that a
-//     lane's eight keys are one 16-byte LDS read.
+//     lane's eight keys are one 16-byte LDS read. K/V tiles are double-buffered in LDS
+//     and the next tile's global loads are in flight while the current one is computed.
 //   * Q~ is pre-multiplied by scale * log2(e) so that p = exp2(s - m).
-//   * The running max is only raised when a tile's max exceeds it by more than 8
-//     (factor 256); the result is unchanged (the same m divides out), rescales get rare.
+//   * Static shift: after RMSNorm every score obeys |s| <= B = qscale * d * max|wq| *
+//     max|wk| (RoPE keeps norms). When B is moderate, p = exp2(s) with no max
+//     subtraction is exact (softmax is shift-invariant) and cannot overflow or flush to
+//     zero, so the running max, its reduction and the accumulator rescale disappear. A
+//     second kernel variant keeps an online max for larger bounds; both variants are
+//     launched and each returns at once unless the bound selects it.
+//   * The O accumulators stay in AGPRs for the whole kernel (the P.V product is issued
+//     through a constrained MFMA), leaving the VGPRs to the scores and operands.
 //   * K~: for global layers a separate pass writes normalised+rotated K once into a
 //     workspace that the tiles read directly; for SWA layers (each K tile visited by
 //     about three query tiles) the transform is fused into the tile load.
+#include <type_traits>
+
 #include "launch.h"
 
 namespace zg {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRows = 256;     // query rows per workgroup
-constexpr int kBN = 64;        // keys per tile
+constexpr int kRows = 256;        // query rows per workgroup
+constexpr int kBN = 64;           // keys per tile
 constexpr int kMaxHalfMfma = 32;  // rotary_dim <= 64 on this path
+constexpr float kStaticShiftMax = 96.0f;  // largest score bound (log2 units) without a max
 
 template <int D>
 struct Smem {
-  static constexpr int kRowB = D * 2 + 16;           // padded bf16 row (bytes)
-  static constexpr int kVtRowB = kBN * 2 + 16;       // padded V^T row (bytes)
+  static constexpr int kRowB = D * 2 + 16;      // padded bf16 row (bytes)
+  static constexpr int kVtRowB = kBN * 2 + 16;  // padded V^T row (bytes)
   // Phase 1 (Q): raw Q rows, transformed in place; then copied to registers.
   static constexpr int kQ = kRows * kRowB;
-  // Main loop: K~ tile, V^T tile, raw K tile (fused), K trig table.
+  static constexpr int kQtrig = kRows * kMaxHalfMfma * 8;
+  // Main loop: two K~ / V^T buffers, raw K tile and its trig table (fused path).
   static constexpr int kK = kBN * kRowB;
   static constexpr int kVt = D * kVtRowB;
+  static constexpr int kBuf = kK + kVt;
   static constexpr int kKraw = kBN * kRowB;
   static constexpr int kKtrig = kBN * kMaxHalfMfma * 8;
-  static constexpr int kLoop = kK + kVt + kKraw + kKtrig;
-  // Q trig table: up to 256 positions x 32 pairs.
-  static constexpr int kQtrig = kRows * kMaxHalfMfma * 8;
+  static constexpr int kLoop = 2 * kBuf + kKraw + kKtrig;
   static constexpr int kW = 2 * D * 4;  // wq, wk
   static constexpr int kUnion = (kQ + kQtrig) > kLoop ? (kQ + kQtrig) : kLoop;
   static constexpr int kTotal = kUnion + kW;
@@ -66,14 +76,33 @@ struct KArgs {
   RopeFreq fr;
 };
 
-__device__ __forceinline__ uint32_t lds_off(const void* p) {
-  return (uint32_t)(uintptr_t)p;
-}
-
 // Swap bits 2 and 3 of a key index within its 16-key group: keys {0-3, 8-11} then
 // {4-7, 12-15}, matching which keys a lane holds in the S^T accumulator.
 __device__ __forceinline__ int vt_slot(int key) {
   return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+}
+
+// O^T += V^T P^T on an accumulator pinned to AGPRs. The leading s_nop covers the two
+// wait states a VALU-written operand (P) needs before an MFMA may read it.
+__device__ __forceinline__ void mfma_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// Keep a value in AGPRs from here on (so that loop-carried accumulators never take a
+// mixed register class).
+__device__ __forceinline__ void pin_agpr(f32x16& v) { asm volatile("" : "+a"(v)); }
+
+// Wait states between the last MFMA that wrote the accumulators and any other access.
+template <int DB>
+__device__ __forceinline__ void acc_fence(f32x16 (&o)[2][DB]) {
+  if constexpr (DB == 4) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[0][2]), "+a"(o[0][3]),
+                   "+a"(o[1][0]), "+a"(o[1][1]), "+a"(o[1][2]), "+a"(o[1][3]));
+  } else {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[1][0]), "+a"(o[1][1]));
+  }
 }
 
 // In-LDS RMSNorm + partial RoPE of one bf16 row (raw -> dst may alias for the
@@ -115,21 +144,22 @@ __device__ __forceinline__ void transform_row(const bf16* raw, bf16* dst, const 
   }
 }
 
-template <int D, bool SWA, bool KPRE>
+template <int D, bool SWA, bool KPRE, bool STATIC>
 __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const KArgs p) {
   using S = Smem<D>;
   constexpr int KS = D / 16;   // k-steps of the QK^T product
   constexpr int DB = D / 32;   // 32-wide d blocks of O
   constexpr int RW = S::kRowB / 2;      // padded row length in bf16 elements
   constexpr int VW = S::kVtRowB / 2;
+  constexpr int DC = D / 8;                     // 16-byte chunks per row
+  constexpr int KIT = (kBN * DC) / kThreads;    // K chunks per thread per tile
+  constexpr int VCH = (kBN / 4) * DC;           // threads that carry V (4 keys x 8 dims)
 
   extern __shared__ __attribute__((aligned(16))) char smem[];
   bf16* sQ = (bf16*)smem;
   float2* sQtrig = (float2*)(smem + S::kQ);
-  bf16* sK = (bf16*)smem;
-  bf16* sVt = (bf16*)(smem + S::kK);
-  bf16* sKraw = (bf16*)(smem + S::kK + S::kVt);
-  float2* sKtrig = (float2*)(smem + S::kK + S::kVt + S::kKraw);
+  bf16* sKraw = (bf16*)(smem + 2 * S::kBuf);
+  float2* sKtrig = (float2*)(smem + 2 * S::kBuf + S::kKraw);
   float* sWq = (float*)(smem + S::kUnion);
   float* sWk = sWq + D;
 
@@ -138,6 +168,28 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const KArgs p
   const int wave = tid >> 6;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
+
+  for (int i = tid; i < D; i += kThreads) {
+    sWq[i] = p.wq[i];
+    sWk[i] = p.wk[i];
+  }
+  __syncthreads();
+  // ---- Score bound and variant selection (uniform over the grid) ---------------------
+  // After RMSNorm, ||q^|| <= sqrt(d) max|wq| and ||k^|| <= sqrt(d) max|wk|, so every
+  // log2-domain score obeys |s| <= qscale * d * max|wq| * max|wk| (2% margin for the
+  // bf16 rounding of q~ and k~).
+  {
+    float wqm = 0.f, wkm = 0.f;
+    for (int c = lane; c < D; c += 64) {
+      wqm = fmaxf(wqm, fabsf(sWq[c]));
+      wkm = fmaxf(wkm, fabsf(sWk[c]));
+    }
+    wqm = wave_max(wqm);
+    wkm = wave_max(wkm);
+    const float bound = p.qscale * (float)D * wqm * wkm * 1.02f;
+    const bool use_static = bound <= kStaticShiftMax;  // false for NaN weights
+    if (use_static != STATIC) return;
+  }
 
   // Heavy query tiles first (global layers); consecutive workgroups cover different
   // (batch, kv-head) pairs so that one pair's tiles share an XCD's L2.
@@ -152,22 +204,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const KArgs p
   const int half = p.rdim >> 1;
   const int bpp = p.bmp >> 5;  // 32-row blocks per head in the tile
 
-  for (int i = tid; i < D; i += kThreads) {
-    sWq[i] = p.wq[i];
-    sWk[i] = p.wk[i];
-  }
-
   // ---- Phase 1: Q tile -> LDS (coalesced), trig table for its positions -------------
   {
     const int g = p.group;
-    const int chunks_per_pos = g * (D / 8);
+    const int chunks_per_pos = g * DC;
     const int n_chunks = p.bmp * chunks_per_pos;
     const bf16* qbase = p.q + ((size_t)b * T * p.Hq + (size_t)kvh * g) * D;
     for (int c = tid; c < n_chunks; c += kThreads) {
       const int pi = c / chunks_per_pos;
       const int rem = c - pi * chunks_per_pos;
-      const int hg = rem / (D / 8);
-      const int dc = rem - hg * (D / 8);
+      const int hg = rem / DC;
+      const int dc = rem - hg * DC;
       const int pos = i0 + pi;
       u32x4 val = {0u, 0u, 0u, 0u};
       if (pos < T) val = *(const u32x4*)(qbase + (size_t)pos * p.Hq * D + hg * D + dc * 8);
@@ -188,7 +235,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const KArgs p
     bf16* r = sQ + row * RW;
     float ss = 0.f;
 #pragma unroll
-    for (int c = 0; c < D / 8; ++c) {
+    for (int c = 0; c < DC; ++c) {
       const u32x4 v = *(const u32x4*)(r + c * 8);
       const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -214,17 +261,33 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const KArgs p
   // Absolute positions of this lane's two query rows (for masking).
   int qpos[2];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int blk = wave * 2 + qb;
-    qpos[qb] = i0 + (blk % bpp) * 32 + l32;
-  }
-  __syncthreads();  // Q region is reused by the K/V tiles below
+  for (int qb = 0; qb < 2; ++qb) qpos[qb] = i0 + ((wave * 2 + qb) % bpp) * 32 + l32;
+  __syncthreads();  // the Q region is reused by the K/V tiles below
 
-  // ---- Key-tile range -----------------------------------------------------------------
-  const int q_last = min(i0 + p.bmp, T) - 1;   // last valid query position of the tile
-  int kt_lo = 0;
-  if (SWA) kt_lo = max(0, i0 - p.window + 1) / kBN;
-  const int kt_hi = q_last / kBN;              // inclusive
+  // ---- Key-tile schedule ----------------------------------------------------------------
+  // Tiles [kt_lo, kt_hi] meet the band. Unmasked tiles are those entirely below every
+  // query of the tile (k0 + 63 <= i0) and, for SWA, entirely inside every query's window
+  // (k0 > q_last - W). They run first, as one branch-free stretch; the masked tiles
+  // (diagonal, band edge) follow.
+  const int q_last = min(i0 + p.bmp, T) - 1;
+  const int kt_lo = SWA ? max(0, i0 - p.window + 1) / kBN : 0;
+  const int kt_hi = q_last / kBN;
+  const int kt_cm = i0 >= kBN - 1 ? (i0 - (kBN - 1)) / kBN + 1 : 0;   // first causal-masked
+  const int kt_bm = (SWA && q_last - p.window >= 0) ? (q_last - p.window) / kBN : -1;
+  int u_lo = max(kt_lo, kt_bm + 1), u_hi = min(kt_hi, kt_cm - 1);
+  if (u_lo > u_hi) {
+    u_lo = kt_lo;
+    u_hi = kt_lo - 1;
+  }
+  const int n_unm = u_hi - u_lo + 1;
+  const int n_hi_m = kt_hi - u_hi;
+  const int n_tiles = kt_hi - kt_lo + 1;
+  auto tile_of = [&](int i) -> int {
+    if (i < n_unm) return u_hi - i;
+    i -= n_unm;
+    if (i < n_hi_m) return u_hi + 1 + i;
+    return kt_lo + (i - n_hi_m);
+  };
 
   f32x16 oacc[2][DB];
 #pragma unroll
@@ -233,39 +296,76 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const KArgs p
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[qb][db][r] = 0.f;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) pin_agpr(oacc[qb][db]);
   float m_run[2] = {-INFINITY, -INFINITY};
   float l_run[2] = {0.f, 0.f};
 
   const bf16* kbase = p.k + ((size_t)b * T * p.Hkv + kvh) * D;
   const bf16* vbase = p.v + ((size_t)b * T * p.Hkv + kvh) * D;
+  const bf16* ktsrc = KPRE ? p.kt + (((size_t)b * p.Hkv + kvh) * T) * D : nullptr;
   const size_t kvstride = (size_t)p.Hkv * D;
 
-  // Tiles from the diagonal backwards: every row sees itself in the first tile it meets
-  // when bmp <= kBN, and the -inf guard below covers the other shapes.
-  for (int kt = kt_hi; kt >= kt_lo; --kt) {
+  // Global -> registers for tile kt (issued one tile ahead of its use). Rows past the
+  // end are clamped to the last row: such keys are always masked out, and clamped
+  // values keep the products finite.
+  u32x4 kreg[KIT];
+  u32x4 vreg[4];
+  auto fetch = [&](int kt) {
     const int k0 = kt * kBN;
-    // -- K tile --
-    if (KPRE) {
-      const bf16* src = p.kt + (((size_t)b * p.Hkv + kvh) * T) * D;
 #pragma unroll
-      for (int it = 0; it < (kBN * D / 8) / kThreads; ++it) {
-        const int c = tid + it * kThreads;
-        const int kr = c / (D / 8), dc = c % (D / 8);
-        const int pos = k0 + kr;
-        u32x4 val = {0u, 0u, 0u, 0u};
-        if (pos < T) val = *(const u32x4*)(src + (size_t)pos * D + dc * 8);
-        *(u32x4*)(sK + kr * RW + dc * 8) = val;
-      }
-    } else {
+    for (int it = 0; it < KIT; ++it) {
+      const int c = tid + it * kThreads;
+      const int kr = c / DC, dc = c % DC;
+      const int pos = min(k0 + kr, T - 1);
+      kreg[it] = KPRE ? *(const u32x4*)(ktsrc + (size_t)pos * D + dc * 8)
+                      : *(const u32x4*)(kbase + (size_t)pos * kvstride + dc * 8);
+    }
+    if (tid < VCH) {
+      const int kg = tid % (kBN / 4), dc = tid / (kBN / 4);  // key group fastest: the
+      // transposed 8-byte LDS writes of one instruction then cover all banks
 #pragma unroll
-      for (int it = 0; it < (kBN * D / 8) / kThreads; ++it) {
-        const int c = tid + it * kThreads;
-        const int kr = c / (D / 8), dc = c % (D / 8);
-        const int pos = k0 + kr;
-        u32x4 val = {0u, 0u, 0u, 0u};
-        if (pos < T) val = *(const u32x4*)(kbase + (size_t)pos * kvstride + dc * 8);
-        *(u32x4*)(sKraw + kr * RW + dc * 8) = val;
+      for (int e = 0; e < 4; ++e) {
+        const int pos = min(k0 + kg * 4 + e, T - 1);
+        vreg[e] = *(const u32x4*)(vbase + (size_t)pos * kvstride + dc * 8);
       }
+    }
+  };
+  // Registers -> LDS buffer `buf`: K rows as they are (or raw, for the fused transform),
+  // V transposed with the per-16-key slot permutation; fused path: the tile's RoPE table.
+  auto stage = [&](int kt, int buf) {
+    const int k0 = kt * kBN;
+    bf16* sK = (bf16*)(smem + buf * S::kBuf);
+    bf16* sVt = (bf16*)(smem + buf * S::kBuf + S::kK);
+#pragma unroll
+    for (int it = 0; it < KIT; ++it) {
+      const int c = tid + it * kThreads;
+      const int kr = c / DC, dc = c % DC;
+      *(u32x4*)((KPRE ? sK : sKraw) + kr * RW + dc * 8) = kreg[it];
+    }
+    if (tid < VCH) {
+      const int kg = tid % (kBN / 4), dc = tid / (kBN / 4);  // key group fastest: the
+      // transposed 8-byte LDS writes of one instruction then cover all banks
+      const int slot = vt_slot(kg * 4);
+#pragma unroll
+      for (int dd = 0; dd < 8; ++dd) {
+        const int wsel = dd >> 1;
+        const uint32_t e0 = vreg[0][wsel], e1 = vreg[1][wsel];
+        const uint32_t e2 = vreg[2][wsel], e3 = vreg[3][wsel];
+        uint32_t lo01, lo23;
+        if (dd & 1) {
+          lo01 = (e0 >> 16) | (e1 & 0xffff0000u);
+          lo23 = (e2 >> 16) | (e3 & 0xffff0000u);
+        } else {
+          lo01 = (e0 & 0xffffu) | (e1 << 16);
+          lo23 = (e2 & 0xffffu) | (e3 << 16);
+        }
+        *(u32x2*)(sVt + (dc * 8 + dd) * VW + slot) = (u32x2){lo01, lo23};
+      }
+    }
+    if (!KPRE) {
       for (int e = tid; e < kBN * half; e += kThreads) {
         const int kr = e / half, j = e - kr * half;
         float c, s;
@@ -273,42 +373,110 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const KArgs p
         sKtrig[kr * kMaxHalfMfma + j] = make_float2(c, s);
       }
     }
-    // -- V tile, transposed: thread loads 4 keys x 8 dims and writes 8 rows of 4 keys --
-    {
-      constexpr int DC = D / 8;  // 8-dim chunks per row
-      for (int c = tid; c < (kBN / 4) * DC; c += kThreads) {
-        const int kg = c / DC;       // group of 4 keys
-        const int dc = c % DC;
-        u32x4 vv[4];
+  };
+
+  const bf16x2 ones2 = {(bf16)1.0f, (bf16)1.0f};
+
+  // One 64-key tile from LDS buffer `buf`, as two 32-key halves so that only 32 score
+  // registers per query block are live at a time.
+  auto compute = [&](int kt, int buf, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const bf16* sK = (const bf16*)(smem + buf * S::kBuf);
+    const bf16* sVt = (const bf16*)(smem + buf * S::kBuf + S::kK);
+    const int k0 = kt * kBN;
+    int rel[2];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int pos = k0 + kg * 4 + e;
-          vv[e] = (u32x4){0u, 0u, 0u, 0u};
-          if (pos < T) vv[e] = *(const u32x4*)(vbase + (size_t)pos * kvstride + dc * 8);
-        }
-        const int slot = vt_slot(kg * 4);
+    for (int qb = 0; qb < 2; ++qb) rel[qb] = qpos[qb] - k0 - 4 * hi;
 #pragma unroll
-        for (int dd = 0; dd < 8; ++dd) {
-          // element dd of each key's chunk
-          const int wsel = dd >> 1;
-          const bool hiw = dd & 1;
-          const uint32_t e0 = vv[0][wsel], e1 = vv[1][wsel];
-          const uint32_t e2 = vv[2][wsel], e3 = vv[3][wsel];
-          uint32_t lo01, lo23;
-          if (hiw) {
-            lo01 = (e0 >> 16) | (e1 & 0xffff0000u);
-            lo23 = (e2 >> 16) | (e3 & 0xffff0000u);
-          } else {
-            lo01 = (e0 & 0xffffu) | (e1 << 16);
-            lo23 = (e2 & 0xffffu) | (e3 << 16);
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 sacc[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[qb][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 a = *(const bf16x8*)(sK + (kb * 32 + l32) * RW + ks * 16 + hi * 8);
+        sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[0][ks], sacc[0], 0, 0, 0);
+        sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[1][ks], sacc[1], 0, 0, 0);
+      }
+      if (MASKED) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int off = kb * 32 + (r >> 2) * 8 + (r & 3);  // key - k0 - 4*hi
+            bool vis = off <= rel[qb];
+            if (SWA) vis = vis && (off > rel[qb] - p.window);
+            if (!vis) sacc[qb][r] = -INFINITY;
           }
-          *(u32x2*)(sVt + (dc * 8 + dd) * VW + slot) = (u32x2){lo01, lo23};
+      }
+      bf16x8 pb[2][2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        float mu = 0.f;
+        if (!STATIC) {
+          float mt = sacc[qb][0];
+#pragma unroll
+          for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sacc[qb][r]);
+          mt = fmaxf(mt, __shfl_xor(mt, 32));
+          const float m_old = m_run[qb];
+          const bool raise = mt > m_old + 8.0f;
+          if (__ballot(raise)) {
+            const float m_new = raise ? mt : m_old;
+            const float alpha = (m_old == -INFINITY) ? 0.f : fast_exp2(m_old - m_new);
+            l_run[qb] *= alpha;
+            acc_fence<DB>(oacc);
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) pin_agpr(oacc[qb][db]);
+            m_run[qb] = m_new;
+          }
+          mu = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
+        }
+        float ls = l_run[qb];
+#pragma unroll
+        for (int jh = 0; jh < 2; ++jh) {
+          bf16x8 v;
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            v[e] = (bf16)fast_exp2(STATIC ? sacc[qb][jh * 8 + e] : sacc[qb][jh * 8 + e] - mu);
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const bf16x2 pr = {v[e], v[e + 1]};
+            ls = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2, ls, false);
+          }
+          pb[qb][jh] = v;
+        }
+        l_run[qb] = ls;
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int jh = 0; jh < 2; ++jh) {
+          const bf16x8 a =
+              *(const bf16x8*)(sVt + (db * 32 + l32) * VW + kb * 32 + jh * 16 + hi * 8);
+          mfma_acc(oacc[0][db], a, pb[0][jh]);
+          mfma_acc(oacc[1][db], a, pb[1][jh]);
         }
       }
     }
-    __syncthreads();
+  };
+
+  // One tile: stage the prefetched data, transform K (fused path), prefetch the next
+  // tile, compute. The unmasked and masked stretches are separate loops so that the
+  // accumulators follow one register assignment around each loop.
+  auto step = [&](int i, auto masked_tag) {
+    const int kt = tile_of(i);
+    const int buf = i & 1;
+    stage(kt, buf);
+    __syncthreads();  // tile i is in LDS; every wave is done with tile i - 2's buffer
     if (!KPRE) {
-      // Fused K transform: 4 threads per key row.
+      // Fused K transform: 4 threads per key row, raw -> this tile's K~ buffer.
+      bf16* sK = (bf16*)(smem + buf * S::kBuf);
       const int kr = tid >> 2, sub = tid & 3;
       const bf16* r = sKraw + kr * RW;
       float ss = 0.f;
@@ -328,107 +496,25 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const KArgs p
       const float rn = __builtin_amdgcn_rsqf(ss * (1.0f / D) + p.eps);
       transform_row<D>(r, sK + kr * RW, sWk, sKtrig + kr * kMaxHalfMfma, rn, 1.0f, p.rdim,
                        sub, 4);
-      __syncthreads();
+      __syncthreads();  // K~ ready; sKraw / sKtrig free for the next stage()
     }
-
-    // -- S^T = K~ Q~^T for both query blocks and both 32-key blocks --
-    f32x16 sacc[2][2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[qb][kb][r] = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a = *(const bf16x8*)(sK + (kb * 32 + l32) * RW + ks * 16 + hi * 8);
-        sacc[0][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[0][ks], sacc[0][kb], 0, 0, 0);
-        sacc[1][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[1][ks], sacc[1][kb], 0, 0, 0);
-      }
-    }
-
-    // -- mask, online softmax, P to bf16 --
-    const bool need_mask = (k0 + kBN - 1 > i0) || (SWA && k0 <= q_last - p.window) ||
-                           (k0 + kBN > T);
-    bf16x8 pb[2][2][2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      if (need_mask) {
-        const int qi = qpos[qb];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kj = k0 + kb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
-            bool vis = kj <= qi;
-            if (SWA) vis = vis && (kj > qi - p.window);
-            if (!vis) sacc[qb][kb][r] = -INFINITY;
-          }
-      }
-      float mt = sacc[qb][0][0];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[qb][kb][r]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float m_old = m_run[qb];
-      const bool raise = mt > m_old + 8.0f;
-      if (__ballot(raise)) {
-        const float m_new = raise ? mt : m_old;
-        const float alpha = (m_old == -INFINITY) ? 0.f : fast_exp2(m_old - m_new);
-        l_run[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha;
-        m_run[qb] = m_new;
-      }
-      const float mu = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
-      float ls = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int jh = 0; jh < 2; ++jh) {
-          bf16x8 v;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float pe = fast_exp2(sacc[qb][kb][jh * 8 + e] - mu);
-            ls += pe;
-            v[e] = (bf16)pe;
-          }
-          pb[qb][kb][jh] = v;
-        }
-      }
-      l_run[qb] += ls;
-    }
-
-    // -- O^T += V^T P^T --
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int jh = 0; jh < 2; ++jh) {
-          const bf16x8 a = *(const bf16x8*)(sVt + (db * 32 + l32) * VW + kb * 32 + jh * 16 + hi * 8);
-          oacc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[0][kb][jh], oacc[0][db], 0, 0, 0);
-          oacc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[1][kb][jh], oacc[1][db], 0, 0, 0);
-        }
-      }
-    }
-    __syncthreads();  // the next tile overwrites sK / sVt
-  }
+    if (i + 1 < n_tiles) fetch(tile_of(i + 1));  // in flight during this tile's math
+    compute(kt, buf, masked_tag);
+  };
+  fetch(tile_of(0));
+  int i = 0;
+  for (; i < n_unm; ++i) step(i, std::integral_constant<bool, false>{});
+  for (; i < n_tiles; ++i) step(i, std::integral_constant<bool, true>{});
 
   // ---- Epilogue: O = acc / l (* sigmoid(G)), bf16 store ------------------------------
+  acc_fence<DB>(oacc);
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32);
     const int pos = qpos[qb];
     if (pos >= T) continue;
     const float inv = 1.0f / lt;
-    const int blk = wave * 2 + qb;
-    const int hg = blk / bpp;
+    const int hg = (wave * 2 + qb) / bpp;
     const int h = kvh * p.group + hg;
     const size_t rowoff = (((size_t)b * T + pos) * p.Hq + h) * D;
 #pragma unroll
@@ -456,11 +542,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const KArgs p
 template <int D, bool SWA, bool KPRE>
 hipError_t launch_t(const KArgs& ka, int n_blocks, hipStream_t s) {
   constexpr int smem = Smem<D>::kTotal;
-  auto kern = prefill_bf16_kernel<D, SWA, KPRE>;
-  hipError_t e = hipFuncSetAttribute((const void*)kern,
+  // Both variants are launched; each returns immediately unless the score bound
+  // (computed on the device from the norm weights) selects it.
+  auto k_static = prefill_bf16_kernel<D, SWA, KPRE, true>;
+  auto k_online = prefill_bf16_kernel<D, SWA, KPRE, false>;
+  hipError_t e = hipFuncSetAttribute((const void*)k_static,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, smem);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(n_blocks), dim3(kThreads), smem, s, ka);
+  e = hipFuncSetAttribute((const void*)k_online, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          smem);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_static, dim3(n_blocks), dim3(kThreads), smem, s, ka);
+  hipLaunchKernelGGL(k_online, dim3(n_blocks), dim3(kThreads), smem, s, ka);
   return hipGetLastError();
 }
 
