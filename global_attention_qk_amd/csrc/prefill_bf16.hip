@@ -36,8 +36,13 @@
 namespace zg {
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kRows = 256;        // query rows per workgroup
+// Waves per workgroup: 8 waves of 32 query rows keep two waves on every SIMD, so one
+// wave's softmax (exp, convert, row sums) overlaps the other's MFMAs.
+#ifndef ZG_PREFILL_WAVES
+#define ZG_PREFILL_WAVES 8
+#endif
+constexpr int kWavesPerBlock = ZG_PREFILL_WAVES;
 constexpr int kBN = 64;           // keys per tile
 constexpr int kMaxHalfMfma = 32;  // rotary_dim <= 64 on this path
 constexpr float kStaticShiftMax = 96.0f;  // largest score bound (log2 units) without a max
@@ -93,16 +98,13 @@ __device__ __forceinline__ void mfma_acc(f32x16& acc, const bf16x8& a, const bf1
 __device__ __forceinline__ void pin_agpr(f32x16& v) { asm volatile("" : "+a"(v)); }
 
 // Wait states between the last MFMA that wrote the accumulators and any other access.
-template <int DB>
-__device__ __forceinline__ void acc_fence(f32x16 (&o)[2][DB]) {
-  if constexpr (DB == 4) {
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
-                 : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[0][2]), "+a"(o[0][3]),
-                   "+a"(o[1][0]), "+a"(o[1][1]), "+a"(o[1][2]), "+a"(o[1][3]));
-  } else {
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
-                 : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[1][0]), "+a"(o[1][1]));
-  }
+template <int QB, int DB>
+__device__ __forceinline__ void acc_fence(f32x16 (&o)[QB][DB]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) asm volatile("" : "+a"(o[qb][db]));
 }
 
 // In-LDS RMSNorm + partial RoPE of one bf16 row (raw -> dst may alias for the
@@ -144,9 +146,12 @@ __device__ __forceinline__ void transform_row(const bf16* raw, bf16* dst, const 
   }
 }
 
-template <int D, bool SWA, bool KPRE, bool STATIC>
-__global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const KArgs p) {
+template <int D, bool SWA, bool KPRE, bool STATIC, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p) {
   using S = Smem<D>;
+  constexpr int kThreads = NW * 64;
+  constexpr int QB = kRows / 32 / NW;  // 32-row query blocks per wave
+  constexpr int TPR = kThreads / kBN;  // threads per key row in the fused K transform
   constexpr int KS = D / 16;   // k-steps of the QK^T product
   constexpr int DB = D / 32;   // 32-wide d blocks of O
   constexpr int RW = S::kRowB / 2;      // padded row length in bf16 elements
@@ -229,7 +234,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const KArgs p
   }
   __syncthreads();
   // Thread-per-row RMSNorm + RoPE + scale, in place.
-  {
+  if (tid < kRows) {
     const int row = tid;
     const int pi = row % p.bmp;
     bf16* r = sQ + row * RW;
@@ -251,17 +256,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const KArgs p
   __syncthreads();
   // Q~ into registers as the B operand: lane holds query row l32 of its block and the
   // eight d values 16*ks + 8*hi .. +7 for each k-step.
-  bf16x8 qreg[2][KS];
+  bf16x8 qreg[QB][KS];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int row = (wave * 2 + qb) * 32 + l32;
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = (wave * QB + qb) * 32 + l32;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qreg[qb][ks] = *(const bf16x8*)(sQ + row * RW + ks * 16 + hi * 8);
   }
   // Absolute positions of this lane's two query rows (for masking).
-  int qpos[2];
+  int qpos[QB];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) qpos[qb] = i0 + ((wave * 2 + qb) % bpp) * 32 + l32;
+  for (int qb = 0; qb < QB; ++qb) qpos[qb] = i0 + ((wave * QB + qb) % bpp) * 32 + l32;
   __syncthreads();  // the Q region is reused by the K/V tiles below
 
   // ---- Key-tile schedule ----------------------------------------------------------------
@@ -289,19 +294,23 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const KArgs p
     return kt_lo + (i - n_hi_m);
   };
 
-  f32x16 oacc[2][DB];
+  f32x16 oacc[QB][DB];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[qb][db][r] = 0.f;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int db = 0; db < DB; ++db) pin_agpr(oacc[qb][db]);
-  float m_run[2] = {-INFINITY, -INFINITY};
-  float l_run[2] = {0.f, 0.f};
+  float m_run[QB], l_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+  }
 
   const bf16* kbase = p.k + ((size_t)b * T * p.Hkv + kvh) * D;
   const bf16* vbase = p.v + ((size_t)b * T * p.Hkv + kvh) * D;
@@ -377,112 +386,167 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const KArgs p
 
   const bf16x2 ones2 = {(bf16)1.0f, (bf16)1.0f};
 
-  // One 64-key tile from LDS buffer `buf`, as two 32-key halves so that only 32 score
-  // registers per query block are live at a time.
-  auto compute = [&](int kt, int buf, auto masked_tag) {
+  // Scores of one 32-key block (rows kb*32.. of the K~ tile) for every query block.
+  auto qk = [&](const bf16* sK, int kb, f32x16 (&sacc)[QB]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[qb][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 a = *(const bf16x8*)(sK + (kb * 32 + l32) * RW + ks * 16 + hi * 8);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[qb][ks], sacc[qb], 0, 0, 0);
+    }
+  };
+  // Mask (edge tiles), exponentiate, round to bf16 (the P operand) and add the rounded
+  // values to the row sums. The online variant also raises the running max.
+  auto probs = [&](f32x16 (&sacc)[QB], int kb, const int (&rel)[QB], bf16x8 (&pb)[QB][2],
+                   auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
-    const bf16* sK = (const bf16*)(smem + buf * S::kBuf);
-    const bf16* sVt = (const bf16*)(smem + buf * S::kBuf + S::kK);
-    const int k0 = kt * kBN;
-    int rel[2];
+    if (MASKED) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) rel[qb] = qpos[qb] - k0 - 4 * hi;
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 sacc[2];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[qb][r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a = *(const bf16x8*)(sK + (kb * 32 + l32) * RW + ks * 16 + hi * 8);
-        sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[0][ks], sacc[0], 0, 0, 0);
-        sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[1][ks], sacc[1], 0, 0, 0);
-      }
-      if (MASKED) {
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int off = kb * 32 + (r >> 2) * 8 + (r & 3);  // key - k0 - 4*hi
-            bool vis = off <= rel[qb];
-            if (SWA) vis = vis && (off > rel[qb] - p.window);
-            if (!vis) sacc[qb][r] = -INFINITY;
-          }
-      }
-      bf16x8 pb[2][2];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        float mu = 0.f;
-        if (!STATIC) {
-          float mt = sacc[qb][0];
-#pragma unroll
-          for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sacc[qb][r]);
-          mt = fmaxf(mt, __shfl_xor(mt, 32));
-          const float m_old = m_run[qb];
-          const bool raise = mt > m_old + 8.0f;
-          if (__ballot(raise)) {
-            const float m_new = raise ? mt : m_old;
-            const float alpha = (m_old == -INFINITY) ? 0.f : fast_exp2(m_old - m_new);
-            l_run[qb] *= alpha;
-            acc_fence<DB>(oacc);
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-              for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) pin_agpr(oacc[qb][db]);
-            m_run[qb] = m_new;
-          }
-          mu = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
+        for (int r = 0; r < 16; ++r) {
+          const int off = kb * 32 + (r >> 2) * 8 + (r & 3);  // key - k0 - 4*hi
+          bool vis = off <= rel[qb];
+          if (SWA) vis = vis && (off > rel[qb] - p.window);
+          if (!vis) sacc[qb][r] = -INFINITY;
         }
-        float ls = l_run[qb];
+    }
 #pragma unroll
-        for (int jh = 0; jh < 2; ++jh) {
-          bf16x8 v;
+    for (int qb = 0; qb < QB; ++qb) {
+      float mu = 0.f;
+      if (!STATIC) {
+        float mt = sacc[qb][0];
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            v[e] = (bf16)fast_exp2(STATIC ? sacc[qb][jh * 8 + e] : sacc[qb][jh * 8 + e] - mu);
+        for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sacc[qb][r]);
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float m_old = m_run[qb];
+        const bool raise = mt > m_old + 8.0f;
+        if (__ballot(raise)) {
+          const float m_new = raise ? mt : m_old;
+          const float alpha = (m_old == -INFINITY) ? 0.f : fast_exp2(m_old - m_new);
+          l_run[qb] *= alpha;
+          acc_fence<QB, DB>(oacc);
 #pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const bf16x2 pr = {v[e], v[e + 1]};
-            ls = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2, ls, false);
-          }
-          pb[qb][jh] = v;
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) pin_agpr(oacc[qb][db]);
+          m_run[qb] = m_new;
         }
-        l_run[qb] = ls;
+        mu = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
       }
+      float ls = l_run[qb];
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
+      for (int jh = 0; jh < 2; ++jh) {
+        bf16x8 v;
 #pragma unroll
-        for (int jh = 0; jh < 2; ++jh) {
-          const bf16x8 a =
-              *(const bf16x8*)(sVt + (db * 32 + l32) * VW + kb * 32 + jh * 16 + hi * 8);
-          mfma_acc(oacc[0][db], a, pb[0][jh]);
-          mfma_acc(oacc[1][db], a, pb[1][jh]);
+        for (int e = 0; e < 8; ++e)
+          v[e] = (bf16)fast_exp2(STATIC ? sacc[qb][jh * 8 + e] : sacc[qb][jh * 8 + e] - mu);
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2 pr = {v[e], v[e + 1]};
+          ls = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2, ls, false);
         }
+        pb[qb][jh] = v;
+      }
+      l_run[qb] = ls;
+    }
+  };
+  // O^T += V^T P^T for one 32-key block.
+  auto pv = [&](const bf16* sVt, int kb, bf16x8 (&pb)[QB][2]) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int jh = 0; jh < 2; ++jh) {
+        const bf16x8 a =
+            *(const bf16x8*)(sVt + (db * 32 + l32) * VW + kb * 32 + jh * 16 + hi * 8);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) mfma_acc(oacc[qb][db], a, pb[qb][jh]);
       }
     }
   };
+  // One 64-key tile from LDS buffer `buf`. With two query blocks per wave the two 32-key
+  // halves go one after the other (32 score registers live per block); with one query
+  // block the halves form two independent MFMA chains. `mid` runs between the score
+  // work and the P.V products (the global path stages the next tile there).
+  auto compute = [&](int kt, int buf, auto masked_tag, auto&& mid) {
+    const bf16* sK = (const bf16*)(smem + buf * S::kBuf);
+    const bf16* sVt = (const bf16*)(smem + buf * S::kBuf + S::kK);
+    const int k0 = kt * kBN;
+    int rel[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) rel[qb] = qpos[qb] - k0 - 4 * hi;
+    if constexpr (QB == 1) {
+      f32x16 s0[1], s1[1];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s0[0][r] = 0.f;
+        s1[0][r] = 0.f;
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 a0 = *(const bf16x8*)(sK + l32 * RW + ks * 16 + hi * 8);
+        const bf16x8 a1 = *(const bf16x8*)(sK + (32 + l32) * RW + ks * 16 + hi * 8);
+        s0[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[0][ks], s0[0], 0, 0, 0);
+        s1[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[0][ks], s1[0], 0, 0, 0);
+      }
+      bf16x8 p0[1][2], p1[1][2];
+      probs(s0, 0, rel, p0, masked_tag);
+      probs(s1, 1, rel, p1, masked_tag);
+      mid();
+      pv(sVt, 0, p0);
+      pv(sVt, 1, p1);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x16 sacc[QB];
+        qk(sK, kb, sacc);
+        bf16x8 pb[QB][2];
+        probs(sacc, kb, rel, pb, masked_tag);
+        if (kb == 0) mid();
+        pv(sVt, kb, pb);
+      }
+    }
+  };
+  auto nothing = [] {};
 
-  // One tile: stage the prefetched data, transform K (fused path), prefetch the next
-  // tile, compute. The unmasked and masked stretches are separate loops so that the
-  // accumulators follow one register assignment around each loop.
-  auto step = [&](int i, auto masked_tag) {
-    const int kt = tile_of(i);
-    const int buf = i & 1;
-    stage(kt, buf);
-    __syncthreads();  // tile i is in LDS; every wave is done with tile i - 2's buffer
-    if (!KPRE) {
-      // Fused K transform: 4 threads per key row, raw -> this tile's K~ buffer.
+  int i = 0;
+  if constexpr (KPRE) {
+    // K~ comes ready-made: tile i + 1 is written to the other LDS buffer and tile i + 2
+    // is fetched while tile i is computed, leaving one barrier per tile.
+    fetch(tile_of(0));
+    stage(tile_of(0), 0);
+    if (n_tiles > 1) fetch(tile_of(1));
+    __syncthreads();
+    auto step = [&](int i, auto masked_tag) {
+      compute(tile_of(i), i & 1, masked_tag, [&] {
+        if (i + 1 < n_tiles) stage(tile_of(i + 1), (i + 1) & 1);
+        if (i + 2 < n_tiles) fetch(tile_of(i + 2));
+      });
+      __syncthreads();  // tile i + 1 is in LDS; tile i's buffer may be overwritten
+    };
+    for (; i < n_unm; ++i) step(i, std::integral_constant<bool, false>{});
+    for (; i < n_tiles; ++i) step(i, std::integral_constant<bool, true>{});
+  } else {
+    // Fused K transform: stage the raw tile, transform it into the K~ buffer, compute.
+    auto step = [&](int i, auto masked_tag) {
+      const int kt = tile_of(i);
+      const int buf = i & 1;
+      stage(kt, buf);
+      __syncthreads();  // tile i is in LDS; every wave is done with tile i - 2's buffer
       bf16* sK = (bf16*)(smem + buf * S::kBuf);
-      const int kr = tid >> 2, sub = tid & 3;
+      const int kr = tid / TPR, sub = tid % TPR;
       const bf16* r = sKraw + kr * RW;
       float ss = 0.f;
 #pragma unroll
-      for (int c = 0; c < D / 32; ++c) {
-        const u32x4 v = *(const u32x4*)(r + (sub * (D / 32) + c) * 8);
+      for (int c = 0; c < DC / TPR; ++c) {
+        const u32x4 v = *(const u32x4*)(r + (sub * (DC / TPR) + c) * 8);
         const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -491,30 +555,29 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const KArgs p
           ss = __builtin_fmaf(bb, bb, ss);
         }
       }
-      ss += __shfl_xor(ss, 1);
-      ss += __shfl_xor(ss, 2);
+#pragma unroll
+      for (int o = 1; o < TPR; o <<= 1) ss += __shfl_xor(ss, o);
       const float rn = __builtin_amdgcn_rsqf(ss * (1.0f / D) + p.eps);
       transform_row<D>(r, sK + kr * RW, sWk, sKtrig + kr * kMaxHalfMfma, rn, 1.0f, p.rdim,
-                       sub, 4);
+                       sub, TPR);
       __syncthreads();  // K~ ready; sKraw / sKtrig free for the next stage()
-    }
-    if (i + 1 < n_tiles) fetch(tile_of(i + 1));  // in flight during this tile's math
-    compute(kt, buf, masked_tag);
-  };
-  fetch(tile_of(0));
-  int i = 0;
-  for (; i < n_unm; ++i) step(i, std::integral_constant<bool, false>{});
-  for (; i < n_tiles; ++i) step(i, std::integral_constant<bool, true>{});
+      if (i + 1 < n_tiles) fetch(tile_of(i + 1));  // in flight during this tile's math
+      compute(kt, buf, masked_tag, nothing);
+    };
+    fetch(tile_of(0));
+    for (; i < n_unm; ++i) step(i, std::integral_constant<bool, false>{});
+    for (; i < n_tiles; ++i) step(i, std::integral_constant<bool, true>{});
+  }
 
   // ---- Epilogue: O = acc / l (* sigmoid(G)), bf16 store ------------------------------
-  acc_fence<DB>(oacc);
+  acc_fence<QB, DB>(oacc);
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32);
     const int pos = qpos[qb];
     if (pos >= T) continue;
     const float inv = 1.0f / lt;
-    const int hg = (wave * 2 + qb) / bpp;
+    const int hg = (wave * QB + qb) / bpp;
     const int h = kvh * p.group + hg;
     const size_t rowoff = (((size_t)b * T + pos) * p.Hq + h) * D;
 #pragma unroll
@@ -539,13 +602,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(const KArgs p
   }
 }
 
-template <int D, bool SWA, bool KPRE>
+template <int D, bool SWA, bool KPRE, int NW = kWavesPerBlock>
 hipError_t launch_t(const KArgs& ka, int n_blocks, hipStream_t s) {
   constexpr int smem = Smem<D>::kTotal;
+  constexpr int kThreads = NW * 64;
   // Both variants are launched; each returns immediately unless the score bound
   // (computed on the device from the norm weights) selects it.
-  auto k_static = prefill_bf16_kernel<D, SWA, KPRE, true>;
-  auto k_online = prefill_bf16_kernel<D, SWA, KPRE, false>;
+  auto k_static = prefill_bf16_kernel<D, SWA, KPRE, true, NW>;
+  auto k_online = prefill_bf16_kernel<D, SWA, KPRE, false, NW>;
   hipError_t e = hipFuncSetAttribute((const void*)k_static,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, smem);
   if (e != hipSuccess) return e;
