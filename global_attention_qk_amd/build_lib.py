@@ -39,7 +39,8 @@ def common_flags():
             # MFMAs issued through builtins write VGPRs (scores feed the VALU softmax);
             # the output accumulators are pinned to AGPRs explicitly.
             "-mllvm", "-amdgpu-mfma-vgpr-form",
-            "-I", INCLUDE, "-I", CSRC, "-Wno-unused-command-line-argument"]
+            "-I", INCLUDE, "-I", CSRC, "-Wno-unused-command-line-argument"
+            ] + os.environ.get("ZGATTN_HIPCC_FLAGS", "").split()
 
 
 def _compile(src: str) -> str:

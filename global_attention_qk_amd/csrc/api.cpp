@@ -73,6 +73,7 @@ PrefillArgs make_prefill(const zgattn_desc* d, const void* q, const void* k, con
   a.wq = wq;
   a.wk = wk;
   a.kt = nullptr;
+  a.vt = nullptr;
   a.B = d->batch;
   a.T = d->seq_len;
   a.Hq = d->n_q_heads;
@@ -174,7 +175,10 @@ int zgattn_swa_prefill(const zgattn_desc* d, const void* q, const void* k, const
 size_t zgattn_global_prefill_workspace_bytes(const zgattn_desc* d) {
   if (check_desc(d) || d->seq_len < 0) return 0;
   if (d->dtype != ZGATTN_BF16) return 0;
-  return (size_t)d->batch * d->n_kv_heads * (size_t)d->seq_len * d->head_dim * 2;
+  // normalised+rotated K, then V as transposed 64-key tiles (256-byte aligned)
+  const size_t kbytes = (size_t)d->batch * d->n_kv_heads * (size_t)d->seq_len * d->head_dim * 2;
+  return ((kbytes + 255) & ~(size_t)255) +
+         prefill_vtiles_bytes(d->batch, d->n_kv_heads, d->seq_len, d->head_dim);
 }
 
 int zgattn_global_prefill(const zgattn_desc* d, const void* q, const void* k, const void* v,
@@ -211,6 +215,10 @@ int zgattn_global_prefill(const zgattn_desc* d, const void* q, const void* k, co
     hipError_t e = launch_qknorm_rope(n, s);
     if (e != hipSuccess) return ZGATTN_EHIP;
     a.kt = (bf16*)workspace;
+    const size_t kbytes = (size_t)a.B * a.Hkv * (size_t)a.T * a.d * 2;
+    a.vt = (bf16*)((char*)workspace + ((kbytes + 255) & ~(size_t)255));
+    e = launch_v_tiles(a, s);
+    if (e != hipSuccess) return ZGATTN_EHIP;
   }
   return hip_status(launch_prefill_bf16(a, s));
 }

@@ -19,6 +19,7 @@ struct PrefillArgs {
   const float* wq;
   const float* wk;
   bf16* kt;           // normalised+rotated K, [B][Hkv][T][d] (global with workspace) or nullptr
+  bf16* vt;           // V as transposed 64-key tiles (with kt), see launch_v_tiles
   int B, T, Hq, Hkv, d, window, rdim, pos_offset;
   int swa;            // 1: gated sliding window; 0: ungated full causal
   float eps;
@@ -29,6 +30,9 @@ struct PrefillArgs {
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 bool prefill_bf16_supported(int d, int group, int rdim);
+// Tile-transposed V for the global path: [B][Hkv][ceil(T/64)][d][64] bf16.
+size_t prefill_vtiles_bytes(int B, int Hkv, int T, int d);
+hipError_t launch_v_tiles(const PrefillArgs& a, hipStream_t s);
 
 // Standalone QK-RMSNorm + partial RoPE with strided output.
 struct NormRopeArgs {

@@ -75,6 +75,7 @@ struct KArgs {
   const float* wq;
   const float* wk;
   const bf16* kt;
+  const bf16* vt;     // tile-transposed V (with kt), see v_tiles_kernel
   int T, Hq, Hkv, window, rdim, pos_offset;
   int group, bmp, n_qtiles, n_hb;
   float eps, qscale;
@@ -91,6 +92,17 @@ __device__ __forceinline__ int vt_slot(int key) {
 // wait states a VALU-written operand (P) needs before an MFMA may read it.
 __device__ __forceinline__ void mfma_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+#ifndef ZG_PREFILL_PIPE
+#define ZG_PREFILL_PIPE 1
+#endif
+#ifndef ZG_PREFILL_SETPRIO
+#define ZG_PREFILL_SETPRIO 0
+#endif
+template <int P>
+__device__ __forceinline__ void set_prio() {
+  if (ZG_PREFILL_SETPRIO) __builtin_amdgcn_s_setprio(P);
 }
 
 // Keep a value in AGPRs from here on (so that loop-carried accumulators never take a
@@ -158,7 +170,8 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
   constexpr int VW = S::kVtRowB / 2;
   constexpr int DC = D / 8;                     // 16-byte chunks per row
   constexpr int KIT = (kBN * DC) / kThreads;    // K chunks per thread per tile
-  constexpr int VCH = (kBN / 4) * DC;           // threads that carry V (4 keys x 8 dims)
+  constexpr int KG = (kBN * DC) / kThreads;     // keys per thread in the V transpose
+  static_assert(KG == 1 || KG == 2 || KG == 4, "V staging expects 1, 2 or 4 keys per thread");
 
   extern __shared__ __attribute__((aligned(16))) char smem[];
   bf16* sQ = (bf16*)smem;
@@ -272,8 +285,11 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
   // ---- Key-tile schedule ----------------------------------------------------------------
   // Tiles [kt_lo, kt_hi] meet the band. Unmasked tiles are those entirely below every
   // query of the tile (k0 + 63 <= i0) and, for SWA, entirely inside every query's window
-  // (k0 > q_last - W). They run first, as one branch-free stretch; the masked tiles
-  // (diagonal, band edge) follow.
+  // (k0 > q_last - W). They run first, as one branch-free stretch in ascending key order
+  // (the workgroups of one KV head, which share an XCD, then stream the same K/V tiles
+  // at about the same time and hit in L2); the masked tiles (diagonal, band edge)
+  // follow. Unmasked tiles are fully visible to every row, so the first tile always
+  // gives the online variant a finite running max.
   const int q_last = min(i0 + p.bmp, T) - 1;
   const int kt_lo = SWA ? max(0, i0 - p.window + 1) / kBN : 0;
   const int kt_hi = q_last / kBN;
@@ -288,7 +304,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
   const int n_hi_m = kt_hi - u_hi;
   const int n_tiles = kt_hi - kt_lo + 1;
   auto tile_of = [&](int i) -> int {
-    if (i < n_unm) return u_hi - i;
+    if (i < n_unm) return u_lo + i;
     i -= n_unm;
     if (i < n_hi_m) return u_hi + 1 + i;
     return kt_lo + (i - n_hi_m);
@@ -315,13 +331,15 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
   const bf16* kbase = p.k + ((size_t)b * T * p.Hkv + kvh) * D;
   const bf16* vbase = p.v + ((size_t)b * T * p.Hkv + kvh) * D;
   const bf16* ktsrc = KPRE ? p.kt + (((size_t)b * p.Hkv + kvh) * T) * D : nullptr;
+  const int n_kt = (T + kBN - 1) / kBN;
+  const bf16* vtsrc = KPRE ? p.vt + ((size_t)b * p.Hkv + kvh) * n_kt * (size_t)(kBN * D) : nullptr;
   const size_t kvstride = (size_t)p.Hkv * D;
 
   // Global -> registers for tile kt (issued one tile ahead of its use). Rows past the
   // end are clamped to the last row: such keys are always masked out, and clamped
   // values keep the products finite.
   u32x4 kreg[KIT];
-  u32x4 vreg[4];
+  u32x4 vreg[KG];
   auto fetch = [&](int kt) {
     const int k0 = kt * kBN;
 #pragma unroll
@@ -332,12 +350,18 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
       kreg[it] = KPRE ? *(const u32x4*)(ktsrc + (size_t)pos * D + dc * 8)
                       : *(const u32x4*)(kbase + (size_t)pos * kvstride + dc * 8);
     }
-    if (tid < VCH) {
-      const int kg = tid % (kBN / 4), dc = tid / (kBN / 4);  // key group fastest: the
-      // transposed 8-byte LDS writes of one instruction then cover all banks
+    if constexpr (KPRE) {
+      // pre-transposed tile: [D][64 keys] rows of 8 chunks, copied as they are
+      const bf16* src = vtsrc + (size_t)kt * (kBN * D);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int pos = min(k0 + kg * 4 + e, T - 1);
+      for (int it = 0; it < KG; ++it) vreg[it] = *(const u32x4*)(src + (tid + it * kThreads) * 8);
+    } else {
+      // every thread carries KG keys x 8 dims of V; the key group is the fastest index
+      // so that the transposed LDS writes of one instruction cover all banks
+      const int kg = tid % (kBN / KG), dc = tid / (kBN / KG);
+#pragma unroll
+      for (int e = 0; e < KG; ++e) {
+        const int pos = min(k0 + kg * KG + e, T - 1);
         vreg[e] = *(const u32x4*)(vbase + (size_t)pos * kvstride + dc * 8);
       }
     }
@@ -354,24 +378,30 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
       const int kr = c / DC, dc = c % DC;
       *(u32x4*)((KPRE ? sK : sKraw) + kr * RW + dc * 8) = kreg[it];
     }
-    if (tid < VCH) {
-      const int kg = tid % (kBN / 4), dc = tid / (kBN / 4);  // key group fastest: the
-      // transposed 8-byte LDS writes of one instruction then cover all banks
-      const int slot = vt_slot(kg * 4);
+    if constexpr (KPRE) {
+#pragma unroll
+      for (int it = 0; it < KG; ++it) {
+        const int c = tid + it * kThreads;   // chunk c: row d = c / 8, 8 slots (c % 8)*8..
+        *(u32x4*)(sVt + (c >> 3) * VW + (c & 7) * 8) = vreg[it];
+      }
+    } else {
+      const int kg = tid % (kBN / KG), dc = tid / (kBN / KG);
+      const int slot = vt_slot(kg * KG);   // KG consecutive keys keep consecutive slots
 #pragma unroll
       for (int dd = 0; dd < 8; ++dd) {
         const int wsel = dd >> 1;
-        const uint32_t e0 = vreg[0][wsel], e1 = vreg[1][wsel];
-        const uint32_t e2 = vreg[2][wsel], e3 = vreg[3][wsel];
-        uint32_t lo01, lo23;
-        if (dd & 1) {
-          lo01 = (e0 >> 16) | (e1 & 0xffff0000u);
-          lo23 = (e2 >> 16) | (e3 & 0xffff0000u);
+        uint32_t h[KG];   // element dd of each key, in the low 16 bits
+#pragma unroll
+        for (int e = 0; e < KG; ++e)
+          h[e] = (dd & 1) ? (vreg[e][wsel] >> 16) : (vreg[e][wsel] & 0xffffu);
+        bf16* dst = sVt + (dc * 8 + dd) * VW + slot;
+        if constexpr (KG == 4) {
+          *(u32x2*)dst = (u32x2){h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+        } else if constexpr (KG == 2) {
+          *(uint32_t*)dst = h[0] | (h[1] << 16);
         } else {
-          lo01 = (e0 & 0xffffu) | (e1 << 16);
-          lo23 = (e2 & 0xffffu) | (e3 << 16);
+          *(uint16_t*)dst = (uint16_t)h[0];
         }
-        *(u32x2*)(sVt + (dc * 8 + dd) * VW + slot) = (u32x2){lo01, lo23};
       }
     }
     if (!KPRE) {
@@ -489,6 +519,10 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
         s0[0][r] = 0.f;
         s1[0][r] = 0.f;
       }
+      // The two waves sharing a SIMD run the same phases; raising the priority in the
+      // MFMA phases lets the MFMA issuer win arbitration while the other wave's
+      // softmax fills the gaps.
+      set_prio<1>();
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const bf16x8 a0 = *(const bf16x8*)(sK + l32 * RW + ks * 16 + hi * 8);
@@ -496,12 +530,46 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
         s0[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[0][ks], s0[0], 0, 0, 0);
         s1[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[0][ks], s1[0], 0, 0, 0);
       }
+      set_prio<0>();
       bf16x8 p0[1][2], p1[1][2];
       probs(s0, 0, rel, p0, masked_tag);
       probs(s1, 1, rel, p1, masked_tag);
       mid();
+      set_prio<1>();
       pv(sVt, 0, p0);
       pv(sVt, 1, p1);
+      set_prio<0>();
+    } else if constexpr (ZG_PREFILL_PIPE) {
+      // Software pipeline within the tile, one wave per SIMD:
+      //   QK(0) | QK(1) with softmax(0) | P.V(0) with softmax(1) | P.V(1)
+      // so that each softmax phase runs under a stretch of independent MFMAs.
+      f32x16 s0[QB], s1[QB];
+      bf16x8 p0[QB][2], p1[QB][2];
+      qk(sK, 0, s0);
+      qk(sK, 1, s1);
+      probs(s0, 0, rel, p0, masked_tag);
+      mid();
+      pv(sVt, 0, p0);
+      probs(s1, 1, rel, p1, masked_tag);
+      pv(sVt, 1, p1);
+      constexpr int kQK = QB * KS;       // MFMAs of one 32-key score block
+      constexpr int kPV = QB * DB * 2;   // MFMAs of one 32-key P.V block
+      constexpr int kSM = QB * 32;       // VALU ops of one softmax block (exp, cvt, dot)
+      // mask bits: 0x8 MFMA, 0x2 VALU, 0x400 transcendental, 0x100 LDS read
+#pragma unroll
+      for (int j = 0; j < kQK; ++j) __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);
+#pragma unroll
+      for (int j = 0; j < kQK; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, kSM / kQK, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < kPV; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, kSM / kPV, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < kPV; ++j) __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);
     } else {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -525,9 +593,11 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
     if (n_tiles > 1) fetch(tile_of(1));
     __syncthreads();
     auto step = [&](int i, auto masked_tag) {
+      // Branch-free: past the end, the last tile is re-staged into the idle buffer and
+      // re-fetched (in-bounds and never read), so the loop body is one basic block.
       compute(tile_of(i), i & 1, masked_tag, [&] {
-        if (i + 1 < n_tiles) stage(tile_of(i + 1), (i + 1) & 1);
-        if (i + 2 < n_tiles) fetch(tile_of(i + 2));
+        stage(tile_of(min(i + 1, n_tiles - 1)), (i + 1) & 1);
+        fetch(tile_of(min(i + 2, n_tiles - 1)));
       });
       __syncthreads();  // tile i + 1 is in LDS; tile i's buffer may be overwritten
     };
@@ -621,6 +691,35 @@ hipError_t launch_t(const KArgs& ka, int n_blocks, hipStream_t s) {
   return hipGetLastError();
 }
 
+
+// V tile transpose for the global path: V [B, T, Hkv, D] -> vt [B, Hkv, ceil(T/64), D, 64]
+// with the 64 keys of each row in the slot order of the LDS V^T tile (keys past T are 0).
+// The attention kernel then stages V^T tiles with plain 16-byte copies.
+template <int D>
+__global__ __launch_bounds__(256) void v_tiles_kernel(const bf16* v, bf16* vt, int T, int Hkv,
+                                                      int n_kt) {
+  __shared__ __attribute__((aligned(16))) bf16 s[kBN][D + 8];
+  const int tile = blockIdx.x, hb = blockIdx.y;
+  const int b = hb / Hkv, kvh = hb % Hkv;
+  const int tid = threadIdx.x;
+  for (int c = tid; c < kBN * (D / 8); c += 256) {
+    const int kr = c / (D / 8), dc = c % (D / 8);
+    const int pos = tile * kBN + kr;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (pos < T) val = *(const u32x4*)(v + (((size_t)b * T + pos) * Hkv + kvh) * D + dc * 8);
+    *(u32x4*)&s[kr][dc * 8] = val;
+  }
+  __syncthreads();
+  bf16* out = vt + ((size_t)hb * n_kt + tile) * (kBN * D);
+  for (int c = tid; c < D * (kBN / 8); c += 256) {
+    const int d = c / (kBN / 8), sc = c % (kBN / 8);
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = s[vt_slot(sc * 8 + e)][d];  // the slot map is an involution
+    *(bf16x8*)(out + d * kBN + sc * 8) = o;
+  }
+}
+
 }  // namespace
 
 bool prefill_bf16_supported(int d, int group, int rdim) {
@@ -640,6 +739,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
   ka.wq = a.wq;
   ka.wk = a.wk;
   ka.kt = a.kt;
+  ka.vt = a.vt;
   ka.T = a.T;
   ka.Hq = a.Hq;
   ka.Hkv = a.Hkv;
@@ -664,6 +764,27 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
   if (a.swa) return launch_t<64, true, false>(ka, n_blocks, s);
   return kpre ? launch_t<64, false, true>(ka, n_blocks, s)
               : launch_t<64, false, false>(ka, n_blocks, s);
+}
+
+}  // namespace zg
+
+namespace zg {
+
+size_t prefill_vtiles_bytes(int B, int Hkv, int T, int d) {
+  return (size_t)B * Hkv * ((T + kBN - 1) / kBN) * kBN * d * 2;
+}
+
+hipError_t launch_v_tiles(const PrefillArgs& a, hipStream_t s) {
+  const int n_kt = (a.T + kBN - 1) / kBN;
+  const dim3 grid(n_kt, a.B * a.Hkv);
+  if (n_kt == 0) return hipSuccess;
+  if (a.d == 128)
+    hipLaunchKernelGGL(v_tiles_kernel<128>, grid, dim3(256), 0, s, (const bf16*)a.v, a.vt, a.T,
+                       a.Hkv, n_kt);
+  else
+    hipLaunchKernelGGL(v_tiles_kernel<64>, grid, dim3(256), 0, s, (const bf16*)a.v, a.vt, a.T,
+                       a.Hkv, n_kt);
+  return hipGetLastError();
 }
 
 }  // namespace zg
