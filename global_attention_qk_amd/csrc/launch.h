@@ -33,6 +33,10 @@ bool prefill_bf16_supported(int d, int group, int rdim);
 // Tile-transposed V for the global path: [B][Hkv][ceil(T/64)][d][64] bf16.
 size_t prefill_vtiles_bytes(int B, int Hkv, int T, int d);
 hipError_t launch_v_tiles(const PrefillArgs& a, hipStream_t s);
+// Streaming sliding-window kernel for the model's layer shape (d 128, 4 query heads per KV
+// head, rotary_dim 42, window <= 128); launch_prefill_bf16 routes such calls to it.
+bool swa_stream_supported(const PrefillArgs& a);
+hipError_t launch_swa_stream(const PrefillArgs& a, hipStream_t s);
 
 // Standalone QK-RMSNorm + partial RoPE with strided output.
 struct NormRopeArgs {

@@ -755,6 +755,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
   ka.fr = a.fr;
   const int n_blocks = ka.n_qtiles * ka.n_hb;
   if (n_blocks == 0) return hipSuccess;
+  if (swa_stream_supported(a)) return launch_swa_stream(a, s);
   const bool kpre = (a.kt != nullptr);
   if (a.d == 128) {
     if (a.swa) return launch_t<128, true, false>(ka, n_blocks, s);
