@@ -8,25 +8,28 @@
 //
 // Such a layer reads Q, K, V and G once and writes O once (28 KiB per position at 32
 // query / 8 KV heads), while its MFMA work is small: it is bound by HBM bandwidth, and the
-// design aims at keeping loads in flight rather than at MFMA throughput.
+// design aims at keeping loads in flight and the vector ALUs' latency hidden.
 //
-//   * A workgroup (8 wave64s) owns one (batch, KV head) and a contiguous segment of the
-//     sequence, which it walks 64 positions per step. The 256 query rows of a step are the
-//     4 heads x 64 positions; wave w takes head w % 4 and the 32 positions 32 * (w / 4) ..
-//     of the step, one query per lane (scores are formed transposed, S^T = K~ Q~^T, so P
-//     lands in the B-operand layout of O^T += V^T P^T).
-//   * K~ (normalised, rotated) and V^T live in LDS as a ring of six 32-key blocks: each
-//     key block is loaded from HBM, transformed and transposed once per segment, and each
-//     wave reads the five blocks its window touches (one band-edge block, three full
-//     blocks, the diagonal block).
-//   * Loads run ahead of use: the next step's Q goes straight into registers in the MFMA
-//     operand layout, the next key tile into registers and then LDS, and the gate of the
-//     current step is issued at the step's start so that it has landed by the epilogue.
+//   * A workgroup (8 wave64s, two per SIMD) owns one (batch, KV head) and a contiguous
+//     segment of the sequence, which it walks 32 positions per step. Wave w takes query
+//     head w % 4 at the 16 positions 16 * (w / 4) .. of the step. Products run on
+//     v_mfma_f32_16x16x32_bf16 with scores formed transposed (S^T = K~ Q~^T: keys on M,
+//     queries on N), so each lane holds one query and P lands in the B-operand layout of
+//     O^T += V^T P^T.
+//   * K~ (normalised, rotated) and V^T live in LDS as a ring of six 32-key blocks: each key
+//     block is loaded from HBM, transformed and transposed once per segment, and each wave
+//     reads the five blocks its window touches (one band-edge block, three full blocks,
+//     the diagonal block). Step s writes block s + 1 into the slot of block s - 5, so a
+//     single barrier per step orders the ring, the raw-K staging and the RoPE tables.
+//   * Loads run one step ahead: Q and G of the next step go straight into registers in
+//     the MFMA operand / accumulator layouts, the next K and V tiles into registers, and
+//     every load of a step is consumed at the top of the next step, before that step's
+//     own loads and stores are issued.
 //   * Head dims are permuted inside the products (the same permutation on both operands
-//     of each product): in Q~ . K~ a lane's two halves hold dims [0, 64) and [64, 128),
-//     so the rotated pairs (j, j + 21) never cross lanes; in O^T the V^T rows are ordered
-//     so that a lane's sixteen accumulator registers of a 32-dim block are sixteen
-//     consecutive dims, which makes the G loads and O stores 16-byte accesses.
+//     of each product): lane group g (lanes 16 g .. 16 g + 15) holds dims [32 g, 32 g + 32)
+//     of its query in Q~ and in O^T, so Q and G are loaded and O stored with 16-byte
+//     accesses, and of the rotated pairs (j, j + 21) only j = 11 .. 20 cross lane groups
+//     (exchanged with one swizzle).
 //   * Static softmax shift as in the other prefill kernel: when the score bound implied
 //     by the norm weights is moderate, p = exp2(s) with no running max; otherwise an
 //     online-max variant runs (both are launched; each returns unless selected).
@@ -41,27 +44,28 @@ constexpr int kD = 128;
 constexpr int kG = 4;              // query heads per KV head
 constexpr int kRH = 21;            // rotated pairs (rotary_dim 42)
 constexpr int kRHP = 22;           // trig table row stride (16-byte aligned rows)
-constexpr int kStep = 64;          // positions per step
-constexpr int kBK = 32;            // keys per ring block
+constexpr int kStep = 32;          // positions per step (= keys per ring block)
 constexpr int kRing = 6;           // ring blocks
-constexpr int kNB = 5;             // blocks a 32-row wave visits per step (window <= 128)
-constexpr int kThreads = 512;
+constexpr int kNB = 5;             // blocks a wave visits per step (window <= 128)
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxWindow = 128;
-constexpr int kMinSegSteps = 4;
+constexpr int kMinSegSteps = 8;
+constexpr int kTrigBufs = 3;
 constexpr float kStaticShiftMax = 96.0f;
 
-constexpr int kKRowB = kD * 2 + 16;        // padded K~ row
-constexpr int kKBlkB = kBK * kKRowB;       // K~ block: 32 rows
-constexpr int kVBlkB = kD * kBK * 2;       // V^T block: 128 rows x 64 B
-constexpr int kRawRowB = kD * 2 + 16;      // padded raw K row
-constexpr int kRawB = kStep * kRawRowB;
+constexpr int kKRowB = kD * 2 + 16;        // padded K~ / raw K row
+constexpr int kKBlkB = kStep * kKRowB;     // K~ block: 32 rows
+constexpr int kVBlkB = kD * kStep * 2;     // V^T block: 128 rows x 64 B
+constexpr int kRawB = kStep * kKRowB;
 constexpr int kTrigB = kStep * kRHP * 8;
 constexpr int kOffK = 0;
 constexpr int kOffV = kOffK + kRing * kKBlkB;
-constexpr int kOffRaw = kOffV + kRing * kVBlkB;   // two raw K buffers
-constexpr int kOffTrig = kOffRaw + 2 * kRawB;     // two trig tables
-constexpr int kOffW = kOffTrig + 2 * kTrigB;      // wq * qscale, wk
-constexpr int kSmem = kOffW + 2 * kD * 4;
+constexpr int kOffRaw = kOffV + kRing * kVBlkB;       // two raw K buffers
+constexpr int kOffTrig = kOffRaw + 2 * kRawB;         // three trig tables
+constexpr int kOffW = kOffTrig + kTrigBufs * kTrigB;  // wq * qscale, wk
+constexpr int kOffFr = kOffW + 2 * kD * 4;            // RoPE frequencies (hi, lo)
+constexpr int kSmem = kOffFr + 2 * 32 * 4;
 static_assert(kSmem <= 160 * 1024, "LDS budget");
 
 struct SArgs {
@@ -78,30 +82,28 @@ struct SArgs {
   RopeFreq fr;
 };
 
-__device__ __forceinline__ int ring_slot(int kb) { return (kb + 4 * kRing) % kRing; }  // kb >= -4
+__device__ __forceinline__ int ring_slot(int kb) { return (kb + 4 * kRing) % kRing; }  // kb >= -24
 
-// K~ block: rows padded by 16 bytes, so one 16-byte chunk read across 16 consecutive keys
-// touches every bank once, and a lane's chunks are one base plus immediate offsets.
-__device__ __forceinline__ int kblk_off(int row, int chunk) { return row * kKRowB + (chunk << 4); }
+// Padded rows: one 16-byte chunk read across 16 consecutive keys touches every bank once,
+// and a lane's chunks are one base plus immediate offsets.
+__device__ __forceinline__ int krow_off(int row, int chunk) { return row * kKRowB + (chunk << 4); }
 // V^T block: row m (0..127) holds 32 key slots (64 B); chunk c at c ^ ((m >> 2) & 3).
 __device__ __forceinline__ int vblk_off(int m, int chunk) {
-  return m * (kBK * 2) + ((chunk ^ ((m >> 2) & 3)) << 4);
+  return m * (kStep * 2) + ((chunk ^ ((m >> 2) & 3)) << 4);
 }
-// Row of a 32-dim block that holds dim dd: rows are ordered so that accumulator register
-// r of lane half h is dim 16 h + r.
-__device__ __forceinline__ int vt_row_of_dim(int dd) {
-  return 8 * ((dd >> 2) & 3) + 4 * (dd >> 4) + (dd & 3);
+// V^T row holding dim d: accumulator register r of 16-row block db in lane group g is
+// dim 32 g + 4 db + r.
+__device__ __forceinline__ int vt_row_of_dim(int d) {
+  return 16 * ((d >> 2) & 7) + 4 * (d >> 5) + (d & 3);
 }
-// Swap bits 2 and 3 of a key index within its 16-key group (which keys a lane holds in
-// the S^T accumulator, in B-operand order).
-__device__ __forceinline__ int key_slot(int key) {
-  return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+// V^T slot of key k (0..31): slot 8 g + e holds the key that lane group g's P value e
+// stands for, 16 (e / 4) + 4 g + e % 4.
+__device__ __forceinline__ int key_slot(int k) {
+  return (((k >> 2) & 3) << 3) | (((k >> 4) & 1) << 2) | (k & 3);
 }
 
-// All accumulators are VGPRs (no AGPRs are used, so the compiler may give the whole
-// 256-register budget of two waves per SIMD to VGPRs).
-__device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 // A value the optimiser must treat as recomputed here: keeps lane-derived indices from
@@ -111,17 +113,39 @@ __device__ __forceinline__ int opaque(int x) {
   return x;
 }
 
-// Sum over the 8 lanes of an aligned lane octet (DPP: xor 1, xor 2, then mirror within 8).
-__device__ __forceinline__ float octet_sum(float x) {
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+// Sum over the 16 lanes of a DPP row: xor 1, xor 2, mirror within 8, mirror within 16.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp<0xB1>(x);
+  x += dpp<0x4E>(x);
+  x += dpp<0x141>(x);
+  x += dpp<0x140>(x);
   return x;
+}
+// Lane l <-> lane l ^ 16 (within each half of the wave).
+__device__ __forceinline__ uint32_t swap16(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x401F);
+}
+__device__ __forceinline__ float swap16f(float x) { return __uint_as_float(swap16(__float_as_uint(x))); }
+// Sum over the four lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48).
+__device__ __forceinline__ float group_sum(float x) {
+  x += swap16f(x);
+  return x + __shfl_xor(x, 32);
+}
+__device__ __forceinline__ float group_max(float x) {
+  x = fmaxf(x, swap16f(x));
+  return fmaxf(x, __shfl_xor(x, 32));
 }
 
 __device__ __forceinline__ float bf16_elem(const u32x4& v, int e) {
   const uint32_t w = v[e >> 1];
   return (e & 1) ? bf16_hi_to_f32(w) : bf16_lo_to_f32(w);
+}
+__device__ __forceinline__ float bf16_word(uint32_t w, int half) {
+  return half ? bf16_hi_to_f32(w) : bf16_lo_to_f32(w);
 }
 
 template <bool STATIC>
@@ -129,18 +153,23 @@ __global__ __launch_bounds__(kThreads, 1) void swa_stream_kernel(const SArgs p) 
   extern __shared__ __attribute__((aligned(16))) char smem[];
   float* sWq = (float*)(smem + kOffW);
   float* sWk = sWq + kD;
+  float* sFr = (float*)(smem + kOffFr);   // [0, 32): hi, [32, 64): lo
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int n = lane & 31;     // query column of this lane
-  const int hi = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hg = wave & 3;     // head within the group
-  const int ph = wave >> 2;    // which 32 positions of the step
+  const int ph = wave >> 2;    // which 16 positions of the step
+  const int n = lane & 15;     // query column of this lane
+  const int grp = lane >> 4;   // lane group: dims [32 grp, 32 grp + 32)
 
   for (int i = tid; i < kD; i += kThreads) {
     sWq[i] = p.wq[i] * p.qscale;
     sWk[i] = p.wk[i];
+  }
+  if (tid < kRH) {
+    sFr[tid] = p.fr.hi[tid];
+    sFr[32 + tid] = p.fr.lo[tid];
   }
   __syncthreads();
   {
@@ -167,86 +196,81 @@ __global__ __launch_bounds__(kThreads, 1) void swa_stream_kernel(const SArgs p) 
   const int T = p.T;
   const int W = p.window;
   const int h = kvh * kG + hg;
-  const size_t qstride = (size_t)p.Hq * kD;
+  // Wave-uniform bases with 32-bit per-lane byte offsets (one sequence of one tensor is
+  // below 4 GiB, checked on the host).
+  const uint32_t qrow_b = (uint32_t)p.Hq * kD * 2;    // bytes between positions in Q/G/O
+  const uint32_t kvrow_b = (uint32_t)p.Hkv * kD * 2;  // bytes between positions in K/V
   const size_t qoff = ((size_t)b * T * p.Hq + h) * kD;
-  const size_t kvstride = (size_t)p.Hkv * kD;
-  const bf16* kbase = p.k + ((size_t)b * T * p.Hkv + kvh) * kD;
-  const bf16* vbase = p.v + ((size_t)b * T * p.Hkv + kvh) * kD;
+  const char* qbase = (const char*)(p.q + qoff);
+  const char* gbase = (const char*)(p.g + qoff);
+  char* obase = (char*)(p.out + qoff);
+  const char* kbase = (const char*)(p.k + ((size_t)b * T * p.Hkv + kvh) * kD);
+  const char* vbase = (const char*)(p.v + ((size_t)b * T * p.Hkv + kvh) * kD);
 
   // ---- loads -----------------------------------------------------------------------
-  // Q of step s in the B-operand layout: this lane's query, dims 64 hi + 8 ks .. + 7.
-  auto load_q = [&](int s, u32x4 (&dst)[8]) {
-    const int pos = min(s * kStep + 32 * ph + n, T - 1);
-    const bf16* src = p.q + qoff + (size_t)pos * qstride + hi * 64;
+  // Q (or G) row of this lane's query at step s: dims 32 grp .. + 31, as four chunks.
+  auto load_row = [&](const char* base, int s, u32x4 (&dst)[4]) {
+    const int pos = min(s * kStep + 16 * ph + n, T - 1);
+    const uint32_t off = (uint32_t)pos * qrow_b + grp * 64;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) dst[ks] = *(const u32x4*)(src + ks * 8);
+    for (int c = 0; c < 4; ++c) dst[c] = *(const u32x4*)(base + off + c * 16);
   };
-  // G of step s in the O^T accumulator layout: dims 32 db + 16 hi .. + 15.
-  auto load_g = [&](int s, u32x4 (&dst)[4][2]) {
-    const int pos = min(s * kStep + 32 * ph + n, T - 1);
-    const bf16* src = p.g + qoff + (size_t)pos * qstride + hi * 16;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int e = 0; e < 2; ++e) dst[db][e] = *(const u32x4*)(src + db * 32 + e * 8);
-  };
-  // K and V rows of tile t (positions 64 t .., clamped into [0, T); such rows are never
-  // visible and keep every product finite). K: chunks (tid & 7) and (tid & 7) + 8 of row
-  // tid >> 3. V: rows 2 (tid & 31) and + 1, chunk tid >> 5.
-  auto load_kv = [&](int t, u32x4 (&kr)[2], u32x4 (&vr)[2]) {
-    const int k0 = t * kStep;
+  // K rows of tile t (positions 32 t .., clamped into [0, T); such rows are never visible
+  // and keep every product finite): chunk tid & 15 of row tid >> 4.
+  auto load_k = [&](int t, u32x4& kr) {
     const int tl = opaque(tid);
-    const int krow = tl >> 3, kc = tl & 7;
-    const bf16* ks = kbase + (size_t)min(max(k0 + krow, 0), T - 1) * kvstride;
-    kr[0] = *(const u32x4*)(ks + kc * 8);
-    kr[1] = *(const u32x4*)(ks + (kc + 8) * 8);
-    const int kp = tl & 31, vc = tl >> 5;
+    const int krow = tl >> 4, kc = tl & 15;
+    kr = *(const u32x4*)(kbase + (uint32_t)min(max(t * kStep + krow, 0), T - 1) * kvrow_b + kc * 16);
+  };
+  // V rows 2 (tid & 15) and + 1 of tile t, dims 4 (tid >> 4) .. + 3.
+  auto load_v = [&](int t, u32x2 (&vr)[2]) {
+    const int tl = opaque(tid);
+    const int kp = tl & 15, dq = tl >> 4;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const int pos = min(max(k0 + 2 * kp + e, 0), T - 1);
-      vr[e] = *(const u32x4*)(vbase + (size_t)pos * kvstride + vc * 8);
+      const int pos = min(max(t * kStep + 2 * kp + e, 0), T - 1);
+      vr[e] = *(const u32x2*)(vbase + (uint32_t)pos * kvrow_b + dq * 8);
     }
   };
 
   // ---- LDS producers -----------------------------------------------------------------
-  // RoPE cos/sin of the 64 positions of tile t.
-  auto make_trig = [&](int t, int buf) {
-    float2* tr = (float2*)(smem + kOffTrig + buf * kTrigB);
+  auto trig_buf = [&](int t) { return (float2*)(smem + kOffTrig + ((t + 3 * kTrigBufs) % kTrigBufs) * kTrigB); };
+  auto raw_buf = [&](int t) { return smem + kOffRaw + (t & 1) * kRawB; };
+  // RoPE cos/sin of the 32 positions of tile t.
+  auto make_trig = [&](int t) {
+    float2* tr = trig_buf(t);
     for (int e = tid; e < kStep * kRH; e += kThreads) {
       const int pl = e / kRH, j = e - pl * kRH;
       float c, s;
-      rope_cos_sin(p.pos_offset + max(t * kStep + pl, 0), p.fr.hi[j], p.fr.lo[j], c, s);
+      // frequencies from LDS: indexing the kernel arguments at run time would be a global
+      // load, and waiting for it would also wait for every prefetch issued before it
+      rope_cos_sin(p.pos_offset + max(t * kStep + pl, 0), sFr[j], sFr[32 + j], c, s);
       tr[pl * kRHP + j] = make_float2(c, s);
     }
   };
-  auto stage_k = [&](const u32x4 (&kr)[2], int buf) {
-    char* raw = smem + kOffRaw + buf * kRawB;
-    const int t8 = opaque(tid);
-    const int krow = t8 >> 3, kc = t8 & 7;
-    *(u32x4*)(raw + krow * kRawRowB + kc * 16) = kr[0];
-    *(u32x4*)(raw + krow * kRawRowB + (kc + 8) * 16) = kr[1];
+  auto stage_k = [&](const u32x4& kr, int t) {
+    const int tl = opaque(tid);
+    *(u32x4*)(raw_buf(t) + krow_off(tl >> 4, tl & 15)) = kr;
   };
-  // RMSNorm + partial RoPE of the staged tile t into its two ring blocks. Eight lanes per
-  // key; a lane writes dims 8 kc .. + 7 (rotated where < 42, partner read from the raw
-  // row) and 64 + 8 kc .. + 7 (never rotated).
-  auto transform_k = [&](const u32x4 (&kr)[2], int t, int buf) {
-    const char* raw = smem + kOffRaw + buf * kRawB;
-    const float2* tr = (const float2*)(smem + kOffTrig + buf * kTrigB);
-    const int t8 = opaque(tid);
-    const int krow = t8 >> 3, kc = t8 & 7;
-    float x0[8], x1[8];
+  // RMSNorm + partial RoPE of staged tile t into its ring block: 16 lanes per key, lane
+  // kc writes dims 8 kc .. + 7 (rotated where < 42, the partner read from the raw row).
+  auto transform_k = [&](int t) {
+    const char* raw = raw_buf(t);
+    const float2* tr = trig_buf(t);
+    const int tl = opaque(tid);
+    const int krow = tl >> 4, kc = tl & 15;
+    const u32x4 r0 = *(const u32x4*)(raw + krow_off(krow, kc));
+    float x[8];
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      x0[e] = bf16_elem(kr[0], e);
-      x1[e] = bf16_elem(kr[1], e);
-      ss = __builtin_fmaf(x0[e], x0[e], ss);
-      ss = __builtin_fmaf(x1[e], x1[e], ss);
+      x[e] = bf16_elem(r0, e);
+      ss = __builtin_fmaf(x[e], x[e], ss);
     }
-    ss = octet_sum(ss);
+    ss = row16_sum(ss);
     const float rn = __builtin_amdgcn_rsqf(ss * (1.0f / kD) + p.eps);
-    const bf16* rrow = (const bf16*)(raw + krow * kRawRowB);
-    bf16x8 o0, o1;
+    const bf16* rrow = (const bf16*)(raw + krow * kKRowB);
+    bf16x8 o;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int d = kc * 8 + e;
@@ -254,228 +278,311 @@ __global__ __launch_bounds__(kThreads, 1) void swa_stream_kernel(const SArgs p) 
       const bool first = d < kRH;
       const int j = first ? d : d - kRH;
       const int pd = rot ? (first ? d + kRH : d - kRH) : d;
-      const float xp = (float)rrow[pd] * sWk[pd];
-      float c = 1.f, s = 0.f;
+      float c = 1.f, s = 0.f, xp = 0.f;
       if (rot) {
         const float2 cs = tr[krow * kRHP + j];
         c = cs.x;
         s = first ? -cs.y : cs.y;
+        xp = (float)rrow[pd] * sWk[pd];
       }
-      o0[e] = (bf16)((x0[e] * sWk[d] * c + xp * s) * rn);
-      o1[e] = (bf16)(x1[e] * sWk[64 + d] * rn);
+      o[e] = (bf16)((x[e] * sWk[d] * c + xp * s) * rn);
     }
-    const int kb = 2 * t + (krow >> 5);
-    char* blk = smem + kOffK + ring_slot(kb) * kKBlkB;
-    const int row = krow & 31;
-    *(bf16x8*)(blk + kblk_off(row, kc)) = o0;
-    *(bf16x8*)(blk + kblk_off(row, kc + 8)) = o1;
+    *(bf16x8*)(smem + kOffK + ring_slot(t) * kKBlkB + krow_off(krow, kc)) = o;
   };
-  // V of tile t, transposed into its two ring blocks (keys 2 kp, 2 kp + 1 of the tile are
-  // adjacent slots, so each store is one 32-bit word).
-  auto stage_v = [&](const u32x4 (&vr)[2], int t) {
-    const int tv = opaque(tid);
-    const int kp = tv & 31, vc = tv >> 5;
-    const int key = 2 * kp;
-    char* blk = smem + kOffV + ring_slot(2 * t + (key >> 5)) * kVBlkB;
-    const int sl = key_slot(key & 31);
+  // V of tile t, transposed into its ring block (keys 2 kp, 2 kp + 1 are adjacent slots,
+  // so each store is one 32-bit word).
+  auto stage_v = [&](const u32x2 (&vr)[2], int t) {
+    const int tl = opaque(tid);
+    const int kp = tl & 15, dq = tl >> 4;
+    char* blk = smem + kOffV + ring_slot(t) * kVBlkB;
+    const int sl = key_slot(2 * kp);
     const int chunk = sl >> 3, within = sl & 7;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = vc * 8 + e;
-      const int m = (d & ~31) + vt_row_of_dim(d & 31);
+    for (int e = 0; e < 4; ++e) {
+      const int m = vt_row_of_dim(dq * 4 + e);
       const uint32_t w0 = vr[0][e >> 1], w1 = vr[1][e >> 1];
       const uint32_t word = (e & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u))
                                     : ((w0 & 0xffffu) | (w1 << 16));
       *(uint32_t*)(blk + vblk_off(m, chunk) + within * 2) = word;
     }
   };
-  // RMSNorm + RoPE + scale of this lane's query row (64 dims per lane half; the rotated
-  // dims [0, 42) all sit in the lower half), as the B operand.
-  auto q_transform = [&](const u32x4 (&raw)[8], int buf, bf16x8 (&qreg)[8]) {
-    // values are unpacked where used, so that no 64-float copy of the row is live
+  // RMSNorm + RoPE + scale of this lane's 32 dims of its query row, as the B operand.
+  // Rotated pairs (j, j + 21): group 0 holds both members for j <= 10 and j's member for
+  // j = 11 .. 20, whose partners (dims 32 .. 41) sit in group 1; those ten values cross
+  // between groups 0 and 1 (and meaningless ones between groups 2 and 3).
+  auto q_transform = [&](const u32x4 (&raw)[4], int s, bf16x8 (&qreg)[4]) {
+    uint32_t dw[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dw[i] = raw[i >> 2][i & 3];
     float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < 64; ++i) {
-      const float xv = bf16_elem(raw[i >> 3], i & 7);
+    for (int i = 0; i < 32; ++i) {
+      const float xv = bf16_word(dw[i >> 1], i & 1);
       ss = __builtin_fmaf(xv, xv, ss);
     }
-    ss += __shfl_xor(ss, 32);
+    ss = group_sum(ss);
     const float rn = __builtin_amdgcn_rsqf(ss * (1.0f / kD) + p.eps);
-    const float* w = sWq + hi * 64;
-    const float2* tr = (const float2*)(smem + kOffTrig + buf * kTrigB) + (32 * ph + n) * kRHP;
+    // group 0 sends its dims 10 .. 21 (words 5 .. 10), group 1 its dims 32 .. 43 (words 0 .. 5)
+    const bool odd = grp & 1;
+    uint32_t rc[6];
 #pragma unroll
-    for (int j = 0; j < kRH; ++j) {
-      const float2 cs = tr[j];
-      const float c = hi ? 1.f : cs.x;
-      const float sn = hi ? 0.f : cs.y;
-      const float a = bf16_elem(raw[j >> 3], j & 7) * w[j];
-      const float bb = bf16_elem(raw[(j + kRH) >> 3], (j + kRH) & 7) * w[j + kRH];
-      qreg[j >> 3][j & 7] = (bf16)((a * c - bb * sn) * rn);
-      qreg[(j + kRH) >> 3][(j + kRH) & 7] = (bf16)((bb * c + a * sn) * rn);
+    for (int k = 0; k < 6; ++k) rc[k] = swap16(odd ? dw[k] : dw[5 + k]);
+    const float* w = sWq + grp * 32;
+    const float2* tr = trig_buf(s) + (16 * ph + n) * kRHP;
+    float2 cs[kRH];
+#pragma unroll
+    for (int j = 0; j < kRH; ++j) cs[j] = tr[j];
+    const bool g0 = grp == 0, g1 = grp == 1;
+    auto outv = [&](int i) -> float {
+      const float xi = bf16_word(dw[i >> 1], i & 1) * w[i];
+      float c = 1.f, sn = 0.f, pv = 0.f;
+      if (i <= 9) {
+        // group 0: partner i + 21 (own), pair j = i; group 1: dim 32 + i, partner 11 + i
+        const float p0 = bf16_word(dw[(i + kRH) >> 1], (i + kRH) & 1) * sWq[i + kRH];
+        const float p1 = bf16_word(rc[(i + 1) >> 1], (i + 1) & 1) * sWq[11 + i];
+        c = g0 ? cs[i].x : (g1 ? cs[11 + i].x : 1.f);
+        sn = g0 ? -cs[i].y : (g1 ? cs[11 + i].y : 0.f);
+        pv = g0 ? p0 : p1;
+      } else if (i == 10) {
+        const float p0 = bf16_word(dw[(i + kRH) >> 1], (i + kRH) & 1) * sWq[i + kRH];
+        c = g0 ? cs[i].x : 1.f;
+        sn = g0 ? -cs[i].y : 0.f;
+        pv = p0;
+      } else if (i <= 20) {
+        // partner dim i + 21 = 32 + (i - 11) from group 1
+        const float p0 = bf16_word(rc[(i - 11) >> 1], (i - 11) & 1) * sWq[i + kRH];
+        c = g0 ? cs[i].x : 1.f;
+        sn = g0 ? -cs[i].y : 0.f;
+        pv = p0;
+      } else {
+        // group 0: second member of pair j = i - 21 (partner own)
+        const float p0 = bf16_word(dw[(i - kRH) >> 1], (i - kRH) & 1) * sWq[i - kRH];
+        c = g0 ? cs[i - kRH].x : 1.f;
+        sn = g0 ? cs[i - kRH].y : 0.f;
+        pv = p0;
+      }
+      return (xi * c + pv * sn) * rn;
+    };
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (bf16)outv(ks * 8 + e);
+      qreg[ks] = v;
     }
-#pragma unroll
-    for (int i = 2 * kRH; i < 64; ++i) qreg[i >> 3][i & 7] = (bf16)(bf16_elem(raw[i >> 3], i & 7) * w[i] * rn);
   };
 
   // ---- attention state -----------------------------------------------------------------
-  f32x16 oacc[4];
+  f32x4 oacc[8];
   float l_run = 0.f, m_run = -INFINITY;
   auto reset_acc = [&] {
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-    }
+    for (int db = 0; db < 8; ++db) oacc[db] = (f32x4){0.f, 0.f, 0.f, 0.f};
     l_run = 0.f;
     m_run = -INFINITY;
   };
   const bf16x2 ones2 = {(bf16)1.0f, (bf16)1.0f};
 
-  // One 32-key ring block for this wave's 32 queries of step s.
-  auto do_block = [&](int s, int jb, const bf16x8 (&qreg)[8], auto masked_tag) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    const int kb = 2 * s - 4 + ph + jb;
+  // Scores of ring block kb for this wave's 16 queries: two 16-key halves; lane group g
+  // holds keys 16 kh + 4 g + r.
+  auto scores = [&](int kb, const bf16x8 (&qreg)[4], f32x4 (&sacc)[2]) {
     const int ln = opaque(lane);
-    const int n = ln & 31, hi = ln >> 5;
+    const int nn = ln & 15, gg = ln >> 4;
     const char* sK = smem + kOffK + ring_slot(kb) * kKBlkB;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      sacc[kh] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 a = *(const bf16x8*)(sK + krow_off(16 * kh + nn, 4 * gg + ks));
+        sacc[kh] = mfma16(a, qreg[ks], sacc[kh]);
+      }
+    }
+  };
+  auto pv_block = [&](int kb, const bf16x8& pb, bool first) {
+    const int ln = opaque(lane);
+    const int nn = ln & 15, gg = ln >> 4;
     const char* sV = smem + kOffV + ring_slot(kb) * kVBlkB;
-    f32x16 sacc;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8 a = *(const bf16x8*)(sK + kblk_off(n, 8 * hi + ks));
-      sacc = mfma(a, qreg[ks], sacc);
+    for (int db = 0; db < 8; ++db) {
+      const bf16x8 a = *(const bf16x8*)(sV + vblk_off(16 * db + nn, gg));
+      oacc[db] = mfma16(a, pb, first ? (f32x4){0.f, 0.f, 0.f, 0.f} : oacc[db]);
     }
-    if (MASKED) {
-      // key - query for register r: 32 kb + 8 (r / 4) + 4 hi + r % 4 - q
-      const int rel = 32 * kb + 4 * hi - (s * kStep + 32 * ph + n);
+  };
+  // P (bf16, B-operand order) from scores, with the row-sum update.
+  auto to_p = [&](const float (&pf)[8], float& ls) -> bf16x8 {
+    bf16x8 v;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int dk = rel + (r >> 2) * 8 + (r & 3);
-        if (dk > 0 || dk <= -W) sacc[r] = -INFINITY;
-      }
+    for (int e = 0; e < 8; ++e) v[e] = (bf16)pf[e];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const bf16x2 pr = {v[e], v[e + 1]};
+      ls = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2, ls, false);
     }
-    float mu = 0.f;
-    if (!STATIC) {
-      float mt = sacc[0];
+    return v;
+  };
+
+  // Fast path (128-key window, static shift, away from position 0): the five blocks
+  // unrolled; masks only on the band-edge block (visible: keys above the query's offset
+  // in its block) and the diagonal block (keys at or below it); the first block starts the
+  // accumulators from zero.
+  auto blocks_full = [&](int s, const bf16x8 (&qreg)[4]) {
+    const int ln = opaque(lane);
+    const int nn = ln & 15, gg = ln >> 4;
+    const int qo = 16 * ph + nn;   // query offset within the step's 32 positions
+    float ls = 0.f;
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sacc[r]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float m_old = m_run;
-      const bool raise = mt > m_old + 8.0f;
-      if (__ballot(raise)) {
-        const float m_new = raise ? mt : m_old;
-        const float alpha = (m_old == -INFINITY) ? 0.f : fast_exp2(m_old - m_new);
-        l_run *= alpha;
+    for (int jb = 0; jb < kNB; ++jb) {
+      const int kb = s - (kNB - 1) + jb;
+      f32x4 sacc[2];
+      scores(kb, qreg, sacc);
+      float pf[8];
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-        m_run = m_new;
+      for (int e = 0; e < 8; ++e) {
+        const int kh = e >> 2, r = e & 3;
+        float pv = fast_exp2(sacc[kh][r]);
+        const bool below = 16 * kh + 4 * gg + r <= qo;
+        if (jb == 0) pv = below ? 0.f : pv;
+        if (jb == kNB - 1) pv = below ? pv : 0.f;
+        pf[e] = pv;
       }
-      mu = (m_run == -INFINITY) ? 0.f : m_run;
-    }
-    bf16x8 pb[2];
-    float ls = l_run;
-#pragma unroll
-    for (int jh = 0; jh < 2; ++jh) {
-      bf16x8 v;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        v[e] = (bf16)fast_exp2(STATIC ? sacc[jh * 8 + e] : sacc[jh * 8 + e] - mu);
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const bf16x2 pr = {v[e], v[e + 1]};
-        ls = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2, ls, false);
-      }
-      pb[jh] = v;
+      const bf16x8 pb = to_p(pf, ls);
+      pv_block(kb, pb, jb == 0);
     }
     l_run = ls;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int jh = 0; jh < 2; ++jh) {
-        const bf16x8 a = *(const bf16x8*)(sV + vblk_off(db * 32 + n, 2 * jh + hi));
-        oacc[db] = mfma(a, pb[jh], oacc[db]);
-      }
   };
-  // Blocks [j0, j1) of step s. The band-edge block (0) and the diagonal block (4) are
-  // masked, and every block when the window is shorter than 128; blocks wholly before
-  // position 0 or wholly outside the window are skipped (uniform per wave).
-  auto blocks = [&](int s, int j0, int j1, const bf16x8 (&qreg)[8]) {
-    const int q_lo = s * kStep + 32 * ph;
-    for (int jb = j0; jb < j1; ++jb) {
-      const int kb = 2 * s - 4 + ph + jb;
-      if (kb < 0 || 32 * kb + 31 <= q_lo - W) continue;
-      if (jb == 0 || jb == kNB - 1 || W < kMaxWindow)
-        do_block(s, jb, qreg, std::integral_constant<bool, true>{});
-      else
-        do_block(s, jb, qreg, std::integral_constant<bool, false>{});
+  // General path: any window <= 128, blocks before position 0, and the online variant.
+  auto blocks = [&](int s, const bf16x8 (&qreg)[4]) {
+    const int q_lo = s * kStep + 16 * ph;
+    for (int jb = 0; jb < kNB; ++jb) {
+      const int kb = s - (kNB - 1) + jb;
+      if (kb < 0 || kStep * kb + kStep - 1 <= q_lo - W) continue;
+      const int ln = opaque(lane);
+      const int nn = ln & 15, gg = ln >> 4;
+      f32x4 sacc[2];
+      scores(kb, qreg, sacc);
+      // key - query for value e: 32 kb + 16 (e / 4) + 4 g + e % 4 - q
+      const int rel = kStep * kb + 4 * gg - (q_lo + nn);
+      float sv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int dk = rel + 16 * (e >> 2) + (e & 3);
+        sv[e] = (dk > 0 || dk <= -W) ? -INFINITY : sacc[e >> 2][e & 3];
+      }
+      float mu = 0.f;
+      if (!STATIC) {
+        float mt = sv[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) mt = fmaxf(mt, sv[e]);
+        mt = group_max(mt);
+        const float m_old = m_run;
+        const bool raise = mt > m_old + 8.0f;
+        if (__ballot(raise)) {
+          const float m_new = raise ? mt : m_old;
+          const float alpha = (m_old == -INFINITY) ? 0.f : fast_exp2(m_old - m_new);
+          l_run *= alpha;
+#pragma unroll
+          for (int db = 0; db < 8; ++db) oacc[db] *= alpha;
+          m_run = m_new;
+        }
+        mu = (m_run == -INFINITY) ? 0.f : m_run;
+      }
+      float pf[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[e] = fast_exp2(sv[e] - mu);
+      float ls = l_run;
+      const bf16x8 pb = to_p(pf, ls);
+      l_run = ls;
+      pv_block(kb, pb, false);
     }
   };
-  auto epilogue = [&](int s, const u32x4 (&graw)[4][2]) {
-    const float lt = l_run + __shfl_xor(l_run, 32);
-    const int pos = s * kStep + 32 * ph + n;
+  // O = acc / l * sigmoid(G) of one step as bf16 (dims 32 g + 8 c .. + 7 in ob[c]):
+  // o / l * sigmoid(g) = o * rcp(l + l * exp(-g)).
+  auto epilogue = [&](const u32x4 (&graw)[4], bf16x8 (&ob)[4]) {
+    const float lt = group_sum(l_run);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float eg = __expf(-bf16_elem(graw[c], e));
+        o[e] = (bf16)(oacc[2 * c + (e >> 2)][e & 3] * __builtin_amdgcn_rcpf(__builtin_fmaf(lt, eg, lt)));
+      }
+      ob[c] = o;
+    }
+  };
+  auto store_out = [&](int s, const bf16x8 (&ob)[4]) {
+    const int pos = s * kStep + 16 * ph + n;
     if (pos < T) {
-      const float inv = 1.0f / lt;
-      bf16* dst = p.out + qoff + (size_t)pos * qstride + hi * 16;
+      char* dst = obase + (uint32_t)pos * qrow_b + grp * 64;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int e2 = 0; e2 < 2; ++e2) {
-          bf16x8 o;
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            o[e] = (bf16)(oacc[db][e2 * 8 + e] * inv * sigmoidf_(bf16_elem(graw[db][e2], e)));
-          *(bf16x8*)(dst + db * 32 + e2 * 8) = o;
-        }
+      for (int c = 0; c < 4; ++c) *(bf16x8*)(dst + c * 16) = ob[c];
     }
   };
 
-  // ---- prologue: ring <- tiles s_begin - 2 .. s_begin, trig of s_begin ---------------
-  u32x4 qraw[8];
-  load_q(s_begin, qraw);
-  for (int t = max(s_begin - 2, 0); t <= s_begin; ++t) {
-    u32x4 kr[2], vr[2];
-    load_kv(t, kr, vr);
-    make_trig(t, t & 1);
-    stage_k(kr, t & 1);
+  // ---- prologue --------------------------------------------------------------------------
+  // Ring <- blocks s_begin - 4 .. s_begin; raw K and trig of block s_begin + 1 staged;
+  // trig of s_begin ready; registers: Q and G of s_begin, V of s_begin + 1, K of
+  // s_begin + 2.
+  for (int t = max(s_begin - (kNB - 1), 0); t <= s_begin; ++t) {
+    u32x4 kr;
+    u32x2 vr[2];
+    load_k(t, kr);
+    load_v(t, vr);
+    make_trig(t);
+    stage_k(kr, t);
     __syncthreads();
-    transform_k(kr, t, t & 1);
+    transform_k(t);
     stage_v(vr, t);
     __syncthreads();
   }
-  u32x4 kr[2], vr[2];
-  if (s_begin + 1 < s_end) load_kv(s_begin + 1, kr, vr);
-  reset_acc();
+  u32x4 kr;
+  u32x2 vr[2];
+  load_k(s_begin + 1, kr);
+  make_trig(s_begin + 1);
+  stage_k(kr, s_begin + 1);
+  // the loads the first step consumes, issued in the order the steady state issues them
+  // (Q, V, K, then G), so that the waits at the loop head are the same on both entries
+  u32x4 qraw[4], graw[4];
+  load_row(qbase, s_begin, qraw);
+  load_v(s_begin + 1, vr);
+  load_k(s_begin + 2, kr);
+  load_row(gbase, s_begin, graw);
+  __syncthreads();
 
   // ---- steady state -------------------------------------------------------------------
+  // Loads run one step ahead. At the top of step s the loads issued at the top of step
+  // s - 1 are consumed (Q of s, V of s + 1, K of s + 2), the outputs of step s - 1 are
+  // stored and the next loads issued; G of s, issued after the previous epilogue, is
+  // consumed by this step's epilogue. Loads past the segment are clamped and unused.
+  bf16x8 ob[4];
   for (int s = s_begin; s < s_end; ++s) {
-    const bool more = s + 1 < s_end;
-    bf16x8 qreg[8];
-    q_transform(qraw, s & 1, qreg);
-    u32x4 graw[4][2];
-    load_g(s, graw);
-    if (more) load_q(s + 1, qraw);
-    blocks(s, 0, 2, qreg);
-    if (more) {
-      stage_k(kr, (s + 1) & 1);
-      make_trig(s + 1, (s + 1) & 1);
+    bf16x8 qreg[4];
+    q_transform(qraw, s, qreg);
+    // V of block s + 1 into the slot of block s - 5 (last read in step s - 1), raw K of
+    // s + 2; then the outputs of step s - 1 leave, and the registers take the next loads
+    stage_v(vr, s + 1);
+    stage_k(kr, s + 2);
+    if (s > s_begin) store_out(s - 1, ob);
+    load_row(qbase, s + 1, qraw);
+    load_v(s + 2, vr);
+    load_k(s + 3, kr);
+    transform_k(s + 1);
+    make_trig(s + 2);
+    if (STATIC && W == kMaxWindow && s >= kNB - 1) {
+      blocks_full(s, qreg);
+    } else {
+      reset_acc();
+      blocks(s, qreg);
     }
-    // Every wave is done with the two oldest blocks; tile s + 1's raw K and trig are in
-    // LDS. (The raw/trig buffers alternate, so the next writes to these ones come after
-    // the next barrier.)
+    epilogue(graw, ob);
+    // G of the next step, consumed by the next epilogue
+    load_row(gbase, s + 1, graw);
+    // Block s + 1, raw K of s + 2 and trig of s + 2 are visible to every wave; every wave
+    // is done with block s - 4 (its slot takes block s + 2 next).
     __syncthreads();
-    if (more) {
-      transform_k(kr, s + 1, (s + 1) & 1);
-      stage_v(vr, s + 1);
-      if (s + 2 < s_end) load_kv(s + 2, kr, vr);
-    }
-    blocks(s, 2, kNB, qreg);
-    epilogue(s, graw);
-    reset_acc();
   }
+  store_out(s_end - 1, ob);
 }
 
 template <bool STATIC>
@@ -487,8 +594,10 @@ hipError_t set_smem() {
 }  // namespace
 
 bool swa_stream_supported(const PrefillArgs& a) {
+  // per-lane offsets are 32-bit byte offsets within one sequence of Q / G / O
+  const bool fits = (size_t)a.T * a.Hq * kD * 2 <= (size_t)UINT32_MAX;
   return a.swa && a.d == kD && a.Hq == kG * a.Hkv && a.rdim == 2 * kRH && a.window >= 1 &&
-         a.window <= kMaxWindow;
+         a.window <= kMaxWindow && fits;
 }
 
 hipError_t launch_swa_stream(const PrefillArgs& a, hipStream_t s) {
