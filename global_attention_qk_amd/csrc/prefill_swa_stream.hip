@@ -87,9 +87,12 @@ __device__ __forceinline__ int ring_slot(int kb) { return (kb + 4 * kRing) % kRi
 // Padded rows: one 16-byte chunk read across 16 consecutive keys touches every bank once,
 // and a lane's chunks are one base plus immediate offsets.
 __device__ __forceinline__ int krow_off(int row, int chunk) { return row * kKRowB + (chunk << 4); }
-// V^T block: row m (0..127) holds 32 key slots (64 B); chunk c at c ^ ((m >> 2) & 3).
+// V^T block: row m (0..127) holds 32 key slots (64 B); chunk c sits at
+// c ^ ((m >> 2) & 3) ^ (m & 2), so that one chunk read across 8 consecutive rows covers
+// 128 distinct bytes and across 16 rows 256 distinct bytes (conflict-free whether the
+// LDS serves 16-byte reads 8 or 16 lanes at a time).
 __device__ __forceinline__ int vblk_off(int m, int chunk) {
-  return m * (kStep * 2) + ((chunk ^ ((m >> 2) & 3)) << 4);
+  return m * (kStep * 2) + ((chunk ^ ((m >> 2) & 3) ^ (m & 2)) << 4);
 }
 // V^T row holding dim d: accumulator register r of 16-row block db in lane group g is
 // dim 32 g + 4 db + r.
