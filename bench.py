@@ -36,7 +36,35 @@ def parse():
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="approximate CPU time budget of the oracle sample")
+    ap.add_argument("--only", choices=["swa_prefill", "global_prefill", "global_decode",
+                                       "swa_decode", "copy"], default=None,
+                    help="run just this call (warmup + steps launches, for profilers); "
+                         "'copy' is a plain 1 GiB device copy used to calibrate counters")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "global_prefill_T262144_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "global_attention_qk_amd", "csrc", f)
+                  for f in ("prefill_bf16.hip", "common.h")]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the global prefill attention kernel, from the committed
+    counter summary (FETCH_SIZE and WRITE_SIZE, each scaled by the same counter's reading
+    for a plain copy of known size); None when the kernel source changed since."""
+    import hashlib
+    try:
+        kv = {}
+        for line in open(TRAFFIC_FILE):
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                kv[key.strip()] = val.strip()
+        src = hashlib.sha256(b"".join(open(f, "rb").read() for f in KERNEL_SOURCES)).hexdigest()
+        if kv.get("kernel_source_sha256") != src:
+            return None
+        return float(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def alg_counts(T, B, Hq, Hkv, d, W, Bdec, S):
@@ -69,6 +97,8 @@ def main():
 
     dev = "cuda"
     torch.cuda.init()
+    if args.only:
+        return run_only(args)
     T, B, Hq, Hkv, d, W = C4.T, C4.B, C4.Hq, C4.Hkv, C4.d, C4.window
     r = C4.rotary_dim
     # ---- inputs (seeded, generated on the device, outside the timed region) -----------
@@ -178,7 +208,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": glob_tflops / PEAK_BF16_TFLOPS,
-            "traffic": None,
+            "traffic": measured_traffic(),
             "alg_flops_per_launch": cnt["glob_flops"],
         },
         "breakdown": breakdown,
@@ -187,6 +217,58 @@ def main():
         del q, k, v, g, out_s, out_g, ws
         rec["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(rec), flush=True)
+
+
+def run_only(args):
+    """One call kind alone, warmup + steps launches (for rocprofv3 runs)."""
+    import torch
+
+    import global_attention_qk_amd as zg
+    from workloads import C4, C5, decode_inputs, prefill_inputs
+
+    dev = "cuda"
+    r, W = C4.rotary_dim, C4.window
+    if args.only == "copy":
+        n = 1 << 30
+        x = torch.randint(0, 255, (n,), dtype=torch.uint8, device=dev)
+        y = torch.empty_like(x)
+        call = lambda: y.copy_(x)
+    elif args.only in ("swa_prefill", "global_prefill"):
+        q, k, v, g, wq, wk = prefill_inputs(C4, device=dev, gated=args.only == "swa_prefill")
+        out = torch.empty_like(q)
+        if args.only == "swa_prefill":
+            call = lambda: zg.swa_prefill(q, k, v, g, wq, wk, window=W, rotary_dim=r, out=out)
+        else:
+            ws = torch.empty(zg.global_prefill_workspace_bytes(q, k, rotary_dim=r),
+                             dtype=torch.uint8, device=dev)
+            call = lambda: zg.global_prefill(q, k, v, wq, wk, rotary_dim=r, workspace=ws, out=out)
+    else:
+        dec = decode_inputs(C5, device=dev)
+        S = C5.T
+        pos = torch.full((C5.B,), S - 1, dtype=torch.int32, device=dev)
+        out = torch.empty_like(dec["q"])
+        if args.only == "global_decode":
+            dws = torch.empty(zg.global_decode_workspace_bytes(dec["q"], dec["k_new"], S),
+                              dtype=torch.uint8, device=dev)
+            call = lambda: zg.global_decode(dec["q"], dec["k_new"], dec["v_new"], dec["wq"],
+                                            dec["wk"], dec["k_cache"], dec["v_cache"], pos,
+                                            rotary_dim=r, workspace=dws, out=out)
+        else:
+            call = lambda: zg.swa_decode(dec["q"], dec["k_new"], dec["v_new"], dec["g"],
+                                         dec["wq"], dec["wk"], dec["k_ring"], dec["v_ring"], pos,
+                                         rotary_dim=r, out=out)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    print(f"[bench] {args.only}: {args.steps} launches, "
+          f"{e0.elapsed_time(e1) / max(args.steps, 1):.3f} ms each", flush=True)
 
 
 def cpu_baseline(budget_s: float):
