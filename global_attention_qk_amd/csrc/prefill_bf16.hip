@@ -43,6 +43,12 @@ constexpr int kRows = 256;        // query rows per workgroup
 #define ZG_PREFILL_WAVES 8
 #endif
 constexpr int kWavesPerBlock = ZG_PREFILL_WAVES;
+// Global layers with K~ / V tiles from the workspace: 4 waves of 64 query rows (one wave
+// per SIMD, half the LDS operand traffic per product of 32-row waves) with the fenced
+// software pipeline of compute_pipe.
+#ifndef ZG_GLOBAL_WAVES
+#define ZG_GLOBAL_WAVES 4
+#endif
 constexpr int kBN = 64;           // keys per tile
 constexpr int kMaxHalfMfma = 32;  // rotary_dim <= 64 on this path
 constexpr float kStaticShiftMax = 96.0f;  // largest score bound (log2 units) without a max
@@ -414,6 +420,30 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
     }
   };
 
+  // Piece `t` (0 .. KIT + KG - 1) of stage() / fetch() for the pre-computed K~ / V-tile
+  // path: one 16-byte chunk per thread, so the pieces can be spread between MFMAs.
+  auto stage_piece = [&](int kt, int buf, int t) {
+    bf16* sK = (bf16*)(smem + buf * S::kBuf);
+    bf16* sVt = (bf16*)(smem + buf * S::kBuf + S::kK);
+    if (t < KIT) {
+      const int c = tid + t * kThreads;
+      *(u32x4*)(sK + (c / DC) * RW + (c % DC) * 8) = kreg[t];
+    } else {
+      const int c = tid + (t - KIT) * kThreads;
+      *(u32x4*)(sVt + (c >> 3) * VW + (c & 7) * 8) = vreg[t - KIT];
+    }
+  };
+  auto fetch_piece = [&](int kt, int t) {
+    if (t < KIT) {
+      const int c = tid + t * kThreads;
+      const int pos = min(kt * kBN + c / DC, T - 1);
+      kreg[t] = *(const u32x4*)(ktsrc + (size_t)pos * D + (c % DC) * 8);
+    } else {
+      const bf16* src = vtsrc + (size_t)kt * (kBN * D);
+      vreg[t - KIT] = *(const u32x4*)(src + (tid + (t - KIT) * kThreads) * 8);
+    }
+  };
+
   const bf16x2 ones2 = {(bf16)1.0f, (bf16)1.0f};
 
   // Scores of one 32-key block (rows kb*32.. of the K~ tile) for every query block.
@@ -582,6 +612,106 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
       }
     }
   };
+  // Two query blocks per wave, static shift, K~ / V tiles from the workspace: a fenced
+  // software pipeline over the tile's two 32-key blocks, one wave per SIMD,
+  //   A: QK(0) | B: QK(1) + softmax(0) | C: P.V(0) + softmax(1) | D: P.V(1) + staging,
+  // with the vector work cut into pieces placed between the MFMAs so that it issues in
+  // their shadow (the P.V products are inline assembly, so the order is pinned with
+  // scheduling barriers rather than left to the scheduler).
+  auto compute_pipe = [&](int kt, int buf, auto masked_tag, int next_kt, int next_buf,
+                          int fetch_kt) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    static_assert(QB == 2, "pipelined path holds two query blocks per wave");
+    constexpr int NPIECE = KIT + KG;             // staging pieces
+    constexpr int QK_SPP = 8 / KS;               // softmax pieces per QK step
+    constexpr int PV_STEPS = 2 * DB;
+    constexpr int PV_SPP = 8 / PV_STEPS;         // softmax pieces per P.V step
+    static_assert(NPIECE == PV_STEPS, "one staging piece per P.V step");
+    const bf16* sK = (const bf16*)(smem + buf * S::kBuf);
+    const bf16* sVt = (const bf16*)(smem + buf * S::kBuf + S::kK);
+    const int k0 = kt * kBN;
+    int rel[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) rel[qb] = qpos[qb] - k0 - 4 * hi;
+    f32x16 sc[2][QB];
+    u32x4 pw[2][QB][2];   // P as packed bf16 pairs: [block][qb][jh]
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[kb][qb][r] = 0.f;
+    // softmax piece j (0..7) of block kb: query block j / 4, half j / 2 % 2 of the 16
+    // scores, four of them (j % 2)
+    auto sm_piece = [&](int kb, int j) {
+      const int qb = j >> 2, jh = (j >> 1) & 1, eh = j & 1;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = jh * 8 + eh * 4 + e;
+        float x = sc[kb][qb][r];
+        if (MASKED) {
+          const int off = kb * 32 + (r >> 2) * 8 + (r & 3);
+          if (off > rel[qb]) x = -INFINITY;
+        }
+        v[e] = fast_exp2(x);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; e += 2) {
+        const bf16x2 pr = {(bf16)v[e], (bf16)v[e + 1]};
+        pw[kb][qb][jh][eh * 2 + (e >> 1)] = __builtin_bit_cast(uint32_t, pr);
+        l_run[qb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2, l_run[qb], false);
+      }
+    };
+    // The tile as one stream of MFMA slots (each: one A operand from LDS, one product
+    // per query block): A = K~ block 0 by k-step, B = K~ block 1, C = V^T block 0 by
+    // (d block, key half), D = V^T block 1. Each slot's operand is read two slots ahead.
+    constexpr int NSLOT = 2 * KS + 2 * PV_STEPS;
+    auto read_op = [&](int u) -> bf16x8 {
+      if (u < 2 * KS) {
+        const int kb = u / KS, ks = u % KS;
+        return *(const bf16x8*)(sK + (kb * 32 + l32) * RW + ks * 16 + hi * 8);
+      }
+      // key half outer, d block inner: an accumulator recurs every DB slots
+      const int t = (u - 2 * KS) % PV_STEPS, kb = (u - 2 * KS) / PV_STEPS;
+      const int db = t % DB, jh = t / DB;
+      return *(const bf16x8*)(sVt + (db * 32 + l32) * VW + kb * 32 + jh * 16 + hi * 8);
+    };
+    bf16x8 op0 = read_op(0), op1 = read_op(1);
+#pragma unroll
+    for (int u = 0; u < NSLOT; ++u) {
+      const bf16x8 a = op0;
+      op0 = op1;
+      if (u + 2 < NSLOT) op1 = read_op(u + 2);
+      if (u < 2 * KS) {
+        const int kb = u / KS, ks = u % KS;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          sc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[qb][ks], sc[kb][qb], 0, 0, 0);
+        if (kb == 1) {
+          // B: softmax of block 0 under the block-1 score products
+#pragma unroll
+          for (int w = 0; w < QK_SPP; ++w) sm_piece(0, ks * QK_SPP + w);
+        }
+      } else {
+        const int t = (u - 2 * KS) % PV_STEPS, kb = (u - 2 * KS) / PV_STEPS;
+        const int db = t % DB, jh = t / DB;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          mfma_acc(oacc[qb][db], a, __builtin_bit_cast(bf16x8, pw[kb][qb][jh]));
+        if (kb == 0) {
+          // C: softmax of block 1 under the block-0 P.V products
+#pragma unroll
+          for (int w = 0; w < PV_SPP; ++w) sm_piece(1, t * PV_SPP + w);
+        } else {
+          // D: the next tile into the other buffer, the one after it fetched
+          stage_piece(next_kt, next_buf, t);
+          fetch_piece(fetch_kt, t);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
   auto nothing = [] {};
 
   int i = 0;
@@ -595,10 +725,15 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
     auto step = [&](int i, auto masked_tag) {
       // Branch-free: past the end, the last tile is re-staged into the idle buffer and
       // re-fetched (in-bounds and never read), so the loop body is one basic block.
-      compute(tile_of(i), i & 1, masked_tag, [&] {
-        stage(tile_of(min(i + 1, n_tiles - 1)), (i + 1) & 1);
-        fetch(tile_of(min(i + 2, n_tiles - 1)));
-      });
+      if constexpr (QB == 2 && STATIC) {
+        compute_pipe(tile_of(i), i & 1, masked_tag, tile_of(min(i + 1, n_tiles - 1)),
+                     (i + 1) & 1, tile_of(min(i + 2, n_tiles - 1)));
+      } else {
+        compute(tile_of(i), i & 1, masked_tag, [&] {
+          stage(tile_of(min(i + 1, n_tiles - 1)), (i + 1) & 1);
+          fetch(tile_of(min(i + 2, n_tiles - 1)));
+        });
+      }
       __syncthreads();  // tile i + 1 is in LDS; tile i's buffer may be overwritten
     };
     for (; i < n_unm; ++i) step(i, std::integral_constant<bool, false>{});
@@ -759,11 +894,11 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
   const bool kpre = (a.kt != nullptr);
   if (a.d == 128) {
     if (a.swa) return launch_t<128, true, false>(ka, n_blocks, s);
-    return kpre ? launch_t<128, false, true>(ka, n_blocks, s)
+    return kpre ? launch_t<128, false, true, ZG_GLOBAL_WAVES>(ka, n_blocks, s)
                 : launch_t<128, false, false>(ka, n_blocks, s);
   }
   if (a.swa) return launch_t<64, true, false>(ka, n_blocks, s);
-  return kpre ? launch_t<64, false, true>(ka, n_blocks, s)
+  return kpre ? launch_t<64, false, true, ZG_GLOBAL_WAVES>(ka, n_blocks, s)
               : launch_t<64, false, false>(ka, n_blocks, s);
 }
 
