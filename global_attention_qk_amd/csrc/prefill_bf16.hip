@@ -688,7 +688,13 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           sc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[qb][ks], sc[kb][qb], 0, 0, 0);
-        if (kb == 1) {
+        if (kb == 0) {
+          // A: the tile that phase D stages is fetched under the block-0 score products
+          if (ks < NPIECE) fetch_piece(fetch_kt, ks);
+          if (ks == KS - 1)
+#pragma unroll
+            for (int w = KS; w < NPIECE; ++w) fetch_piece(fetch_kt, w);
+        } else {
           // B: softmax of block 0 under the block-1 score products
 #pragma unroll
           for (int w = 0; w < QK_SPP; ++w) sm_piece(0, ks * QK_SPP + w);
@@ -704,9 +710,8 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
 #pragma unroll
           for (int w = 0; w < PV_SPP; ++w) sm_piece(1, t * PV_SPP + w);
         } else {
-          // D: the next tile into the other buffer, the one after it fetched
+          // D: the next tile (fetched in phase A) into the other buffer
           stage_piece(next_kt, next_buf, t);
-          fetch_piece(fetch_kt, t);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -720,14 +725,15 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
     // is fetched while tile i is computed, leaving one barrier per tile.
     fetch(tile_of(0));
     stage(tile_of(0), 0);
-    if (n_tiles > 1) fetch(tile_of(1));
+    // (the pipelined path fetches each tile in the step that stages it)
+    if (!(QB == 2 && STATIC) && n_tiles > 1) fetch(tile_of(1));
     __syncthreads();
     auto step = [&](int i, auto masked_tag) {
       // Branch-free: past the end, the last tile is re-staged into the idle buffer and
       // re-fetched (in-bounds and never read), so the loop body is one basic block.
       if constexpr (QB == 2 && STATIC) {
         compute_pipe(tile_of(i), i & 1, masked_tag, tile_of(min(i + 1, n_tiles - 1)),
-                     (i + 1) & 1, tile_of(min(i + 2, n_tiles - 1)));
+                     (i + 1) & 1, tile_of(min(i + 1, n_tiles - 1)));
       } else {
         compute(tile_of(i), i & 1, masked_tag, [&] {
           stage(tile_of(min(i + 1, n_tiles - 1)), (i + 1) & 1);
