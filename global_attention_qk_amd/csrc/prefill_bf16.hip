@@ -67,8 +67,14 @@ struct Smem {
   static constexpr int kKraw = kBN * kRowB;
   static constexpr int kKtrig = kBN * kMaxHalfMfma * 8;
   static constexpr int kLoop = 2 * kBuf + kKraw + kKtrig;
+  // Pipelined global path: three buffers filled by LDS DMA, each K~ as 64 unpadded rows
+  // of 2*D bytes and V^T as D unpadded rows of 128 bytes (16-byte chunks swizzled).
+  static constexpr int kDK = kBN * D * 2;
+  static constexpr int kDBuf = kDK + D * kBN * 2;
+  static constexpr int kDLoop = 3 * kDBuf;
   static constexpr int kW = 2 * D * 4;  // wq, wk
-  static constexpr int kUnion = (kQ + kQtrig) > kLoop ? (kQ + kQtrig) : kLoop;
+  static constexpr int kMain = kLoop > kDLoop ? kLoop : kDLoop;
+  static constexpr int kUnion = (kQ + kQtrig) > kMain ? (kQ + kQtrig) : kMain;
   static constexpr int kTotal = kUnion + kW;
 };
 
@@ -114,6 +120,37 @@ __device__ __forceinline__ void set_prio() {
 // Keep a value in AGPRs from here on (so that loop-carried accumulators never take a
 // mixed register class).
 __device__ __forceinline__ void pin_agpr(f32x16& v) { asm volatile("" : "+a"(v)); }
+
+// Position of 16-byte chunk c within row r of an unpadded LDS tile with CPR (16 or 8)
+// chunks per row. The XOR swizzle sends the 16 consecutive rows read by one operand load
+// (same chunk) to 16 distinct 16-byte bank groups, and any 8 of them to distinct groups
+// of a 128-byte bank row, so the reads are conflict-free with 32 or 64 banks.
+template <int CPR>
+__device__ __forceinline__ int chunk_pos(int r, int c) {
+  return c ^ (CPR == 16 ? (r & 15) : ((r & 7) ^ ((r >> 3) & 1)));
+}
+
+// LDS DMA of 16 bytes per lane: lane L's bytes from gbase + voff land at lds + 16 L.
+// gbase and lds must be wave-uniform (scalar base, M0). Completion is counted by vmcnt
+// and left to the caller (vm_wait): the compiler does not see these loads and inserts
+// no wait for them. One wait state separates the M0 write from the DMA that reads it.
+__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, const void* lds) {
+  // (readfirstlane returns int: each half goes through uint32_t so that it is
+  // zero-extended, never sign-extended, into the 64-bit address)
+  const uint64_t g = (uint64_t)(uintptr_t)gbase;
+  const uint32_t glo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)g);
+  const uint32_t ghi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(g >> 32));
+  const uint64_t gu = ((uint64_t)ghi << 32) | (uint64_t)glo;
+  const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(m0), "v"(voff), "s"(gu) : "memory", "m0");
+}
+// Wait until at most N vector-memory operations of this wave are outstanding (they
+// complete in issue order).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
 
 // Wait states between the last MFMA that wrote the accumulators and any other access.
 template <int QB, int DB>
@@ -189,7 +226,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
@@ -420,27 +457,28 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
     }
   };
 
-  // Piece `t` (0 .. KIT + KG - 1) of stage() / fetch() for the pre-computed K~ / V-tile
-  // path: one 16-byte chunk per thread, so the pieces can be spread between MFMAs.
-  auto stage_piece = [&](int kt, int buf, int t) {
-    bf16* sK = (bf16*)(smem + buf * S::kBuf);
-    bf16* sVt = (bf16*)(smem + buf * S::kBuf + S::kK);
-    if (t < KIT) {
-      const int c = tid + t * kThreads;
-      *(u32x4*)(sK + (c / DC) * RW + (c % DC) * 8) = kreg[t];
+  // LDS DMA of tile kt into buffer buf of the pipelined path. Piece j (0 .. KS-1) is one
+  // 1 KiB block per wave, its 64 lanes landing in consecutive 16-byte slots: the first
+  // D/32 pieces cover K~ (512 / D rows per block), the rest V^T (8 rows per block).
+  // Each lane fetches the chunk that the swizzle puts in its slot; K~ rows past the end
+  // are clamped to the last row (masked keys).
+  constexpr int KPW = D / 32;
+  auto dma_piece = [&](int kt, int buf, int j) {
+    const char* dst = smem + buf * S::kDBuf;
+    const int k0 = kt * kBN;
+    if (j < KPW) {
+      constexpr int CPR = D / 8, RPB = 1024 / (2 * D);
+      const int blk = wave * KPW + j;
+      const int r = blk * RPB + lane / CPR;
+      const int c = chunk_pos<CPR>(r, lane % CPR);
+      dma16(ktsrc + (size_t)k0 * D, (uint32_t)(min(r, T - 1 - k0) * (2 * D) + c * 16),
+            dst + blk * 1024);
     } else {
-      const int c = tid + (t - KIT) * kThreads;
-      *(u32x4*)(sVt + (c >> 3) * VW + (c & 7) * 8) = vreg[t - KIT];
-    }
-  };
-  auto fetch_piece = [&](int kt, int t) {
-    if (t < KIT) {
-      const int c = tid + t * kThreads;
-      const int pos = min(kt * kBN + c / DC, T - 1);
-      kreg[t] = *(const u32x4*)(ktsrc + (size_t)pos * D + (c % DC) * 8);
-    } else {
-      const bf16* src = vtsrc + (size_t)kt * (kBN * D);
-      vreg[t - KIT] = *(const u32x4*)(src + (tid + (t - KIT) * kThreads) * 8);
+      const int blk = wave * KPW + (j - KPW);
+      const int d = blk * 8 + (lane >> 3);
+      const int c = chunk_pos<8>(d, lane & 7);
+      dma16(vtsrc + (size_t)kt * (kBN * D), (uint32_t)(d * 128 + c * 16),
+            dst + S::kDK + blk * 1024);
     }
   };
 
@@ -614,21 +652,28 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
   };
   // Two query blocks per wave, static shift, K~ / V tiles from the workspace: a fenced
   // software pipeline over the tile's two 32-key blocks, one wave per SIMD,
-  //   A: QK(0) | B: QK(1) + softmax(0) | C: P.V(0) + softmax(1) | D: P.V(1) + staging,
+  //   A: QK(0) + DMA of tile i+2 | B: QK(1) + softmax(0) | C: P.V(0) + softmax(1) | D: P.V(1)
   // with the vector work cut into pieces placed between the MFMAs so that it issues in
   // their shadow (the P.V products are inline assembly, so the order is pinned with
   // scheduling barriers rather than left to the scheduler).
-  auto compute_pipe = [&](int kt, int buf, auto masked_tag, int next_kt, int next_buf,
-                          int fetch_kt) {
+  // Per-lane byte offsets of the operand reads within a buffer: the K~ row of a lane is
+  // kb*32 + l32 and its chunk 2*ks + hi; the V^T row is db*32 + l32 and its chunk
+  // 4*kb + 2*jh + hi. Both swizzles depend on the row only through l32 & 15, so the
+  // block indices kb / db become immediate offsets.
+  int koff[KS], voff[4];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    koff[ks] = l32 * (2 * D) + chunk_pos<D / 8>(l32, 2 * ks + hi) * 16;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) voff[x] = S::kDK + l32 * 128 + chunk_pos<8>(l32, 2 * x + hi) * 16;
+  auto compute_pipe = [&](int kt, int buf, auto masked_tag, int dma_kt, int dma_buf) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     static_assert(QB == 2, "pipelined path holds two query blocks per wave");
-    constexpr int NPIECE = KIT + KG;             // staging pieces
     constexpr int QK_SPP = 8 / KS;               // softmax pieces per QK step
     constexpr int PV_STEPS = 2 * DB;
     constexpr int PV_SPP = 8 / PV_STEPS;         // softmax pieces per P.V step
-    static_assert(NPIECE == PV_STEPS, "one staging piece per P.V step");
-    const bf16* sK = (const bf16*)(smem + buf * S::kBuf);
-    const bf16* sVt = (const bf16*)(smem + buf * S::kBuf + S::kK);
+    static_assert(KS == 2 * KPW, "one DMA piece per block-0 score step");
+    const char* tb = smem + buf * S::kDBuf;
     const int k0 = kt * kBN;
     int rel[QB];
 #pragma unroll
@@ -670,12 +715,12 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
     auto read_op = [&](int u) -> bf16x8 {
       if (u < 2 * KS) {
         const int kb = u / KS, ks = u % KS;
-        return *(const bf16x8*)(sK + (kb * 32 + l32) * RW + ks * 16 + hi * 8);
+        return *(const bf16x8*)(tb + koff[ks] + kb * 32 * (2 * D));
       }
       // key half outer, d block inner: an accumulator recurs every DB slots
       const int t = (u - 2 * KS) % PV_STEPS, kb = (u - 2 * KS) / PV_STEPS;
       const int db = t % DB, jh = t / DB;
-      return *(const bf16x8*)(sVt + (db * 32 + l32) * VW + kb * 32 + jh * 16 + hi * 8);
+      return *(const bf16x8*)(tb + voff[2 * kb + jh] + db * 32 * 128);
     };
     bf16x8 op0 = read_op(0), op1 = read_op(1);
 #pragma unroll
@@ -689,11 +734,8 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
         for (int qb = 0; qb < QB; ++qb)
           sc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[qb][ks], sc[kb][qb], 0, 0, 0);
         if (kb == 0) {
-          // A: the tile that phase D stages is fetched under the block-0 score products
-          if (ks < NPIECE) fetch_piece(fetch_kt, ks);
-          if (ks == KS - 1)
-#pragma unroll
-            for (int w = KS; w < NPIECE; ++w) fetch_piece(fetch_kt, w);
+          // A: the tile two ahead goes to its buffer under the block-0 score products
+          dma_piece(dma_kt, dma_buf, ks);
         } else {
           // B: softmax of block 0 under the block-1 score products
 #pragma unroll
@@ -709,9 +751,6 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
           // C: softmax of block 1 under the block-0 P.V products
 #pragma unroll
           for (int w = 0; w < PV_SPP; ++w) sm_piece(1, t * PV_SPP + w);
-        } else {
-          // D: the next tile (fetched in phase A) into the other buffer
-          stage_piece(next_kt, next_buf, t);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -720,26 +759,42 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
   auto nothing = [] {};
 
   int i = 0;
-  if constexpr (KPRE) {
+  if constexpr (KPRE && QB == 2 && STATIC) {
+    // K~ / V^T tiles go from the workspace straight into LDS (DMA), two tiles ahead of
+    // their use, through three rotating buffers: one barrier per tile. Past the end the
+    // last tile is fetched again into the idle buffer (in bounds, never read).
+    const int last = n_tiles - 1;
+#pragma unroll
+    for (int j = 0; j < KS; ++j) dma_piece(tile_of(0), 0, j);
+#pragma unroll
+    for (int j = 0; j < KS; ++j) dma_piece(tile_of(min(1, last)), 1, j);
+    vm_wait<KS>();
+    __syncthreads();
+    int cur = 0;
+    auto step = [&](int i, auto masked_tag) {
+      const int ahead = cur == 0 ? 2 : cur - 1;   // (cur + 2) % 3
+      compute_pipe(tile_of(i), cur, masked_tag, tile_of(min(i + 2, last)), ahead);
+      vm_wait<KS>();   // this wave's DMA of tile i + 1 has landed ...
+      __syncthreads();  // ... and every wave's; tile i's buffer may be overwritten
+      cur = cur == 2 ? 0 : cur + 1;
+    };
+    for (; i < n_unm; ++i) step(i, std::integral_constant<bool, false>{});
+    for (; i < n_tiles; ++i) step(i, std::integral_constant<bool, true>{});
+    vm_wait<0>();   // no DMA may still be writing LDS when the workgroup ends
+  } else if constexpr (KPRE) {
     // K~ comes ready-made: tile i + 1 is written to the other LDS buffer and tile i + 2
     // is fetched while tile i is computed, leaving one barrier per tile.
     fetch(tile_of(0));
     stage(tile_of(0), 0);
-    // (the pipelined path fetches each tile in the step that stages it)
-    if (!(QB == 2 && STATIC) && n_tiles > 1) fetch(tile_of(1));
+    if (n_tiles > 1) fetch(tile_of(1));
     __syncthreads();
     auto step = [&](int i, auto masked_tag) {
       // Branch-free: past the end, the last tile is re-staged into the idle buffer and
       // re-fetched (in-bounds and never read), so the loop body is one basic block.
-      if constexpr (QB == 2 && STATIC) {
-        compute_pipe(tile_of(i), i & 1, masked_tag, tile_of(min(i + 1, n_tiles - 1)),
-                     (i + 1) & 1, tile_of(min(i + 1, n_tiles - 1)));
-      } else {
-        compute(tile_of(i), i & 1, masked_tag, [&] {
-          stage(tile_of(min(i + 1, n_tiles - 1)), (i + 1) & 1);
-          fetch(tile_of(min(i + 2, n_tiles - 1)));
-        });
-      }
+      compute(tile_of(i), i & 1, masked_tag, [&] {
+        stage(tile_of(min(i + 1, n_tiles - 1)), (i + 1) & 1);
+        fetch(tile_of(min(i + 2, n_tiles - 1)));
+      });
       __syncthreads();  // tile i + 1 is in LDS; tile i's buffer may be overwritten
     };
     for (; i < n_unm; ++i) step(i, std::integral_constant<bool, false>{});
