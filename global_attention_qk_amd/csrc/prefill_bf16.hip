@@ -49,6 +49,16 @@ constexpr int kWavesPerBlock = ZG_PREFILL_WAVES;
 #ifndef ZG_GLOBAL_WAVES
 #define ZG_GLOBAL_WAVES 4
 #endif
+// LDS DMA buffers of the pipelined global path: tiles are fetched kDmaBufs - 1 ahead.
+#ifndef ZG_DMA_BUFS
+#define ZG_DMA_BUFS 3
+#endif
+constexpr int kDmaBufs = ZG_DMA_BUFS;
+// Phase of the pipelined tile (0 A .. 3 D) whose slots issue the DMA pieces.
+#ifndef ZG_DMA_PHASE
+#define ZG_DMA_PHASE 2
+#endif
+constexpr int kDmaPhase = ZG_DMA_PHASE;
 constexpr int kBN = 64;           // keys per tile
 constexpr int kMaxHalfMfma = 32;  // rotary_dim <= 64 on this path
 constexpr float kStaticShiftMax = 96.0f;  // largest score bound (log2 units) without a max
@@ -67,11 +77,11 @@ struct Smem {
   static constexpr int kKraw = kBN * kRowB;
   static constexpr int kKtrig = kBN * kMaxHalfMfma * 8;
   static constexpr int kLoop = 2 * kBuf + kKraw + kKtrig;
-  // Pipelined global path: three buffers filled by LDS DMA, each K~ as 64 unpadded rows
-  // of 2*D bytes and V^T as D unpadded rows of 128 bytes (16-byte chunks swizzled).
+  // Pipelined global path: kDmaBufs buffers filled by LDS DMA, each K~ as 64 unpadded
+  // rows of 2*D bytes and V^T as D unpadded rows of 128 bytes (16-byte chunks swizzled).
   static constexpr int kDK = kBN * D * 2;
   static constexpr int kDBuf = kDK + D * kBN * 2;
-  static constexpr int kDLoop = 3 * kDBuf;
+  static constexpr int kDLoop = kDmaBufs * kDBuf;
   static constexpr int kW = 2 * D * 4;  // wq, wk
   static constexpr int kMain = kLoop > kDLoop ? kLoop : kDLoop;
   static constexpr int kUnion = (kQ + kQtrig) > kMain ? (kQ + kQtrig) : kMain;
@@ -130,18 +140,18 @@ __device__ __forceinline__ int chunk_pos(int r, int c) {
   return c ^ (CPR == 16 ? (r & 15) : ((r & 7) ^ ((r >> 3) & 1)));
 }
 
-// LDS DMA of 16 bytes per lane: lane L's bytes from gbase + voff land at lds + 16 L.
-// gbase and lds must be wave-uniform (scalar base, M0). Completion is counted by vmcnt
+// LDS DMA of 16 bytes per lane: lane L's bytes from gbase + voff land at LDS byte
+// address lds + 16 L. gbase and lds must be wave-uniform (scalar base, M0). Completion is counted by vmcnt
 // and left to the caller (vm_wait): the compiler does not see these loads and inserts
 // no wait for them. One wait state separates the M0 write from the DMA that reads it.
-__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, const void* lds) {
+__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds) {
   // (readfirstlane returns int: each half goes through uint32_t so that it is
   // zero-extended, never sign-extended, into the 64-bit address)
   const uint64_t g = (uint64_t)(uintptr_t)gbase;
   const uint32_t glo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)g);
   const uint32_t ghi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(g >> 32));
   const uint64_t gu = ((uint64_t)ghi << 32) | (uint64_t)glo;
-  const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane(lds);
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                :: "s"(m0), "v"(voff), "s"(gu) : "memory", "m0");
 }
@@ -463,8 +473,9 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
   // Each lane fetches the chunk that the swizzle puts in its slot; K~ rows past the end
   // are clamped to the last row (masked keys).
   constexpr int KPW = D / 32;
+  const uint32_t lds_smem = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
   auto dma_piece = [&](int kt, int buf, int j) {
-    const char* dst = smem + buf * S::kDBuf;
+    const uint32_t dst = lds_smem + buf * S::kDBuf;
     const int k0 = kt * kBN;
     if (j < KPW) {
       constexpr int CPR = D / 8, RPB = 1024 / (2 * D);
@@ -652,7 +663,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
   };
   // Two query blocks per wave, static shift, K~ / V tiles from the workspace: a fenced
   // software pipeline over the tile's two 32-key blocks, one wave per SIMD,
-  //   A: QK(0) + DMA of tile i+2 | B: QK(1) + softmax(0) | C: P.V(0) + softmax(1) | D: P.V(1)
+  //   A: QK(0) | B: QK(1) + softmax(0) | C: P.V(0) + softmax(1) + DMA | D: P.V(1)
   // with the vector work cut into pieces placed between the MFMAs so that it issues in
   // their shadow (the P.V products are inline assembly, so the order is pinned with
   // scheduling barriers rather than left to the scheduler).
@@ -672,7 +683,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
     constexpr int QK_SPP = 8 / KS;               // softmax pieces per QK step
     constexpr int PV_STEPS = 2 * DB;
     constexpr int PV_SPP = 8 / PV_STEPS;         // softmax pieces per P.V step
-    static_assert(KS == 2 * KPW, "one DMA piece per block-0 score step");
+    static_assert(KS == 2 * KPW && PV_STEPS == KS, "one DMA piece per slot of a phase");
     const char* tb = smem + buf * S::kDBuf;
     const int k0 = kt * kBN;
     int rel[QB];
@@ -733,10 +744,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           sc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[qb][ks], sc[kb][qb], 0, 0, 0);
-        if (kb == 0) {
-          // A: the tile two ahead goes to its buffer under the block-0 score products
-          dma_piece(dma_kt, dma_buf, ks);
-        } else {
+        if (kb == 1) {
           // B: softmax of block 0 under the block-1 score products
 #pragma unroll
           for (int w = 0; w < QK_SPP; ++w) sm_piece(0, ks * QK_SPP + w);
@@ -753,6 +761,8 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
           for (int w = 0; w < PV_SPP; ++w) sm_piece(1, t * PV_SPP + w);
         }
       }
+      // a later tile goes to its buffer, one piece per slot of phase kDmaPhase
+      if (u / KS == kDmaPhase) dma_piece(dma_kt, dma_buf, u % KS);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -760,23 +770,25 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
 
   int i = 0;
   if constexpr (KPRE && QB == 2 && STATIC) {
-    // K~ / V^T tiles go from the workspace straight into LDS (DMA), two tiles ahead of
-    // their use, through three rotating buffers: one barrier per tile. Past the end the
-    // last tile is fetched again into the idle buffer (in bounds, never read).
+    // K~ / V^T tiles go from the workspace straight into LDS (DMA), kDmaBufs - 1 tiles
+    // ahead of their use, through kDmaBufs rotating buffers: one barrier per tile. Past
+    // the end the last tile is fetched again into an idle buffer (in bounds, never read).
+    constexpr int AHEAD = kDmaBufs - 1;
+    static_assert(AHEAD >= 1 && S::kDLoop <= S::kUnion, "DMA buffers");
     const int last = n_tiles - 1;
 #pragma unroll
-    for (int j = 0; j < KS; ++j) dma_piece(tile_of(0), 0, j);
+    for (int a = 0; a < AHEAD; ++a)
 #pragma unroll
-    for (int j = 0; j < KS; ++j) dma_piece(tile_of(min(1, last)), 1, j);
-    vm_wait<KS>();
+      for (int j = 0; j < KS; ++j) dma_piece(tile_of(min(a, last)), a, j);
+    vm_wait<(AHEAD - 1) * KS>();
     __syncthreads();
     int cur = 0;
     auto step = [&](int i, auto masked_tag) {
-      const int ahead = cur == 0 ? 2 : cur - 1;   // (cur + 2) % 3
-      compute_pipe(tile_of(i), cur, masked_tag, tile_of(min(i + 2, last)), ahead);
-      vm_wait<KS>();   // this wave's DMA of tile i + 1 has landed ...
+      const int ahead = (cur + AHEAD) % kDmaBufs;
+      compute_pipe(tile_of(i), cur, masked_tag, tile_of(min(i + AHEAD, last)), ahead);
+      vm_wait<(AHEAD - 1) * KS>();   // this wave's DMA of tile i + 1 has landed ...
       __syncthreads();  // ... and every wave's; tile i's buffer may be overwritten
-      cur = cur == 2 ? 0 : cur + 1;
+      cur = cur == kDmaBufs - 1 ? 0 : cur + 1;
     };
     for (; i < n_unm; ++i) step(i, std::integral_constant<bool, false>{});
     for (; i < n_tiles; ++i) step(i, std::integral_constant<bool, true>{});
