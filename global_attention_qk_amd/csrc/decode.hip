@@ -14,7 +14,8 @@
 //               the chunk's scores in LDS), then P.V streams V once on the vector ALUs.
 //               Partial (max, sum, acc) per split go to the workspace.
 //   3. combine: log-sum-exp merge of the splits per (sequence, query head).
-// SWA layers: one workgroup per (sequence, kv head) does the whole step over the ring.
+// SWA layers: one workgroup per (sequence, kv head) does the whole step over the ring
+// (staged in LDS when it holds at most 128 slots).
 #include "launch.h"
 
 namespace zg {
@@ -360,6 +361,147 @@ __global__ __launch_bounds__(kThreads) void swa_decode_kernel(const DecodeArgs p
   }
 }
 
+// Ring of at most 128 slots (the model's window): the whole ring is staged in LDS with
+// 16-byte loads issued together (one memory round trip instead of one per slot), and the
+// scores, softmax and P.V run from LDS. K rows are padded by 16 bytes so that the 64 lanes
+// of a wave, one slot each, read distinct banks.
+constexpr int kRingMax = 128;
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void swa_decode_ring_kernel(const DecodeArgs p) {
+  constexpr int KRB = D * 2 + 16;                  // padded K row (bytes)
+  constexpr int CPR = D / 8;                       // 16-byte chunks per row
+  constexpr int RIT = kRingMax * CPR / kThreads;   // chunks per thread per ring tensor
+  const int kvh = blockIdx.x, b = blockIdx.y;
+  const int G = p.Hq / p.Hkv;
+  const int W = p.window;
+  const int pos = p.pos[b];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  bf16* out = (bf16*)p.out + ((size_t)b * p.Hq + kvh * G) * D;
+  if (!pos_valid(pos, ZGATTN_POS_LIMIT)) {
+    for (int i = t; i < G * D; i += kThreads) out[i] = (bf16)__builtin_nanf("");
+    return;
+  }
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char* sK = smem;                                  // [W][KRB]
+  bf16* sV = (bf16*)(smem + kRingMax * KRB);        // [W][D]
+  float* buf = (float*)(smem + kRingMax * KRB + kRingMax * D * 2);   // G q rows + k_new
+  float* tmp = buf + (G + 1) * D;
+  float* sv = tmp + (G + 1) * D;                    // v_new
+  float* sS = sv + D;                               // [G][W]
+  bf16* kr = (bf16*)p.k_cache + ((size_t)b * p.Hkv + kvh) * W * D;
+  bf16* vr = (bf16*)p.v_cache + ((size_t)b * p.Hkv + kvh) * W * D;
+  // ring -> registers (all loads in flight together), then the new token's rows
+  const int nch = W * CPR;
+  u32x4 kc[RIT], vc[RIT];
+#pragma unroll
+  for (int it = 0; it < RIT; ++it) {
+    const int c = t + it * kThreads;
+    if (c < nch) {
+      kc[it] = *(const u32x4*)(kr + (size_t)c * 8);
+      vc[it] = *(const u32x4*)(vr + (size_t)c * 8);
+    }
+  }
+  const bf16* q = (const bf16*)p.q + ((size_t)b * p.Hq + kvh * G) * D;
+  const bf16* kn = (const bf16*)p.k_new + ((size_t)b * p.Hkv + kvh) * D;
+  const bf16* vn = (const bf16*)p.v_new + ((size_t)b * p.Hkv + kvh) * D;
+  for (int i = t; i < (G + 1) * D; i += kThreads)
+    buf[i] = i < G * D ? (float)q[i] : (float)kn[i - G * D];
+  for (int c = t; c < D; c += kThreads) sv[c] = (float)vn[c];
+  const float* wrow[9];
+  for (int r = 0; r < 9; ++r) wrow[r] = r < G ? p.wq : p.wk;
+  __syncthreads();
+  norm_rope_rows_lds<D>(buf, wrow, G + 1, pos, p.rdim, p.eps, p.fr, tmp);
+  const int slot = pos % W;
+#pragma unroll
+  for (int it = 0; it < RIT; ++it) {
+    const int c = t + it * kThreads;
+    if (c < nch) {
+      const int row = c / CPR, ch = c % CPR;
+      *(u32x4*)(sK + row * KRB + ch * 16) = kc[it];
+      *(u32x4*)(sV + (size_t)c * 8) = vc[it];
+    }
+  }
+  __syncthreads();
+  // the new entry as the ring will hold it (bf16), over the slot's old contents
+  for (int c = t; c < D; c += kThreads) {
+    const bf16 kb = (bf16)buf[G * D + c];
+    buf[G * D + c] = (float)kb;
+    ((bf16*)(sK + slot * KRB))[c] = kb;
+    sV[slot * D + c] = (bf16)sv[c];
+  }
+  __syncthreads();
+  // scores: one (head, slot) per thread and pass; four partial sums per dot product
+  const float qs = p.scale * 1.4426950408889634f;
+  for (int idx = t; idx < G * W; idx += kThreads) {
+    const int h = idx / W, s = idx - h * W;
+    float d = -INFINITY;
+    if (pos >= W - 1 || s <= pos) {
+      const float* qh = buf + h * D;
+      float a4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+      for (int ch = 0; ch < CPR; ++ch) {
+        const u32x4 raw = *(const u32x4*)(sK + s * KRB + ch * 16);
+        const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a4[e] = __builtin_fmaf(qh[ch * 8 + 2 * e], bf16_lo_to_f32(w4[e]), a4[e]);
+          a4[e] = __builtin_fmaf(qh[ch * 8 + 2 * e + 1], bf16_hi_to_f32(w4[e]), a4[e]);
+        }
+      }
+      d = ((a4[0] + a4[1]) + (a4[2] + a4[3])) * qs;
+    }
+    sS[idx] = d;
+  }
+  __syncthreads();
+  for (int h = wave; h < G; h += kThreads / 64) {
+    float m = -INFINITY;
+    for (int s = lane; s < W; s += 64) m = fmaxf(m, sS[h * W + s]);
+    m = wave_max(m);
+    float l = 0.f;
+    for (int s = lane; s < W; s += 64) {
+      const float e = fast_exp2(sS[h * W + s] - m);
+      sS[h * W + s] = e;
+      l += e;
+    }
+    l = wave_sum(l);
+    const float inv = 1.0f / l;
+    for (int s = lane; s < W; s += 64) sS[h * W + s] *= inv;
+  }
+  __syncthreads();
+  // P.V: two adjacent dims of one head per thread and pass
+  const bf16* g = (const bf16*)p.g + ((size_t)b * p.Hq + kvh * G) * D;
+  const int ns = pos >= W - 1 ? W : pos + 1;
+  for (int idx = t; idx < G * D / 2; idx += kThreads) {
+    const int h = idx / (D / 2), c = 2 * (idx - h * (D / 2));
+    const float* ph = sS + h * W;
+    float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+    int s = 0;
+    for (; s + 1 < ns; s += 2) {
+      const uint32_t v0 = *(const uint32_t*)(sV + s * D + c);
+      const uint32_t v1 = *(const uint32_t*)(sV + (s + 1) * D + c);
+      o0 = __builtin_fmaf(ph[s], bf16_lo_to_f32(v0), o0);
+      o1 = __builtin_fmaf(ph[s], bf16_hi_to_f32(v0), o1);
+      o2 = __builtin_fmaf(ph[s + 1], bf16_lo_to_f32(v1), o2);
+      o3 = __builtin_fmaf(ph[s + 1], bf16_hi_to_f32(v1), o3);
+    }
+    if (s < ns) {
+      const uint32_t v0 = *(const uint32_t*)(sV + s * D + c);
+      o0 = __builtin_fmaf(ph[s], bf16_lo_to_f32(v0), o0);
+      o1 = __builtin_fmaf(ph[s], bf16_hi_to_f32(v0), o1);
+    }
+    const uint32_t gw = *(const uint32_t*)(g + h * D + c);
+    const bf16x2 ov = {(bf16)((o0 + o2) * sigmoidf_(bf16_lo_to_f32(gw))),
+                       (bf16)((o1 + o3) * sigmoidf_(bf16_hi_to_f32(gw)))};
+    *(bf16x2*)(out + h * D + c) = ov;
+  }
+  // the ring slot last (every read of the old ring came from the staged copy)
+  for (int c = t; c < D; c += kThreads) {
+    kr[(size_t)slot * D + c] = (bf16)buf[G * D + c];
+    vr[(size_t)slot * D + c] = (bf16)sv[c];
+  }
+}
+
 template <typename K>
 hipError_t launch_dyn(K kern, dim3 grid, dim3 block, int smem, hipStream_t s,
                       const DecodeArgs& a) {
@@ -416,6 +558,14 @@ hipError_t launch_global_decode(const DecodeArgs& a, hipStream_t s) {
 hipError_t launch_swa_decode(const DecodeArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   const int smem = (2 * (G + 1) * a.d + a.d + G * a.window) * 4;
+  if (a.window <= kRingMax) {
+    const int ring = kRingMax * (a.d * 2 + 16) + kRingMax * a.d * 2;
+    if (a.d == 128)
+      return launch_dyn(swa_decode_ring_kernel<128>, dim3(a.Hkv, a.B), dim3(kThreads),
+                        ring + smem, s, a);
+    return launch_dyn(swa_decode_ring_kernel<64>, dim3(a.Hkv, a.B), dim3(kThreads), ring + smem,
+                      s, a);
+  }
   if (a.d == 128) return launch_dyn(swa_decode_kernel<128>, dim3(a.Hkv, a.B), dim3(kThreads), smem, s, a);
   return launch_dyn(swa_decode_kernel<64>, dim3(a.Hkv, a.B), dim3(kThreads), smem, s, a);
 }

@@ -94,26 +94,34 @@ def test_global_decode_vs_oracle(B, Hq, Hkv, d, S, pos):
         assert np.array_equal(kc2[b, :, mask], host64(kc)[b, :, mask])
 
 
-@pytest.mark.parametrize("pos", [[0, 5, 126, 127, 128, 300, 100000]])
-def test_swa_decode_vs_oracle(pos):
+# Rings of at most 128 slots are staged in LDS; larger rings take the per-slot kernel.
+@pytest.mark.parametrize("W,d,Hq,Hkv", [(128, 128, 8, 2), (128, 64, 8, 1), (50, 128, 2, 2),
+                                        (77, 64, 16, 2), (1, 128, 4, 1), (300, 128, 8, 2)])
+def test_swa_decode_vs_oracle(W, d, Hq, Hkv):
     zg = _zg()
     import torch
-    B, Hq, Hkv, d, W = len(pos), 8, 2, 128, 128
-    q, g, kn, vn, kr, vr, wq, wk = _decode_case(B, Hq, Hkv, d, W, 2000)
+    pos = sorted({0, 5, max(W - 2, 0), W - 1, W, 300, 100000})
+    B = len(pos)
+    r = zg.rotary_dim_for(d)
+    q, g, kn, vn, kr, vr, wq, wk = _decode_case(B, Hq, Hkv, d, W, 2000 + W)
     krd, vrd = kr.cuda(), vr.cuda()
     posd = torch.tensor(pos, dtype=torch.int32, device="cuda")
     out = zg.swa_decode(q.cuda(), kn.cuda(), vn.cuda(), g.cuda(), wq.cuda(), wk.cuda(), krd,
-                        vrd, posd)
+                        vrd, posd, rotary_dim=r)
     torch.cuda.synchronize()
     want, ktn = O.decode_swa(host64(q), host64(kn), host64(vn), host64(g), host64(wq),
                              host64(wk), host64(kr), host64(vr), np.array(pos), window=W,
-                             rotary_dim=42)
+                             rotary_dim=r)
     err = maxabs(host64(out), want)
-    say("swa_decode", pos, err)
+    say("swa_decode", W, d, Hq, Hkv, pos, err)
     assert err <= TOL_BF16
-    kr2 = host64(krd)
+    kr2, vr2 = host64(krd), host64(vrd)
     for b, p in enumerate(pos):
         assert maxabs(kr2[b, :, p % W], ktn[b]) <= 2e-2
+        assert np.array_equal(vr2[b, :, p % W], host64(vn)[b])
+        others = np.ones(W, bool)
+        others[p % W] = False
+        assert np.array_equal(kr2[b, :, others], host64(kr)[b, :, others])
 
 
 def test_decode_equals_prefill_row():
