@@ -40,6 +40,9 @@ def parse():
                                        "swa_decode", "copy"], default=None,
                     help="run just this call (warmup + steps launches, for profilers); "
                          "'copy' is a plain 1 GiB device copy used to calibrate counters")
+    ap.add_argument("--sweep", action="store_true",
+                    help="attention-stack sweep: 32-layer hybrid / SWA 3:1 / full-attention "
+                         "stacks at T = 4K .. 256K (one JSON line per T)")
     return ap.parse_args()
 
 
@@ -99,6 +102,8 @@ def main():
     torch.cuda.init()
     if args.only:
         return run_only(args)
+    if args.sweep:
+        return run_sweep(args)
     T, B, Hq, Hkv, d, W = C4.T, C4.B, C4.Hq, C4.Hkv, C4.d, C4.window
     r = C4.rotary_dim
     # ---- inputs (seeded, generated on the device, outside the timed region) -----------
@@ -217,6 +222,72 @@ def main():
         del q, k, v, g, out_s, out_g, ws
         rec["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(rec), flush=True)
+
+
+SWEEP_T = (4096, 8192, 16384, 32768, 65536, 131072, 262144)
+
+
+def run_sweep(args):
+    """Attention-only stack sweep (B=1, Hq=32, Hkv=8, d=128, rotary 42, W=128): for each
+    T, the 32 layers of each stack run back-to-back on one stream over one seeded input
+    set (a layer's time does not depend on the values), timed with HIP events around the
+    whole stack. Prints one JSON line per T."""
+    import torch
+
+    import global_attention_qk_amd as zg
+    from workloads import C4, STACKS, prefill_inputs, stack_kinds
+
+    dev = "cuda"
+    r, W = C4.rotary_dim, C4.window
+    kv_tok = {n: 2 * stack_kinds(p).count("global") * C4.Hkv * C4.d * 2
+              for n, p in STACKS.items()}
+    for T in SWEEP_T:
+        q, k, v, g, wq, wk = prefill_inputs(C4, device=dev, T=T)
+        out_s, out_g = torch.empty_like(q), torch.empty_like(q)
+        ws = torch.empty(zg.global_prefill_workspace_bytes(q, k, rotary_dim=r),
+                         dtype=torch.uint8, device=dev)
+
+        def layer(kind):
+            if kind == "swa":
+                zg.swa_prefill(q, k, v, g, wq, wk, window=W, rotary_dim=r, out=out_s)
+            else:
+                zg.global_prefill(q, k, v, wq, wk, rotary_dim=r, workspace=ws, out=out_g)
+
+        def timed(fn, reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            best = []
+            for _ in range(reps):
+                e0.record()
+                fn()
+                e1.record()
+                torch.cuda.synchronize()
+                best.append(e0.elapsed_time(e1))
+            return sorted(best)[len(best) // 2]
+
+        layer("swa")
+        layer("global")
+        torch.cuda.synchronize()
+        reps = 3 if T <= 65536 else 1
+        one = {kind: timed(lambda kind=kind: layer(kind), 3) for kind in ("swa", "global")}
+        ms = {}
+        for name, period in STACKS.items():
+            kinds = stack_kinds(period)
+            ms[name] = timed(lambda kinds=kinds: [layer(kd) for kd in kinds], reps)
+            print(f"[sweep] T={T} {name}: {ms[name]:.2f} ms", file=sys.stderr, flush=True)
+        rec = {
+            "sweep": "32-layer attention stack, B=1 Hq=32 Hkv=8 d=128 rotary 42 W=128 bf16",
+            "T": T,
+            "layer_ms": {kd: round(x, 4) for kd, x in one.items()},
+            "stack_ms": {n: round(x, 3) for n, x in ms.items()},
+            "stack_tokens_per_s": {n: T / (x / 1e3) for n, x in ms.items()},
+            "full_over_hybrid": ms["full"] / ms["hybrid_5to1"],
+            "full_over_swa_3to1": ms["full"] / ms["swa_3to1"],
+            "kv_cache_bytes_per_token": kv_tok,
+            "kv_cache_GiB_at_T": {n: x * T / 2 ** 30 for n, x in kv_tok.items()},
+        }
+        print(json.dumps(rec), flush=True)
+        del q, k, v, g, out_s, out_g, ws
+        torch.cuda.empty_cache()
 
 
 def run_only(args):

@@ -57,6 +57,17 @@ C5 = Workload("c5_decode_bf16_B32_ctx262144", 5, "decode", "bf16", 32, 262144, 3
               _rdim(128))
 CONFIGS = {1: C1, 2: C2, 3: C3, 4: C4, 5: C5}
 
+# Attention stacks of the 32-layer backbone compared in the stack sweep: the model's
+# hybrid (every sixth layer global: 27 gated SWA + 5 global), the SWA 3:1 alternative
+# (every fourth layer global: 24 + 8) and the full-attention baseline (32 global).
+STACKS = {"hybrid_5to1": 6, "swa_3to1": 4, "full": 1}
+
+
+def stack_kinds(period: int, n_layers: int = 32):
+    """Per-layer kind ("swa" / "global") of a stack whose every ``period``-th layer
+    (counting from 1) is global; period 1 makes every layer global."""
+    return ["global" if (i + 1) % period == 0 else "swa" for i in range(n_layers)]
+
 
 def seed_for(config: int, layer: int, slot: str) -> int:
     return 1000 * config + 10 * layer + SLOT[slot]
