@@ -40,6 +40,10 @@ def parse():
                                        "swa_decode", "copy"], default=None,
                     help="run just this call (warmup + steps launches, for profilers); "
                          "'copy' is a plain 1 GiB device copy used to calibrate counters")
+    ap.add_argument("--model-decode", action="store_true",
+                    help="decode step of the whole 32-layer hybrid stack (27 SWA rings + 5 "
+                         "global caches, B=32 at context 262144): one batched call against "
+                         "32 single-layer calls")
     ap.add_argument("--sweep", action="store_true",
                     help="attention-stack sweep: 32-layer hybrid / SWA 3:1 / full-attention "
                          "stacks at T = 4K .. 256K (one JSON line per T)")
@@ -104,6 +108,8 @@ def main():
         return run_only(args)
     if args.sweep:
         return run_sweep(args)
+    if args.model_decode:
+        return run_model_decode(args)
     T, B, Hq, Hkv, d, W = C4.T, C4.B, C4.Hq, C4.Hkv, C4.d, C4.window
     r = C4.rotary_dim
     # ---- inputs (seeded, generated on the device, outside the timed region) -----------
@@ -221,6 +227,90 @@ def main():
     if args.cpu_baseline == "on":
         del q, k, v, g, out_s, out_g, ws
         rec["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+def run_model_decode(args):
+    """Decode step of the model's 32-layer stack at B=32, context 262,144: 27 gated SWA
+    layers (128-slot rings) and 5 global layers (262,144-position caches), each layer with
+    its own seeded tensors. Times the batched zgattn_model_decode call and, for reference,
+    the same step as 32 single-layer calls. Prints one JSON line."""
+    import torch
+
+    import global_attention_qk_amd as zg
+    from workloads import C5, STACKS, decode_inputs, stack_kinds
+
+    dev = "cuda"
+    kinds = stack_kinds(STACKS["hybrid_5to1"])
+    B, S, W, r = C5.B, C5.T, C5.window, C5.rotary_dim
+    layers = []
+    for i, kind in enumerate(kinds):
+        x = decode_inputs(C5, device=dev, layer=i, kind=kind)
+        layers.append(dict(kind=kind, q=x["q"], g=x["g"] if kind == "swa" else None,
+                           k_new=x["k_new"], v_new=x["v_new"], wq=x["wq"], wk=x["wk"],
+                           k_cache=x["k_ring"] if kind == "swa" else x["k_cache"],
+                           v_cache=x["v_ring"] if kind == "swa" else x["v_cache"],
+                           out=torch.empty_like(x["q"])))
+        print(f"[model-decode] layer {i} ({kind}) inputs ready", file=sys.stderr, flush=True)
+    pos = torch.full((B,), S - 1, dtype=torch.int32, device=dev)
+    ws = torch.empty(zg.model_decode_workspace_bytes(layers, S, rotary_dim=r), dtype=torch.uint8,
+                     device=dev)
+    dws = torch.empty(zg.global_decode_workspace_bytes(layers[0]["q"], layers[0]["k_new"], S),
+                      dtype=torch.uint8, device=dev)
+
+    def batched():
+        zg.model_decode(layers, pos, window=W, capacity=S, rotary_dim=r, workspace=ws)
+
+    def per_layer():
+        for L in layers:
+            if L["kind"] == "swa":
+                zg.swa_decode(L["q"], L["k_new"], L["v_new"], L["g"], L["wq"], L["wk"],
+                              L["k_cache"], L["v_cache"], pos, rotary_dim=r, out=L["out"])
+            else:
+                zg.global_decode(L["q"], L["k_new"], L["v_new"], L["wq"], L["wk"],
+                                 L["k_cache"], L["v_cache"], pos, rotary_dim=r, workspace=dws,
+                                 out=L["out"])
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    swa_layers = [L for L in layers if L["kind"] == "swa"]
+
+    def batched_swa():
+        zg.model_decode(swa_layers, pos, window=W, capacity=S, rotary_dim=r, workspace=ws)
+
+    steps = max(args.steps, 1)
+    t_b = timed(batched, steps)
+    t_l = timed(per_layer, steps)
+    t_s = timed(batched_swa, steps)
+    n_glob, n_swa = kinds.count("global"), kinds.count("swa")
+    el = 2
+    glob_bytes = B * C5.Hkv * S * C5.d * el * 2 + B * C5.d * el * (2 * C5.Hq + 2 * C5.Hkv)
+    swa_bytes = B * C5.Hkv * W * C5.d * el * 2 + B * C5.d * el * (3 * C5.Hq + 2 * C5.Hkv)
+    total = n_glob * glob_bytes + n_swa * swa_bytes
+    rec = {
+        "model_decode": "32-layer hybrid stack (27 gated SWA, 5 global), B=32, context 262144, "
+                        "Hq=32 Hkv=8 d=128 bf16",
+        "steps": steps,
+        "ms_per_step_batched": t_b,
+        "ms_per_step_single_layer_calls": t_l,
+        "tokens_per_s": B / (t_b / 1e3),
+        "alg_bytes_per_step": total,
+        "hbm_GBs": total / (t_b / 1e3) / 1e9,
+        "hbm_frac": total / (t_b / 1e3) / 1e9 / PEAK_HBM_GBS,
+        "ms_swa_layers_batched": t_s,
+        "swa_layers_hbm_GBs": n_swa * swa_bytes / (t_s / 1e3) / 1e9,
+        "kv_cache_GiB": (n_glob * B * C5.Hkv * S * C5.d * el * 2 + n_swa * B * C5.Hkv * W * C5.d
+                         * el * 2) / 2 ** 30,
+    }
     print(json.dumps(rec), flush=True)
 
 

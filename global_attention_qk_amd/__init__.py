@@ -11,6 +11,8 @@ from .api import (  # noqa: F401
     global_prefill,
     global_prefill_workspace_bytes,
     make_desc,
+    model_decode,
+    model_decode_workspace_bytes,
     qknorm_rope,
     rotary_dim_for,
     swa_decode,

@@ -33,6 +33,12 @@ class Desc(ctypes.Structure):
     ]
 
 
+class DecodeLayer(ctypes.Structure):
+    """zgattn_decode_layer: one layer's device tensors in a stack decode step."""
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("q", "k_new", "v_new", "g", "wq", "wk", "k_cache", "v_cache", "out")]
+
+
 class ZgattnError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -55,6 +61,9 @@ SIGNATURES = {
     "zgattn_global_decode": (ctypes.c_int, [DP, P, P, P, P, P, P, P, I32, P, P, SZ, P, P]),
     "zgattn_global_decode_workspace_bytes": (SZ, [DP, I32]),
     "zgattn_qknorm_rope": (ctypes.c_int, [DP, I32, P, P, P, P, I64, I64, I64, P]),
+    "zgattn_model_decode": (ctypes.c_int, [DP, I32, ctypes.POINTER(I32),
+                                           ctypes.POINTER(DecodeLayer), I32, P, P, SZ, P]),
+    "zgattn_model_decode_workspace_bytes": (SZ, [DP, I32, ctypes.POINTER(I32), I32]),
 }
 
 

@@ -14,7 +14,7 @@ from typing import Optional
 
 import torch
 
-from ._lib import BF16, F32, Desc, check, lib
+from ._lib import BF16, F32, DecodeLayer, Desc, check, lib
 
 
 def rotary_dim_for(head_dim: int, ratio: float = 0.33) -> int:
@@ -171,3 +171,56 @@ def qknorm_rope(x, w, *, pos=None, rotary_dim=None, pos_offset=0, rope_base=1000
                                    _ptr(out), sb, st, sh, _stream()),
           "zgattn_qknorm_rope")
     return out
+
+
+def _stack_tables(layers):
+    n = len(layers)
+    kinds = (ctypes.c_int32 * max(n, 1))(*[1 if L["kind"] == "global" else 0 for L in layers])
+    return n, kinds
+
+
+def model_decode_workspace_bytes(layers, capacity: int, *, rotary_dim=None) -> int:
+    """Workspace bytes of a model_decode call over ``layers`` (global layers' partials)."""
+    L0 = layers[0]
+    n, kinds = _stack_tables(layers)
+    d = _decode_desc(L0["q"], L0["k_new"], 1, rotary_dim, 10000.0, 1e-6, 0.0)
+    return int(lib().zgattn_model_decode_workspace_bytes(ctypes.byref(d), n, kinds, capacity))
+
+
+def model_decode(layers, pos, *, window=128, capacity=None, rotary_dim=None,
+                 rope_base=10000.0, eps=1e-6, scale=0.0, workspace=None):
+    """One decode step of a layer stack in a few launches.
+
+    ``layers``: list of dicts with kind ("swa" / "global"), q, k_new, v_new, g (SWA only),
+    wq, wk, k_cache, v_cache (SWA rings [B,Hkv,window,d] / global caches
+    [B,Hkv,capacity,d]) and optional out. Returns the list of outputs; caches are updated
+    in place.
+    """
+    if not layers:
+        return []
+    for L in layers:
+        _dev(L["q"], L["k_new"], L["v_new"], L.get("g"), L["wq"], L["wk"], L["k_cache"],
+             L["v_cache"], L.get("out"))
+        if L.get("out") is None:
+            L["out"] = torch.empty_like(L["q"])
+    _dev(pos)
+    if pos.dtype != torch.int32:
+        raise TypeError("pos must be int32")
+    if capacity is None:
+        caps = [L["k_cache"].shape[2] for L in layers if L["kind"] == "global"]
+        capacity = caps[0] if caps else 1
+    n, kinds = _stack_tables(layers)
+    L0 = layers[0]
+    d = _decode_desc(L0["q"], L0["k_new"], window, rotary_dim, rope_base, eps, scale)
+    if workspace is None:
+        nbytes = int(lib().zgattn_model_decode_workspace_bytes(ctypes.byref(d), n, kinds,
+                                                              capacity))
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=L0["q"].device)
+    tab = (DecodeLayer * n)(*[DecodeLayer(*[None if L.get(f) is None else L[f].data_ptr()
+                                            for f in ("q", "k_new", "v_new", "g", "wq", "wk",
+                                                      "k_cache", "v_cache", "out")])
+                              for L in layers])
+    check(lib().zgattn_model_decode(ctypes.byref(d), n, kinds, tab, capacity, _ptr(pos),
+                                    _ptr(workspace), workspace.numel(), _stream()),
+          "zgattn_model_decode")
+    return [L["out"] for L in layers]

@@ -260,6 +260,76 @@ int zgattn_global_decode(const zgattn_desc* d, const void* q, const void* k_new,
   return hip_status(launch_global_decode(a, (hipStream_t)stream));
 }
 
+size_t zgattn_model_decode_workspace_bytes(const zgattn_desc* d, int32_t n_layers,
+                                           const int32_t* is_global, int32_t capacity) {
+  if (check_desc(d) || n_layers < 0 || (n_layers > 0 && !is_global)) return 0;
+  int n_glob = 0;
+  for (int i = 0; i < n_layers; ++i) n_glob += is_global[i] != 0;
+  if (n_glob == 0) return 0;
+  const size_t per = zgattn_global_decode_workspace_bytes(d, capacity);
+  return per ? n_glob * ((per + 255) & ~(size_t)255) : 0;
+}
+
+int zgattn_model_decode(const zgattn_desc* d, int32_t n_layers, const int32_t* is_global,
+                        const zgattn_decode_layer* layers, int32_t capacity,
+                        const int32_t* pos, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  int st = check_desc(d);
+  if (st) return st;
+  if (n_layers < 0 || n_layers > 1024) return ZGATTN_EINVAL;
+  if (n_layers == 0) return ZGATTN_OK;
+  if (!is_global || !layers || !pos) return ZGATTN_ENULL;
+  // every layer is checked before anything is launched
+  int n_glob = 0, n_swa = 0;
+  for (int i = 0; i < n_layers; ++i) {
+    const zgattn_decode_layer& L = layers[i];
+    st = decode_common(d, L.q, L.k_new, L.v_new, L.wq, L.wk, L.k_cache, L.v_cache, pos, L.out);
+    if (st) return st;
+    if (is_global[i]) {
+      ++n_glob;
+    } else {
+      if (!L.g) return ZGATTN_ENULL;
+      if (!aligned16(L.g)) return ZGATTN_EINVAL;
+      ++n_swa;
+    }
+  }
+  if (n_swa && (d->window < 1 || d->window > kSwaDecodeLayersMaxWindow))
+    return ZGATTN_EUNSUPPORTED;
+  DecodeArgs a = make_decode(d, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                             nullptr, pos, nullptr);
+  size_t stride = 0;
+  if (n_glob) {
+    if (capacity < 1 || capacity > ZGATTN_MAX_POSITION + 1) return ZGATTN_ERANGE;
+    if (!workspace || !aligned16(workspace)) return ZGATTN_EWORKSPACE;
+    size_t per;
+    global_decode_geometry(a.B, a.Hq, a.d, capacity, &a.nsplit, &a.chunk, &per);
+    stride = (per + 255) & ~(size_t)255;
+    if (workspace_bytes < n_glob * stride) return ZGATTN_EWORKSPACE;
+    a.S = capacity;
+  }
+  // launches per kind, kMaxDecodeLayers layers at a time (all SWA layers first)
+  const hipStream_t s = (hipStream_t)stream;
+  LayerIO io[kMaxDecodeLayers];
+  for (int kind = 0; kind < 2; ++kind) {
+    int m = 0, gi = 0;
+    for (int i = 0; i <= n_layers; ++i) {
+      const bool take = i < n_layers && (is_global[i] != 0) == (kind == 1);
+      if (take) {
+        const zgattn_decode_layer& L = layers[i];
+        io[m++] = LayerIO{L.q, L.k_new, L.v_new, L.g, L.wq, L.wk, L.k_cache, L.v_cache, L.out,
+                          kind ? (float*)((char*)workspace + (gi++) * stride) : nullptr};
+      }
+      if (m == kMaxDecodeLayers || (i == n_layers && m > 0)) {
+        st = hip_status(kind ? launch_global_decode_layers(a, io, m, s)
+                             : launch_swa_decode_layers(a, io, m, s));
+        if (st) return st;
+        m = 0;
+      }
+    }
+  }
+  return ZGATTN_OK;
+}
+
 int zgattn_qknorm_rope(const zgattn_desc* d, int32_t n_heads, const void* x, const float* w,
                        const int32_t* pos, void* y, int64_t y_stride_b, int64_t y_stride_t,
                        int64_t y_stride_h, void* stream) {

@@ -25,6 +25,11 @@ constexpr int kThreads = 256;
 
 __device__ __forceinline__ bool pos_valid(int pos, int limit) { return pos >= 0 && pos < limit; }
 
+// The per-layer tensors of a single-layer call.
+__device__ __forceinline__ LayerIO layer_io(const DecodeArgs& p) {
+  return LayerIO{p.q, p.k_new, p.v_new, p.g, p.wq, p.wk, p.k_cache, p.v_cache, p.out, p.ws};
+}
+
 // Normalise + rotate `nrows` rows of d values held in LDS (fp32, stride D) in place.
 // Each wave takes rows wave, wave + 4, ...; all threads must call it.
 template <int D>
@@ -73,8 +78,7 @@ __device__ void norm_rope_rows_lds(float* buf, const float* wrow[], int nrows, i
 // Global decode, step 1: prep.
 // ---------------------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kThreads) void gdec_prep_kernel(const DecodeArgs p) {
-  const int kvh = blockIdx.x, b = blockIdx.y;
+__device__ __forceinline__ void gdec_prep_kernel_body(const DecodeArgs& p, const LayerIO& io, int kvh, int b) {
   const int G = p.Hq / p.Hkv;
   const int pos = p.pos[b];
   if (!pos_valid(pos, p.S)) return;
@@ -82,34 +86,42 @@ __global__ __launch_bounds__(kThreads) void gdec_prep_kernel(const DecodeArgs p)
   float* buf = (float*)smem;                 // (G + 1) rows
   float* tmp = buf + (G + 1) * D;
   const int t = threadIdx.x;
-  const bf16* q = (const bf16*)p.q + ((size_t)b * p.Hq + kvh * G) * D;
-  const bf16* kn = (const bf16*)p.k_new + ((size_t)b * p.Hkv + kvh) * D;
+  const bf16* q = (const bf16*)io.q + ((size_t)b * p.Hq + kvh * G) * D;
+  const bf16* kn = (const bf16*)io.k_new + ((size_t)b * p.Hkv + kvh) * D;
   for (int i = t; i < (G + 1) * D; i += kThreads)
     buf[i] = i < G * D ? (float)q[i] : (float)kn[i - G * D];
   const float* wrow[9];
-  for (int r = 0; r < 9; ++r) wrow[r] = r < G ? p.wq : p.wk;
+  for (int r = 0; r < 9; ++r) wrow[r] = r < G ? io.wq : io.wk;
   __syncthreads();
   norm_rope_rows_lds<D>(buf, wrow, G + 1, pos, p.rdim, p.eps, p.fr, tmp);
   const float qs = p.scale * 1.4426950408889634f;
-  float* wsq = p.ws + ((size_t)b * p.Hq + kvh * G) * D;
+  float* wsq = io.ws + ((size_t)b * p.Hq + kvh * G) * D;
   for (int i = t; i < G * D; i += kThreads) wsq[i] = buf[i] * qs;
   const size_t crow = (((size_t)b * p.Hkv + kvh) * p.S + pos) * D;
-  const bf16* vn = (const bf16*)p.v_new + ((size_t)b * p.Hkv + kvh) * D;
+  const bf16* vn = (const bf16*)io.v_new + ((size_t)b * p.Hkv + kvh) * D;
   for (int c = t; c < D; c += kThreads) {
-    ((bf16*)p.k_cache)[crow + c] = (bf16)buf[G * D + c];
-    ((bf16*)p.v_cache)[crow + c] = vn[c];
+    ((bf16*)io.k_cache)[crow + c] = (bf16)buf[G * D + c];
+    ((bf16*)io.v_cache)[crow + c] = vn[c];
   }
+}
+template <int D>
+__global__ __launch_bounds__(kThreads) void gdec_prep_kernel(const DecodeArgs p) {
+  gdec_prep_kernel_body<D>(p, layer_io(p), (int)blockIdx.x, (int)blockIdx.y);
+}
+template <int D>
+__global__ __launch_bounds__(kThreads) void gdec_prep_kernel_layers(const DecodeBatchArgs pb) {
+  const int layer = blockIdx.z;
+  gdec_prep_kernel_body<D>(pb.a, pb.io[layer], (int)blockIdx.x, (int)blockIdx.y);
 }
 
 // ---------------------------------------------------------------------------------------
 // Global decode, step 2: one split of the cache.
 // ---------------------------------------------------------------------------------------
 template <int D, int G>
-__global__ __launch_bounds__(kThreads) void gdec_split_kernel(const DecodeArgs p) {
+__device__ __forceinline__ void gdec_split_kernel_body(const DecodeArgs& p, const LayerIO& io, int split, int kvh, int b) {
   constexpr int KS = D / 32;            // k-steps of the 16x16x32 product
   constexpr int DC = D / 8;             // 8-wide d chunks
   constexpr int NKL = kThreads / DC;    // key lanes in the P.V phase
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int pos = p.pos[b];
   if (!pos_valid(pos, p.S)) return;
   const int c0 = split * p.chunk;
@@ -124,13 +136,13 @@ __global__ __launch_bounds__(kThreads) void gdec_split_kernel(const DecodeArgs p
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int l16 = lane & 15, q4 = lane >> 4;
   const size_t cbase = (((size_t)b * p.Hkv + kvh) * p.S + c0) * D;
-  const bf16* kc = (const bf16*)p.k_cache + cbase;
-  const bf16* vc = (const bf16*)p.v_cache + cbase;
+  const bf16* kc = (const bf16*)io.k_cache + cbase;
+  const bf16* vc = (const bf16*)io.v_cache + cbase;
 
   // q~ as the B operand: column = head l16 (zero beyond G), k = d.
   bf16x8 qb[KS];
   {
-    const float* wsq = p.ws + ((size_t)b * p.Hq + kvh * G) * D;
+    const float* wsq = io.ws + ((size_t)b * p.Hq + kvh * G) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       bf16x8 v;
@@ -227,32 +239,41 @@ __global__ __launch_bounds__(kThreads) void gdec_split_kernel(const DecodeArgs p
     float s = 0.f;
     for (int k = 0; k < NKL; ++k) s += sRed[(k * G + h) * D + d];
     const size_t hq = (size_t)b * p.Hq + kvh * G + h;
-    p.ws[(size_t)p.B * p.Hq * D + (hq * p.nsplit + split) * D + d] = s;
+    io.ws[(size_t)p.B * p.Hq * D + (hq * p.nsplit + split) * D + d] = s;
   }
   if (t < G) {
     const size_t hq = (size_t)b * p.Hq + kvh * G + t;
-    float* ml = p.ws + (size_t)p.B * p.Hq * D * (1 + (size_t)p.nsplit);
+    float* ml = io.ws + (size_t)p.B * p.Hq * D * (1 + (size_t)p.nsplit);
     ml[(hq * p.nsplit + split) * 2 + 0] = sM[t];
     ml[(hq * p.nsplit + split) * 2 + 1] = sL[t];
   }
+}
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void gdec_split_kernel(const DecodeArgs p) {
+  gdec_split_kernel_body<D, G>(p, layer_io(p), (int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z);
+}
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void gdec_split_kernel_layers(const DecodeBatchArgs pb) {
+  const int layer = blockIdx.z / pb.a.B;
+  gdec_split_kernel_body<D, G>(pb.a, pb.io[layer], (int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z % pb.a.B);
 }
 
 // ---------------------------------------------------------------------------------------
 // Global decode, step 3: log-sum-exp merge of the splits.
 // ---------------------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(D) void gdec_combine_kernel(const DecodeArgs p) {
-  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+__device__ __forceinline__ void gdec_combine_kernel_body(const DecodeArgs& p, const LayerIO& io, int h, int b) {
+  const int d = threadIdx.x;
   const int pos = p.pos[b];
-  bf16* out = (bf16*)p.out + ((size_t)b * p.Hq + h) * D;
+  bf16* out = (bf16*)io.out + ((size_t)b * p.Hq + h) * D;
   if (!pos_valid(pos, p.S)) {
     out[d] = (bf16)__builtin_nanf("");
     return;
   }
   const int ns = min(p.nsplit, pos / p.chunk + 1);
   const size_t hq = (size_t)b * p.Hq + h;
-  const float* acc = p.ws + (size_t)p.B * p.Hq * D + hq * p.nsplit * D;
-  const float* ml = p.ws + (size_t)p.B * p.Hq * D * (1 + (size_t)p.nsplit) + hq * p.nsplit * 2;
+  const float* acc = io.ws + (size_t)p.B * p.Hq * D + hq * p.nsplit * D;
+  const float* ml = io.ws + (size_t)p.B * p.Hq * D * (1 + (size_t)p.nsplit) + hq * p.nsplit * 2;
   float M = -INFINITY;
   for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[2 * s]);
   float L = 0.f, o = 0.f;
@@ -262,6 +283,15 @@ __global__ __launch_bounds__(D) void gdec_combine_kernel(const DecodeArgs p) {
     o = __builtin_fmaf(acc[(size_t)s * D + d], w, o);
   }
   out[d] = (bf16)(o / L);
+}
+template <int D>
+__global__ __launch_bounds__(D) void gdec_combine_kernel(const DecodeArgs p) {
+  gdec_combine_kernel_body<D>(p, layer_io(p), (int)blockIdx.x, (int)blockIdx.y);
+}
+template <int D>
+__global__ __launch_bounds__(D) void gdec_combine_kernel_layers(const DecodeBatchArgs pb) {
+  const int layer = blockIdx.z;
+  gdec_combine_kernel_body<D>(pb.a, pb.io[layer], (int)blockIdx.x, (int)blockIdx.y);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -363,34 +393,36 @@ __global__ __launch_bounds__(kThreads) void swa_decode_kernel(const DecodeArgs p
 
 // Ring of at most 128 slots (the model's window): the whole ring is staged in LDS with
 // 16-byte loads issued together (one memory round trip instead of one per slot), and the
-// scores, softmax and P.V run from LDS. K rows are padded by 16 bytes so that the 64 lanes
-// of a wave, one slot each, read distinct banks.
+// scores, softmax and P.V run from LDS. The 16-byte chunks of a K row are XOR-swizzled by
+// the row index so that the 64 lanes of a wave, one slot each, read distinct banks while
+// the ring stays unpadded (two workgroups fit a CU's LDS).
 constexpr int kRingMax = 128;
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void swa_decode_ring_kernel(const DecodeArgs p) {
-  constexpr int KRB = D * 2 + 16;                  // padded K row (bytes)
+__device__ __forceinline__ void swa_decode_ring_kernel_body(const DecodeArgs& p, const LayerIO& io, int kvh, int b) {
+  constexpr int KRB = D * 2;                       // K row (bytes)
   constexpr int CPR = D / 8;                       // 16-byte chunks per row
+  // byte offset of chunk ch of K row s
+  auto kpos = [](int s, int ch) { return s * KRB + ((ch ^ (s & (CPR - 1))) << 4); };
   constexpr int RIT = kRingMax * CPR / kThreads;   // chunks per thread per ring tensor
-  const int kvh = blockIdx.x, b = blockIdx.y;
   const int G = p.Hq / p.Hkv;
   const int W = p.window;
   const int pos = p.pos[b];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  bf16* out = (bf16*)p.out + ((size_t)b * p.Hq + kvh * G) * D;
+  bf16* out = (bf16*)io.out + ((size_t)b * p.Hq + kvh * G) * D;
   if (!pos_valid(pos, ZGATTN_POS_LIMIT)) {
     for (int i = t; i < G * D; i += kThreads) out[i] = (bf16)__builtin_nanf("");
     return;
   }
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  char* sK = smem;                                  // [W][KRB]
+  char* sK = smem;                                  // [W][KRB], swizzled chunks
   bf16* sV = (bf16*)(smem + kRingMax * KRB);        // [W][D]
   float* buf = (float*)(smem + kRingMax * KRB + kRingMax * D * 2);   // G q rows + k_new
   float* tmp = buf + (G + 1) * D;
   float* sv = tmp + (G + 1) * D;                    // v_new
   float* sS = sv + D;                               // [G][W]
-  bf16* kr = (bf16*)p.k_cache + ((size_t)b * p.Hkv + kvh) * W * D;
-  bf16* vr = (bf16*)p.v_cache + ((size_t)b * p.Hkv + kvh) * W * D;
+  bf16* kr = (bf16*)io.k_cache + ((size_t)b * p.Hkv + kvh) * W * D;
+  bf16* vr = (bf16*)io.v_cache + ((size_t)b * p.Hkv + kvh) * W * D;
   // ring -> registers (all loads in flight together), then the new token's rows
   const int nch = W * CPR;
   u32x4 kc[RIT], vc[RIT];
@@ -402,14 +434,14 @@ __global__ __launch_bounds__(kThreads) void swa_decode_ring_kernel(const DecodeA
       vc[it] = *(const u32x4*)(vr + (size_t)c * 8);
     }
   }
-  const bf16* q = (const bf16*)p.q + ((size_t)b * p.Hq + kvh * G) * D;
-  const bf16* kn = (const bf16*)p.k_new + ((size_t)b * p.Hkv + kvh) * D;
-  const bf16* vn = (const bf16*)p.v_new + ((size_t)b * p.Hkv + kvh) * D;
+  const bf16* q = (const bf16*)io.q + ((size_t)b * p.Hq + kvh * G) * D;
+  const bf16* kn = (const bf16*)io.k_new + ((size_t)b * p.Hkv + kvh) * D;
+  const bf16* vn = (const bf16*)io.v_new + ((size_t)b * p.Hkv + kvh) * D;
   for (int i = t; i < (G + 1) * D; i += kThreads)
     buf[i] = i < G * D ? (float)q[i] : (float)kn[i - G * D];
   for (int c = t; c < D; c += kThreads) sv[c] = (float)vn[c];
   const float* wrow[9];
-  for (int r = 0; r < 9; ++r) wrow[r] = r < G ? p.wq : p.wk;
+  for (int r = 0; r < 9; ++r) wrow[r] = r < G ? io.wq : io.wk;
   __syncthreads();
   norm_rope_rows_lds<D>(buf, wrow, G + 1, pos, p.rdim, p.eps, p.fr, tmp);
   const int slot = pos % W;
@@ -418,7 +450,7 @@ __global__ __launch_bounds__(kThreads) void swa_decode_ring_kernel(const DecodeA
     const int c = t + it * kThreads;
     if (c < nch) {
       const int row = c / CPR, ch = c % CPR;
-      *(u32x4*)(sK + row * KRB + ch * 16) = kc[it];
+      *(u32x4*)(sK + kpos(row, ch)) = kc[it];
       *(u32x4*)(sV + (size_t)c * 8) = vc[it];
     }
   }
@@ -427,7 +459,7 @@ __global__ __launch_bounds__(kThreads) void swa_decode_ring_kernel(const DecodeA
   for (int c = t; c < D; c += kThreads) {
     const bf16 kb = (bf16)buf[G * D + c];
     buf[G * D + c] = (float)kb;
-    ((bf16*)(sK + slot * KRB))[c] = kb;
+    *(bf16*)(sK + kpos(slot, c >> 3) + (c & 7) * 2) = kb;
     sV[slot * D + c] = (bf16)sv[c];
   }
   __syncthreads();
@@ -441,7 +473,7 @@ __global__ __launch_bounds__(kThreads) void swa_decode_ring_kernel(const DecodeA
       float a4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
       for (int ch = 0; ch < CPR; ++ch) {
-        const u32x4 raw = *(const u32x4*)(sK + s * KRB + ch * 16);
+        const u32x4 raw = *(const u32x4*)(sK + kpos(s, ch));
         const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -470,7 +502,7 @@ __global__ __launch_bounds__(kThreads) void swa_decode_ring_kernel(const DecodeA
   }
   __syncthreads();
   // P.V: two adjacent dims of one head per thread and pass
-  const bf16* g = (const bf16*)p.g + ((size_t)b * p.Hq + kvh * G) * D;
+  const bf16* g = (const bf16*)io.g + ((size_t)b * p.Hq + kvh * G) * D;
   const int ns = pos >= W - 1 ? W : pos + 1;
   for (int idx = t; idx < G * D / 2; idx += kThreads) {
     const int h = idx / (D / 2), c = 2 * (idx - h * (D / 2));
@@ -500,6 +532,15 @@ __global__ __launch_bounds__(kThreads) void swa_decode_ring_kernel(const DecodeA
     kr[(size_t)slot * D + c] = (bf16)buf[G * D + c];
     vr[(size_t)slot * D + c] = (bf16)sv[c];
   }
+}
+template <int D>
+__global__ __launch_bounds__(kThreads) void swa_decode_ring_kernel(const DecodeArgs p) {
+  swa_decode_ring_kernel_body<D>(p, layer_io(p), (int)blockIdx.x, (int)blockIdx.y);
+}
+template <int D>
+__global__ __launch_bounds__(kThreads) void swa_decode_ring_kernel_layers(const DecodeBatchArgs pb) {
+  const int layer = blockIdx.z;
+  swa_decode_ring_kernel_body<D>(pb.a, pb.io[layer], (int)blockIdx.x, (int)blockIdx.y);
 }
 
 template <typename K>
@@ -555,11 +596,76 @@ hipError_t launch_global_decode(const DecodeArgs& a, hipStream_t s) {
   return a.d == 128 ? global_decode_t<128>(a, s) : global_decode_t<64>(a, s);
 }
 
+template <typename K>
+hipError_t launch_layers(K kern, dim3 grid, dim3 block, int smem, hipStream_t s,
+                         const DecodeBatchArgs& pb) {
+  if (smem > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kern, grid, block, smem, s, pb);
+  return hipGetLastError();
+}
+
+hipError_t launch_swa_decode_layers(const DecodeArgs& a, const LayerIO* io, int n, hipStream_t s) {
+  if (a.window > kRingMax) return hipErrorInvalidValue;
+  const int G = a.Hq / a.Hkv;
+  const int smem = 2 * kRingMax * a.d * 2 +
+                   (2 * (G + 1) * a.d + a.d + G * a.window) * 4;
+  DecodeBatchArgs pb;
+  pb.a = a;
+  for (int l0 = 0; l0 < n; l0 += kMaxDecodeLayers) {
+    const int m = min(kMaxDecodeLayers, n - l0);
+    for (int i = 0; i < m; ++i) pb.io[i] = io[l0 + i];
+    const dim3 grid(a.Hkv, a.B, m);
+    hipError_t e = a.d == 128
+        ? launch_layers(swa_decode_ring_kernel_layers<128>, grid, dim3(kThreads), smem, s, pb)
+        : launch_layers(swa_decode_ring_kernel_layers<64>, grid, dim3(kThreads), smem, s, pb);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int D>
+hipError_t global_decode_layers_t(const DecodeArgs& a, const LayerIO* io, int n, hipStream_t s) {
+  const int G = a.Hq / a.Hkv;
+  constexpr int NKL = kThreads / (D / 8);
+  const int smem_split = max(a.chunk * G * 4, NKL * G * D * 4);
+  DecodeBatchArgs pb;
+  pb.a = a;
+  for (int l0 = 0; l0 < n; l0 += kMaxDecodeLayers) {
+    const int m = min(kMaxDecodeLayers, n - l0);
+    for (int i = 0; i < m; ++i) pb.io[i] = io[l0 + i];
+    hipError_t e = launch_layers(gdec_prep_kernel_layers<D>, dim3(a.Hkv, a.B, m), dim3(kThreads),
+                                 2 * (G + 1) * D * 4, s, pb);
+    if (e != hipSuccess) return e;
+    const dim3 g3(a.nsplit, a.Hkv, a.B * m);
+    switch (G) {
+      case 1: e = launch_layers(gdec_split_kernel_layers<D, 1>, g3, dim3(kThreads), smem_split, s, pb); break;
+      case 2: e = launch_layers(gdec_split_kernel_layers<D, 2>, g3, dim3(kThreads), smem_split, s, pb); break;
+      case 4: e = launch_layers(gdec_split_kernel_layers<D, 4>, g3, dim3(kThreads), smem_split, s, pb); break;
+      case 8: e = launch_layers(gdec_split_kernel_layers<D, 8>, g3, dim3(kThreads), smem_split, s, pb); break;
+      default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
+    e = launch_layers(gdec_combine_kernel_layers<D>, dim3(a.Hq, a.B, m), dim3(D), 0, s, pb);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_global_decode_layers(const DecodeArgs& a, const LayerIO* io, int n,
+                                       hipStream_t s) {
+  return a.d == 128 ? global_decode_layers_t<128>(a, io, n, s)
+                    : global_decode_layers_t<64>(a, io, n, s);
+}
+
 hipError_t launch_swa_decode(const DecodeArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   const int smem = (2 * (G + 1) * a.d + a.d + G * a.window) * 4;
   if (a.window <= kRingMax) {
-    const int ring = kRingMax * (a.d * 2 + 16) + kRingMax * a.d * 2;
+    const int ring = 2 * kRingMax * a.d * 2;
     if (a.d == 128)
       return launch_dyn(swa_decode_ring_kernel<128>, dim3(a.Hkv, a.B), dim3(kThreads),
                         ring + smem, s, a);

@@ -70,6 +70,34 @@ struct DecodeArgs {
   RopeFreq fr;
 };
 hipError_t launch_swa_decode(const DecodeArgs& a, hipStream_t s);
+
+// The tensors of one layer in a batched (several layers, one launch per kernel) decode
+// step; the scalar fields (shapes, positions, RoPE table) come from the DecodeArgs.
+struct LayerIO {
+  const void* q;
+  const void* k_new;
+  const void* v_new;
+  const void* g;
+  const float* wq;
+  const float* wk;
+  void* k_cache;
+  void* v_cache;
+  void* out;
+  float* ws;
+};
+constexpr int kMaxDecodeLayers = 32;   // layers per launch (kernel-argument table)
+struct DecodeBatchArgs {
+  DecodeArgs a;
+  LayerIO io[kMaxDecodeLayers];
+};
+static_assert(sizeof(DecodeBatchArgs) <= 4096, "kernel arguments");
+// One decode step of many layers: SWA layers (rings of a.window <= 128 slots) in one
+// launch per kMaxDecodeLayers, global layers (caches of a.S positions, split-K geometry
+// in a.nsplit / a.chunk, workspace per layer in io.ws) in three.
+hipError_t launch_swa_decode_layers(const DecodeArgs& a, const LayerIO* io, int n, hipStream_t s);
+hipError_t launch_global_decode_layers(const DecodeArgs& a, const LayerIO* io, int n,
+                                       hipStream_t s);
+constexpr int kSwaDecodeLayersMaxWindow = 128;
 hipError_t launch_global_decode(const DecodeArgs& a, hipStream_t s);
 // Split-K geometry and workspace bytes for a global decode call.
 void global_decode_geometry(int B, int Hq, int d, int capacity, int* nsplit, int* chunk,

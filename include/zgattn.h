@@ -139,6 +139,42 @@ int zgattn_global_decode(const zgattn_desc* desc, const void* q, const void* k_n
 size_t zgattn_global_decode_workspace_bytes(const zgattn_desc* desc, int32_t capacity);
 
 /*
+ * One decode step of a whole layer stack (explainer, section アーキテクチャ: 27 gated SWA
+ * layers with a fixed 128-token cache and 5 global layers with the full sequence; the
+ * jaehun.me review, section "KV 캐시가 6.4배 줄어드는 이유": 20 KiB of KV per token for the
+ * stack). Each layer is exactly zgattn_swa_decode or zgattn_global_decode on its own
+ * tensors; the layers are independent (post-projection inputs are given per layer), so
+ * the call runs all SWA layers in one launch and all global layers in three (per 32
+ * layers), instead of one to three launches per layer.
+ *   layers: host array [n_layers]; is_global: host int32 [n_layers] (0 = gated SWA).
+ *   Per layer: q, g, out [B, Hq, d]; k_new, v_new [B, Hkv, d]; wq, wk fp32 [d];
+ *   k_cache, v_cache: SWA ring [B, Hkv, window, d] (window <= 128 here) or global cache
+ *   [B, Hkv, capacity, d]. g is ignored (may be NULL) for global layers.
+ *   pos: device int32 [B], shared by every layer. workspace (device, >=
+ *   zgattn_model_decode_workspace_bytes(...) bytes) holds the global layers' partials.
+ * Shapes and parameters come from desc (one desc for the stack). Errors as for the
+ * single-layer calls; any invalid layer fails the whole call before anything launches.
+ */
+typedef struct {
+  const void* q;
+  const void* k_new;
+  const void* v_new;
+  const void* g;
+  const float* wq;
+  const float* wk;
+  void* k_cache;
+  void* v_cache;
+  void* out;
+} zgattn_decode_layer;
+
+int zgattn_model_decode(const zgattn_desc* desc, int32_t n_layers, const int32_t* is_global,
+                        const zgattn_decode_layer* layers, int32_t capacity,
+                        const int32_t* pos, void* workspace, size_t workspace_bytes,
+                        void* stream);
+size_t zgattn_model_decode_workspace_bytes(const zgattn_desc* desc, int32_t n_layers,
+                                           const int32_t* is_global, int32_t capacity);
+
+/*
  * Standalone QK-RMSNorm + partial RoPE (the q/k-branch transform of both layer kinds).
  *   x: [B, T, n_heads, d] contiguous (desc->dtype);  w: fp32 [d];
  *   pos: device int32 [B*T] absolute positions, or NULL for pos_offset + t;

@@ -18,7 +18,7 @@ FAKE = ctypes.c_void_p(4096)  # never dereferenced: every call below fails valid
 def test_exports_every_declared_symbol():
     lib = L.lib()
     declared = L.header_symbols()
-    assert len(declared) == 9
+    assert len(declared) == 11
     for name in declared:
         assert hasattr(lib, name), name
     assert set(declared) == set(L.SIGNATURES)
@@ -116,3 +116,37 @@ def test_qknorm_rope_checks():
     assert lib.zgattn_qknorm_rope(ctypes.byref(d), 0, FAKE, FAKE, None, FAKE, *ok_strides, None) == -1
     assert lib.zgattn_qknorm_rope(ctypes.byref(d), 4, FAKE, FAKE, None, FAKE, 16 * 128, 127, 128 * 16, None) == -1
     assert lib.zgattn_qknorm_rope(ctypes.byref(d), 4, None, FAKE, None, FAKE, *ok_strides, None) == -2
+
+
+def test_model_decode_checks():
+    lib = L.lib()
+    d = _d(batch=4, seq_len=1, n_q_heads=32, n_kv_heads=8)
+    cap = 4096
+    kinds = (ctypes.c_int32 * 3)(0, 1, 0)
+    lay = lambda **kw: L.DecodeLayer(*[kw.get(f, 4096) for f in (
+        "q", "k_new", "v_new", "g", "wq", "wk", "k_cache", "v_cache", "out")])
+    tab = (L.DecodeLayer * 3)(lay(), lay(), lay())
+    need = lib.zgattn_model_decode_workspace_bytes(ctypes.byref(d), 3, kinds, cap)
+    one = lib.zgattn_global_decode_workspace_bytes(ctypes.byref(d), cap)
+    assert need == ((one + 255) // 256) * 256        # one global layer
+    none = (ctypes.c_int32 * 2)(0, 0)
+    assert lib.zgattn_model_decode_workspace_bytes(ctypes.byref(d), 2, none, cap) == 0
+    call = lambda **kw: lib.zgattn_model_decode(
+        ctypes.byref(kw.get("d", d)), kw.get("n", 3), kw.get("kinds", kinds),
+        kw.get("tab", tab), kw.get("cap", cap), kw.get("pos", FAKE), kw.get("ws", FAKE),
+        kw.get("nb", need), None)
+    assert call(n=0, tab=None, kinds=None, pos=None) == 0    # nothing to do, nothing touched
+    assert lib.zgattn_model_decode(None, 3, kinds, tab, cap, FAKE, FAKE, need, None) == -2
+    assert call(tab=None) == -2
+    assert call(kinds=None) == -2
+    assert call(pos=None) == -2
+    assert call(n=-1) == -1
+    assert call(ws=None) == -5
+    assert call(nb=need - 1) == -5
+    assert call(cap=0) == -6
+    bad = (L.DecodeLayer * 3)(lay(), lay(), lay(g=None))       # an SWA layer without gate
+    assert call(tab=bad) == -2
+    bad = (L.DecodeLayer * 3)(lay(), lay(out=4100), lay())     # misaligned output
+    assert call(tab=bad) == -1
+    assert call(d=_d(batch=4, seq_len=1, n_q_heads=32, n_kv_heads=8, window=129)) == -4
+    assert call(d=_d(batch=4, seq_len=1, n_q_heads=32, n_kv_heads=8, dtype=L.F32)) == -4

@@ -160,10 +160,11 @@ def prefill_inputs(w: Workload, layer: int = 0, *, device: Optional[str] = None,
 
 
 def decode_inputs(w: Workload, *, device: Optional[str] = None, B: Optional[int] = None,
-                  S: Optional[int] = None, layer: int = 0):
+                  S: Optional[int] = None, layer: int = 0, kind: str = "both"):
     """Seeded decode-step inputs: q, g [B,Hq,d]; k_new, v_new [B,Hkv,d]; norm weights;
     global caches [B,Hkv,S,d]; SWA rings [B,Hkv,window,d]. Caches hold N(0,1) values that
-    stand for already-normalised/rotated K and raw V."""
+    stand for already-normalised/rotated K and raw V. ``kind`` "swa" skips the global
+    caches and "global" the rings (None in their place)."""
     import torch
     B = w.B if B is None else B
     S = w.T if S is None else S
@@ -175,15 +176,15 @@ def decode_inputs(w: Workload, *, device: Optional[str] = None, B: Optional[int]
                                                                   w.dtype, std)
         q, g = mk(qs, "q"), mk(qs, "g")
         kn, vn = mk(ns, "k_new"), mk(ns, "v_new")
-        kc, vc = mk(cs, "k", 1), mk(cs, "v", 1)
-        kr, vr = mk(rs, "k", 2), mk(rs, "v", 2)
+        kc, vc = (mk(cs, "k", 1), mk(cs, "v", 1)) if kind != "swa" else (None, None)
+        kr, vr = (mk(rs, "k", 2), mk(rs, "v", 2)) if kind != "global" else (None, None)
     else:
         mk = lambda shape, slot, lay=layer, big=False: device_tensor(
             shape, seed_for(c, lay, slot), w.dtype, device, chunk_dim0=big)
         q, g = mk(qs, "q"), mk(qs, "g")
         kn, vn = mk(ns, "k_new"), mk(ns, "v_new")
-        kc, vc = mk(cs, "k", 1, True), mk(cs, "v", 1, True)
-        kr, vr = mk(rs, "k", 2), mk(rs, "v", 2)
+        kc, vc = (mk(cs, "k", 1, True), mk(cs, "v", 1, True)) if kind != "swa" else (None, None)
+        kr, vr = (mk(rs, "k", 2), mk(rs, "v", 2)) if kind != "global" else (None, None)
     wq = torch.from_numpy(norm_weight(w.d, seed_for(c, layer, "wq")))
     wk = torch.from_numpy(norm_weight(w.d, seed_for(c, layer, "wk")))
     if device is not None:
