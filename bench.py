@@ -44,6 +44,9 @@ def parse():
                     help="decode step of the whole 32-layer hybrid stack (27 SWA rings + 5 "
                          "global caches, B=32 at context 262144): one batched call against "
                          "32 single-layer calls")
+    ap.add_argument("--varlen", action="store_true",
+                    help="packed-document prefill: 262144 tokens in 16 documents of 16K and "
+                         "in 24 documents of mixed length (one JSON line per packing)")
     ap.add_argument("--sweep", action="store_true",
                     help="attention-stack sweep: 32-layer hybrid / SWA 3:1 / full-attention "
                          "stacks at T = 4K .. 256K (one JSON line per T)")
@@ -110,6 +113,8 @@ def main():
         return run_sweep(args)
     if args.model_decode:
         return run_model_decode(args)
+    if args.varlen:
+        return run_varlen(args)
     T, B, Hq, Hkv, d, W = C4.T, C4.B, C4.Hq, C4.Hkv, C4.d, C4.window
     r = C4.rotary_dim
     # ---- inputs (seeded, generated on the device, outside the timed region) -----------
@@ -312,6 +317,71 @@ def run_model_decode(args):
                          * el * 2) / 2 ** 30,
     }
     print(json.dumps(rec), flush=True)
+
+
+def varlen_packings(T: int = 262144):
+    """Document lengths of the packed-prefill measurement: 16 equal documents, and 24
+    seeded lengths between 1K and 32K tokens rescaled to fill T."""
+    import numpy as np
+    rng = np.random.default_rng(4242)
+    raw = rng.integers(1024, 32768, 24).astype(np.float64)
+    lens = np.floor(raw / raw.sum() * T).astype(np.int64)
+    lens[-1] += T - lens.sum()
+    return {"16x16K": [T // 16] * 16, "24_mixed": [int(x) for x in lens]}
+
+
+def run_varlen(args):
+    """Packed-document prefill of 262,144 tokens (B=1, Hq=32, Hkv=8, d=128, rotary 42,
+    W=128): each document attends only within itself, so the global layer's causal work is
+    sum(len^2)/2 instead of T^2/2. HIP events around each call (median of the steps)."""
+    import numpy as np
+    import torch
+
+    import global_attention_qk_amd as zg
+    from workloads import C4, prefill_inputs
+
+    dev = "cuda"
+    r, W, T = C4.rotary_dim, C4.window, C4.T
+    q, k, v, g, wq, wk = prefill_inputs(C4, device=dev)
+    q, k, v, g = (x[0] for x in (q, k, v, g))        # packed [T, H, d]
+    out = torch.empty_like(q)
+    for name, lens in varlen_packings(T).items():
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32,
+                          device=dev)
+        mx = max(lens)
+        ws = torch.empty(zg.global_prefill_varlen_workspace_bytes(q, k, len(lens), rotary_dim=r),
+                         dtype=torch.uint8, device=dev)
+        calls = {
+            "swa": lambda: zg.swa_prefill_varlen(q, k, v, g, wq, wk, cu, mx, window=W,
+                                                 rotary_dim=r, out=out),
+            "global": lambda: zg.global_prefill_varlen(q, k, v, wq, wk, cu, mx, rotary_dim=r,
+                                                       workspace=ws, out=out),
+        }
+        ms = {}
+        for kind, fn in calls.items():
+            fn()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(max(args.steps, 1)):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            ms[kind] = sorted(ts)[len(ts) // 2]
+        pairs = sum(n * (n + 1) // 2 for n in lens)
+        flops = 4 * C4.d * pairs * C4.Hq
+        swa_bytes = T * C4.d * 2 * (3 * C4.Hq + 2 * C4.Hkv)
+        rec = {
+            "varlen": name, "T": T, "n_docs": len(lens), "max_len": mx,
+            "ms": {kd: round(x, 3) for kd, x in ms.items()},
+            "tokens_per_s": {kd: T / (x / 1e3) for kd, x in ms.items()},
+            "global_tflops": flops / (ms["global"] / 1e3) / 1e12,
+            "global_mfma_frac": flops / (ms["global"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+            "swa_hbm_frac": swa_bytes / (ms["swa"] / 1e3) / 1e9 / PEAK_HBM_GBS,
+        }
+        print(json.dumps(rec), flush=True)
 
 
 SWEEP_T = (4096, 8192, 16384, 32768, 65536, 131072, 262144)

@@ -9,6 +9,8 @@ from .api import (  # noqa: F401
     global_decode,
     global_decode_workspace_bytes,
     global_prefill,
+    global_prefill_varlen,
+    global_prefill_varlen_workspace_bytes,
     global_prefill_workspace_bytes,
     make_desc,
     model_decode,
@@ -17,5 +19,6 @@ from .api import (  # noqa: F401
     rotary_dim_for,
     swa_decode,
     swa_prefill,
+    swa_prefill_varlen,
 )
 from ._lib import ZgattnError, lib  # noqa: F401

@@ -61,6 +61,10 @@ SIGNATURES = {
     "zgattn_global_decode": (ctypes.c_int, [DP, P, P, P, P, P, P, P, I32, P, P, SZ, P, P]),
     "zgattn_global_decode_workspace_bytes": (SZ, [DP, I32]),
     "zgattn_qknorm_rope": (ctypes.c_int, [DP, I32, P, P, P, P, I64, I64, I64, P]),
+    "zgattn_swa_prefill_varlen": (ctypes.c_int, [DP, P, I32, I32, P, P, P, P, P, P, P, P]),
+    "zgattn_global_prefill_varlen": (ctypes.c_int, [DP, P, I32, I32, P, P, P, P, P, P, SZ, P,
+                                                    P]),
+    "zgattn_global_prefill_varlen_workspace_bytes": (SZ, [DP, I32]),
     "zgattn_model_decode": (ctypes.c_int, [DP, I32, ctypes.POINTER(I32),
                                            ctypes.POINTER(DecodeLayer), I32, P, P, SZ, P]),
     "zgattn_model_decode_workspace_bytes": (SZ, [DP, I32, ctypes.POINTER(I32), I32]),

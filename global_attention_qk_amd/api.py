@@ -102,6 +102,65 @@ def global_prefill(q, k, v, wq, wk, *, rotary_dim=None, pos_offset=0, rope_base=
     return out
 
 
+def _varlen_desc(q, k, window, rotary_dim, pos_offset, rope_base, eps, scale):
+    T, Hq, d = q.shape
+    return make_desc(batch=1, seq_len=T, n_q_heads=Hq, n_kv_heads=k.shape[1], head_dim=d,
+                     window=window, rotary_dim=rotary_dim, pos_offset=pos_offset,
+                     rope_base=rope_base, rms_eps=eps, softmax_scale=scale,
+                     dtype=_dtype_code(q))
+
+
+def _cu(cu_seqlens):
+    _dev(cu_seqlens)
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+        raise TypeError("cu_seqlens must be a 1-D int32 CUDA tensor")
+    return cu_seqlens.numel() - 1
+
+
+def swa_prefill_varlen(q, k, v, g, wq, wk, cu_seqlens, max_seqlen, *, window=128,
+                       rotary_dim=None, pos_offset=0, rope_base=10000.0, eps=1e-6, scale=0.0,
+                       out=None):
+    """Gated SWA over packed documents: q, g [T, Hq, d]; k, v [T, Hkv, d]; document i is
+    tokens cu_seqlens[i] .. cu_seqlens[i+1]-1 (int32 on the device)."""
+    _dev(q, k, v, g, wq, wk, out)
+    n_docs = _cu(cu_seqlens)
+    if out is None:
+        out = torch.empty_like(q)
+    d = _varlen_desc(q, k, window, rotary_dim, pos_offset, rope_base, eps, scale)
+    check(lib().zgattn_swa_prefill_varlen(ctypes.byref(d), _ptr(cu_seqlens), n_docs,
+                                          int(max_seqlen), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                          _ptr(wq), _ptr(wk), _ptr(out), _stream()),
+          "zgattn_swa_prefill_varlen")
+    return out
+
+
+def global_prefill_varlen_workspace_bytes(q, k, n_docs: int, rotary_dim=None) -> int:
+    d = _varlen_desc(q, k, 1, rotary_dim, 0, 10000.0, 1e-6, 0.0)
+    return int(lib().zgattn_global_prefill_varlen_workspace_bytes(ctypes.byref(d), n_docs))
+
+
+def global_prefill_varlen(q, k, v, wq, wk, cu_seqlens, max_seqlen, *, rotary_dim=None,
+                          pos_offset=0, rope_base=10000.0, eps=1e-6, scale=0.0,
+                          workspace="auto", out=None):
+    """Global causal layer over packed documents (see swa_prefill_varlen for the layout)."""
+    _dev(q, k, v, wq, wk, out)
+    n_docs = _cu(cu_seqlens)
+    if out is None:
+        out = torch.empty_like(q)
+    d = _varlen_desc(q, k, 1, rotary_dim, pos_offset, rope_base, eps, scale)
+    ws_bytes = int(lib().zgattn_global_prefill_varlen_workspace_bytes(ctypes.byref(d), n_docs))
+    if isinstance(workspace, str):
+        workspace = (torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+                     if ws_bytes > 0 else None)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(lib().zgattn_global_prefill_varlen(ctypes.byref(d), _ptr(cu_seqlens), n_docs,
+                                             int(max_seqlen), _ptr(q), _ptr(k), _ptr(v),
+                                             _ptr(wq), _ptr(wk), _ptr(workspace), nbytes,
+                                             _ptr(out), _stream()),
+          "zgattn_global_prefill_varlen")
+    return out
+
+
 def _decode_desc(q, k_new, window, rotary_dim, rope_base, eps, scale):
     B, Hq, dd = q.shape
     return make_desc(batch=B, seq_len=1, n_q_heads=Hq, n_kv_heads=k_new.shape[1],

@@ -270,6 +270,98 @@ size_t zgattn_model_decode_workspace_bytes(const zgattn_desc* d, int32_t n_layer
   return per ? n_glob * ((per + 255) & ~(size_t)255) : 0;
 }
 
+// Packed documents: B == 1, T = total tokens, cu [n_docs + 1] on the device.
+int varlen_common(const zgattn_desc* d, const int32_t* cu, int32_t n_docs, int32_t max_len,
+                  const void* q, const void* k, const void* v, const float* wq,
+                  const float* wk, void* out) {
+  int st = check_desc(d);
+  if (st) return st;
+  if (d->batch != 1 || d->seq_len < 0) return ZGATTN_EINVAL;
+  if (n_docs < 1 || n_docs > 65535 || max_len < 0 || max_len > d->seq_len) return ZGATTN_EINVAL;
+  if (max_len > 0 && (int64_t)d->pos_offset + max_len - 1 > ZGATTN_MAX_POSITION)
+    return ZGATTN_ERANGE;
+  if (d->seq_len == 0 || max_len == 0) return ZGATTN_OK;
+  if (!cu || !q || !k || !v || !wq || !wk || !out) return ZGATTN_ENULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ZGATTN_EINVAL;
+  if (d->dtype != ZGATTN_BF16) return ZGATTN_EUNSUPPORTED;
+  if (!prefill_bf16_supported(d->head_dim, d->n_q_heads / d->n_kv_heads, d->rotary_dim))
+    return ZGATTN_EUNSUPPORTED;
+  return ZGATTN_OK;
+}
+
+int zgattn_swa_prefill_varlen(const zgattn_desc* d, const int32_t* cu_seqlens, int32_t n_docs,
+                              int32_t max_seqlen, const void* q, const void* k, const void* v,
+                              const void* g, const float* wq, const float* wk, void* out,
+                              void* stream) {
+  int st = varlen_common(d, cu_seqlens, n_docs, max_seqlen, q, k, v, wq, wk, out);
+  if (st) return st;
+  if (d->window < 1) return ZGATTN_EINVAL;
+  if (d->seq_len == 0 || max_seqlen == 0) return ZGATTN_OK;
+  if (!g) return ZGATTN_ENULL;
+  if (!aligned16(g)) return ZGATTN_EINVAL;
+  PrefillArgs a = make_prefill(d, q, k, v, g, wq, wk, out, 1);
+  a.cu = cu_seqlens;
+  a.n_docs = n_docs;
+  a.max_len = max_seqlen;
+  return hip_status(launch_prefill_bf16(a, (hipStream_t)stream));
+}
+
+size_t zgattn_global_prefill_varlen_workspace_bytes(const zgattn_desc* d, int32_t n_docs) {
+  if (check_desc(d) || d->seq_len < 0 || d->batch != 1 || n_docs < 1) return 0;
+  if (d->dtype != ZGATTN_BF16) return 0;
+  const size_t kbytes = (size_t)d->n_kv_heads * (size_t)d->seq_len * d->head_dim * 2;
+  return ((kbytes + 255) & ~(size_t)255) +
+         prefill_vtiles_bytes_varlen(d->n_kv_heads, d->seq_len, n_docs, d->head_dim);
+}
+
+int zgattn_global_prefill_varlen(const zgattn_desc* d, const int32_t* cu_seqlens,
+                                 int32_t n_docs, int32_t max_seqlen, const void* q,
+                                 const void* k, const void* v, const float* wq,
+                                 const float* wk, void* workspace, size_t workspace_bytes,
+                                 void* out, void* stream) {
+  int st = varlen_common(d, cu_seqlens, n_docs, max_seqlen, q, k, v, wq, wk, out);
+  if (st) return st;
+  if (d->seq_len == 0 || max_seqlen == 0) return ZGATTN_OK;
+  PrefillArgs a = make_prefill(d, q, k, v, nullptr, wq, wk, out, 0);
+  a.cu = cu_seqlens;
+  a.n_docs = n_docs;
+  a.max_len = max_seqlen;
+  hipStream_t s = (hipStream_t)stream;
+  if (workspace) {
+    if (workspace_bytes < zgattn_global_prefill_varlen_workspace_bytes(d, n_docs) ||
+        !aligned16(workspace))
+      return ZGATTN_EWORKSPACE;
+    NormRopeArgs n;
+    n.x = k;
+    n.w = wk;
+    n.pos = nullptr;
+    n.y = workspace;
+    n.B = 1;
+    n.T = a.T;
+    n.H = a.Hkv;
+    n.d = a.d;
+    n.ysb = 0;
+    n.yst = a.d;                          // [Hkv][T][d]
+    n.ysh = (int64_t)a.T * a.d;
+    n.rdim = a.rdim;
+    n.pos_offset = a.pos_offset;
+    n.is_bf16 = 1;
+    n.eps = a.eps;
+    n.out_scale = 1.0f;
+    n.fr = a.fr;
+    n.cu = cu_seqlens;
+    n.n_docs = n_docs;
+    hipError_t e = launch_qknorm_rope(n, s);
+    if (e != hipSuccess) return ZGATTN_EHIP;
+    a.kt = (bf16*)workspace;
+    const size_t kbytes = (size_t)a.Hkv * (size_t)a.T * a.d * 2;
+    a.vt = (bf16*)((char*)workspace + ((kbytes + 255) & ~(size_t)255));
+    e = launch_v_tiles(a, s);
+    if (e != hipSuccess) return ZGATTN_EHIP;
+  }
+  return hip_status(launch_prefill_bf16(a, s));
+}
+
 int zgattn_model_decode(const zgattn_desc* d, int32_t n_layers, const int32_t* is_global,
                         const zgattn_decode_layer* layers, int32_t capacity,
                         const int32_t* pos, void* workspace, size_t workspace_bytes,

@@ -54,6 +54,30 @@ __device__ __forceinline__ float sigmoidf_(float x) {
   return __builtin_amdgcn_rcpf(1.0f + __expf(-x));
 }
 
+// Packed documents (variable-length prefill): document d covers packed positions
+// [cu[d], cu[d+1]). The bounds are clamped into [0, total] and the length to max_len, so a
+// malformed table cannot send an access outside the packed tensors.
+__device__ __forceinline__ void doc_range(const int32_t* cu, int d, int total, int max_len,
+                                          int& start, int& len) {
+  const int s0 = min(max(cu[d], 0), total);
+  const int s1 = min(max(cu[d + 1], s0), total);
+  start = s0;
+  len = min(s1 - s0, max_len);
+}
+// Document holding packed position t: the largest d < n_docs with cu[d] <= t.
+__device__ __forceinline__ int doc_of(const int32_t* cu, int n_docs, int t) {
+  int lo = 0, hi = n_docs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+// First V-tile slot of document d in the per-KV-head tile array of a packed batch: the
+// slots of document d are [cu[d] / 64 + d, + ceil(len / 64)), which never overlap the next
+// document's, and all fit in total / 64 + n_docs slots.
+__device__ __forceinline__ int doc_tile_base(int start, int d) { return (start >> 6) + d; }
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

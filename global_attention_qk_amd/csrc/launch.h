@@ -25,7 +25,15 @@ struct PrefillArgs {
   float eps;
   float scale;        // softmax scale (natural-log units)
   RopeFreq fr;
+  // Packed documents (B == 1, T = total tokens): cu [n_docs + 1] on the device, each
+  // document an independent sequence of at most max_len tokens; nullptr for dense batches.
+  const int32_t* cu = nullptr;
+  int n_docs = 0;
+  int max_len = 0;
 };
+// V-tile slots per KV head of a packed batch (see doc_tile_base).
+inline int varlen_vtile_slots(int T, int n_docs) { return T / 64 + n_docs; }
+size_t prefill_vtiles_bytes_varlen(int Hkv, int T, int n_docs, int d);
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
@@ -49,6 +57,8 @@ struct NormRopeArgs {
   float eps;
   float out_scale;        // multiplies the result (1 for the public entry point)
   RopeFreq fr;
+  const int32_t* cu = nullptr;   // packed documents (B == 1): positions restart per document
+  int n_docs = 0;
 };
 hipError_t launch_qknorm_rope(const NormRopeArgs& a, hipStream_t s);
 

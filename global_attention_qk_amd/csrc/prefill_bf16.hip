@@ -102,6 +102,10 @@ struct KArgs {
   int group, bmp, n_qtiles, n_hb;
   float eps, qscale;
   RopeFreq fr;
+  // packed documents (B == 1, T = total tokens): cu [n_docs + 1], n_hb = n_docs * Hkv,
+  // n_qtiles sized by max_len; nullptr for dense batches
+  const int32_t* cu;
+  int max_len, vt_slots;
 };
 
 // Swap bits 2 and 3 of a key index within its 16-key group: keys {0-3, 8-11} then
@@ -267,11 +271,26 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
   const int lin = blockIdx.x;
   const int hb = lin % p.n_hb;
   const int tile_rank = lin / p.n_hb;
-  const int qt = SWA ? tile_rank : (p.n_qtiles - 1 - tile_rank);
-  const int b = hb / p.Hkv;
+  const int b = hb / p.Hkv;        // batch element, or document of a packed batch
   const int kvh = hb % p.Hkv;
+  // Sequence of this workgroup: `seq0` is its first row in the [B*T] (or packed) token
+  // order, T its length; K~ rows and V tiles start at kt_row0 / vt_tile0 of the workspace.
+  int T = p.T, n_qtiles = p.n_qtiles;
+  size_t seq0 = (size_t)b * p.T;
+  size_t kt_row0 = ((size_t)b * p.Hkv + kvh) * p.T;
+  size_t vt_tile0 = ((size_t)b * p.Hkv + kvh) * ((p.T + kBN - 1) / kBN);
+  if (p.cu) {
+    int start, len;
+    doc_range(p.cu, b, p.T, p.max_len, start, len);
+    T = len;
+    n_qtiles = (len + p.bmp - 1) / p.bmp;
+    if (tile_rank >= n_qtiles) return;   // the whole workgroup, before any later barrier
+    seq0 = start;
+    kt_row0 = (size_t)kvh * p.T + start;
+    vt_tile0 = (size_t)kvh * p.vt_slots + doc_tile_base(start, b);
+  }
+  const int qt = SWA ? tile_rank : (n_qtiles - 1 - tile_rank);
   const int i0 = qt * p.bmp;
-  const int T = p.T;
   const int half = p.rdim >> 1;
   const int bpp = p.bmp >> 5;  // 32-row blocks per head in the tile
 
@@ -280,7 +299,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
     const int g = p.group;
     const int chunks_per_pos = g * DC;
     const int n_chunks = p.bmp * chunks_per_pos;
-    const bf16* qbase = p.q + ((size_t)b * T * p.Hq + (size_t)kvh * g) * D;
+    const bf16* qbase = p.q + (seq0 * p.Hq + (size_t)kvh * g) * D;
     for (int c = tid; c < n_chunks; c += kThreads) {
       const int pi = c / chunks_per_pos;
       const int rem = c - pi * chunks_per_pos;
@@ -381,11 +400,10 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
     l_run[qb] = 0.f;
   }
 
-  const bf16* kbase = p.k + ((size_t)b * T * p.Hkv + kvh) * D;
-  const bf16* vbase = p.v + ((size_t)b * T * p.Hkv + kvh) * D;
-  const bf16* ktsrc = KPRE ? p.kt + (((size_t)b * p.Hkv + kvh) * T) * D : nullptr;
-  const int n_kt = (T + kBN - 1) / kBN;
-  const bf16* vtsrc = KPRE ? p.vt + ((size_t)b * p.Hkv + kvh) * n_kt * (size_t)(kBN * D) : nullptr;
+  const bf16* kbase = p.k + (seq0 * p.Hkv + kvh) * D;
+  const bf16* vbase = p.v + (seq0 * p.Hkv + kvh) * D;
+  const bf16* ktsrc = KPRE ? p.kt + kt_row0 * D : nullptr;
+  const bf16* vtsrc = KPRE ? p.vt + vt_tile0 * (size_t)(kBN * D) : nullptr;
   const size_t kvstride = (size_t)p.Hkv * D;
 
   // Global -> registers for tile kt (issued one tile ahead of its use). Rows past the
@@ -857,7 +875,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
     const float inv = 1.0f / lt;
     const int hg = (wave * QB + qb) / bpp;
     const int h = kvh * p.group + hg;
-    const size_t rowoff = (((size_t)b * T + pos) * p.Hq + h) * D;
+    const size_t rowoff = ((seq0 + pos) * p.Hq + h) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -903,22 +921,37 @@ hipError_t launch_t(const KArgs& ka, int n_blocks, hipStream_t s) {
 // V tile transpose for the global path: V [B, T, Hkv, D] -> vt [B, Hkv, ceil(T/64), D, 64]
 // with the 64 keys of each row in the slot order of the LDS V^T tile (keys past T are 0).
 // The attention kernel then stages V^T tiles with plain 16-byte copies.
+// Packed documents (cu != nullptr, B == 1): blockIdx.z is the document, its tiles start at
+// its own first token and go to slots doc_tile_base(start, doc) .. of each KV head's
+// vt_slots.
 template <int D>
 __global__ __launch_bounds__(256) void v_tiles_kernel(const bf16* v, bf16* vt, int T, int Hkv,
-                                                      int n_kt) {
+                                                      int n_kt, const int32_t* cu, int max_len,
+                                                      int vt_slots) {
   __shared__ __attribute__((aligned(16))) bf16 s[kBN][D + 8];
   const int tile = blockIdx.x, hb = blockIdx.y;
   const int b = hb / Hkv, kvh = hb % Hkv;
   const int tid = threadIdx.x;
+  size_t seq0 = (size_t)b * T;
+  int len = T;
+  size_t out_tile = (size_t)hb * n_kt + tile;
+  if (cu) {
+    const int doc = blockIdx.z;
+    int start;
+    doc_range(cu, doc, T, max_len, start, len);
+    if (tile * kBN >= len) return;
+    seq0 = start;
+    out_tile = (size_t)kvh * vt_slots + doc_tile_base(start, doc) + tile;
+  }
   for (int c = tid; c < kBN * (D / 8); c += 256) {
     const int kr = c / (D / 8), dc = c % (D / 8);
     const int pos = tile * kBN + kr;
     u32x4 val = {0u, 0u, 0u, 0u};
-    if (pos < T) val = *(const u32x4*)(v + (((size_t)b * T + pos) * Hkv + kvh) * D + dc * 8);
+    if (pos < len) val = *(const u32x4*)(v + ((seq0 + pos) * Hkv + kvh) * D + dc * 8);
     *(u32x4*)&s[kr][dc * 8] = val;
   }
   __syncthreads();
-  bf16* out = vt + ((size_t)hb * n_kt + tile) * (kBN * D);
+  bf16* out = vt + out_tile * (kBN * D);
   for (int c = tid; c < D * (kBN / 8); c += 256) {
     const int d = c / (kBN / 8), sc = c % (kBN / 8);
     bf16x8 o;
@@ -961,6 +994,13 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
   ka.eps = a.eps;
   ka.qscale = a.scale * 1.4426950408889634f;
   ka.fr = a.fr;
+  ka.cu = a.cu;
+  ka.max_len = a.max_len;
+  ka.vt_slots = a.cu ? varlen_vtile_slots(a.T, a.n_docs) : 0;
+  if (a.cu) {   // one (document, KV head) per sequence slot, tiles sized by the longest
+    ka.n_hb = a.n_docs * a.Hkv;
+    ka.n_qtiles = (a.max_len + ka.bmp - 1) / ka.bmp;
+  }
   const int n_blocks = ka.n_qtiles * ka.n_hb;
   if (n_blocks == 0) return hipSuccess;
   if (swa_stream_supported(a)) return launch_swa_stream(a, s);
@@ -983,16 +1023,22 @@ size_t prefill_vtiles_bytes(int B, int Hkv, int T, int d) {
   return (size_t)B * Hkv * ((T + kBN - 1) / kBN) * kBN * d * 2;
 }
 
+size_t prefill_vtiles_bytes_varlen(int Hkv, int T, int n_docs, int d) {
+  return (size_t)Hkv * varlen_vtile_slots(T, n_docs) * kBN * d * 2;
+}
+
 hipError_t launch_v_tiles(const PrefillArgs& a, hipStream_t s) {
-  const int n_kt = (a.T + kBN - 1) / kBN;
-  const dim3 grid(n_kt, a.B * a.Hkv);
+  const bool packed = a.cu != nullptr;
+  const int n_kt = ((packed ? a.max_len : a.T) + kBN - 1) / kBN;
+  const dim3 grid(n_kt, a.B * a.Hkv, packed ? a.n_docs : 1);
+  const int slots = packed ? varlen_vtile_slots(a.T, a.n_docs) : 0;
   if (n_kt == 0) return hipSuccess;
   if (a.d == 128)
     hipLaunchKernelGGL(v_tiles_kernel<128>, grid, dim3(256), 0, s, (const bf16*)a.v, a.vt, a.T,
-                       a.Hkv, n_kt);
+                       a.Hkv, n_kt, a.cu, a.max_len, slots);
   else
     hipLaunchKernelGGL(v_tiles_kernel<64>, grid, dim3(256), 0, s, (const bf16*)a.v, a.vt, a.T,
-                       a.Hkv, n_kt);
+                       a.Hkv, n_kt, a.cu, a.max_len, slots);
   return hipGetLastError();
 }
 

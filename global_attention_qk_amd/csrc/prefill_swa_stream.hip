@@ -80,6 +80,8 @@ struct SArgs {
   int n_hb, seg_steps, n_steps;
   float eps, qscale;
   RopeFreq fr;
+  const int32_t* cu;   // packed documents (B == 1, T = total tokens), or nullptr
+  int max_len;
 };
 
 __device__ __forceinline__ int ring_slot(int kb) { return (kb + 4 * kRing) % kRing; }  // kb >= -24
@@ -191,24 +193,32 @@ __global__ __launch_bounds__(kThreads, 1) void swa_stream_kernel(const SArgs p) 
   const int lin = blockIdx.x;
   const int hb = lin % p.n_hb;
   const int seg = lin / p.n_hb;
-  const int b = hb / p.Hkv;
+  const int b = hb / p.Hkv;        // batch element, or document of a packed batch
   const int kvh = hb % p.Hkv;
+  int T = p.T, n_steps = p.n_steps;
+  size_t seq0 = (size_t)b * p.T;   // first token of the sequence in token order
+  if (p.cu) {
+    int start, len;
+    doc_range(p.cu, b, p.T, p.max_len, start, len);
+    T = len;
+    n_steps = (len + kStep - 1) / kStep;
+    seq0 = start;
+  }
   const int s_begin = seg * p.seg_steps;
-  const int s_end = min(s_begin + p.seg_steps, p.n_steps);
+  const int s_end = min(s_begin + p.seg_steps, n_steps);
   if (s_begin >= s_end) return;
-  const int T = p.T;
   const int W = p.window;
   const int h = kvh * kG + hg;
   // Wave-uniform bases with 32-bit per-lane byte offsets (one sequence of one tensor is
   // below 4 GiB, checked on the host).
   const uint32_t qrow_b = (uint32_t)p.Hq * kD * 2;    // bytes between positions in Q/G/O
   const uint32_t kvrow_b = (uint32_t)p.Hkv * kD * 2;  // bytes between positions in K/V
-  const size_t qoff = ((size_t)b * T * p.Hq + h) * kD;
+  const size_t qoff = (seq0 * p.Hq + h) * kD;
   const char* qbase = (const char*)(p.q + qoff);
   const char* gbase = (const char*)(p.g + qoff);
   char* obase = (char*)(p.out + qoff);
-  const char* kbase = (const char*)(p.k + ((size_t)b * T * p.Hkv + kvh) * kD);
-  const char* vbase = (const char*)(p.v + ((size_t)b * T * p.Hkv + kvh) * kD);
+  const char* kbase = (const char*)(p.k + (seq0 * p.Hkv + kvh) * kD);
+  const char* vbase = (const char*)(p.v + (seq0 * p.Hkv + kvh) * kD);
 
   // ---- loads -----------------------------------------------------------------------
   // Q (or G) row of this lane's query at step s: dims 32 grp .. + 31, as four chunks.
@@ -598,7 +608,7 @@ hipError_t set_smem() {
 
 bool swa_stream_supported(const PrefillArgs& a) {
   // per-lane offsets are 32-bit byte offsets within one sequence of Q / G / O
-  const bool fits = (size_t)a.T * a.Hq * kD * 2 <= (size_t)UINT32_MAX;
+  const bool fits = (size_t)(a.cu ? a.max_len : a.T) * a.Hq * kD * 2 <= (size_t)UINT32_MAX;
   return a.swa && a.d == kD && a.Hq == kG * a.Hkv && a.rdim == 2 * kRH && a.window >= 1 &&
          a.window <= kMaxWindow && fits;
 }
@@ -620,8 +630,10 @@ hipError_t launch_swa_stream(const PrefillArgs& a, hipStream_t s) {
   ka.eps = a.eps;
   ka.qscale = a.scale * 1.4426950408889634f;
   ka.fr = a.fr;
-  ka.n_hb = a.B * a.Hkv;
-  ka.n_steps = (a.T + kStep - 1) / kStep;
+  ka.cu = a.cu;
+  ka.max_len = a.max_len;
+  ka.n_hb = (a.cu ? a.n_docs : a.B) * a.Hkv;
+  ka.n_steps = ((a.cu ? a.max_len : a.T) + kStep - 1) / kStep;
   if (ka.n_steps == 0 || ka.n_hb == 0) return hipSuccess;
   // One resident workgroup per CU (the LDS ring takes most of a CU): split every
   // (batch, KV head) stream into segments so that the grid covers the CUs once.
@@ -634,6 +646,13 @@ hipError_t launch_swa_stream(const PrefillArgs& a, hipStream_t s) {
   // (and its serial load latency) small against the segment's work.
   const int n_seg_target = max(1, (cus + ka.n_hb - 1) / ka.n_hb);
   ka.seg_steps = max(kMinSegSteps, (ka.n_steps + n_seg_target - 1) / n_seg_target);
+  if (a.cu) {
+    // Packed documents differ in length: segments sized from the total work (about two
+    // per CU) rather than from the longest document keep the CUs evenly loaded; the
+    // segments past a short document's end exit at once.
+    const int64_t units = ((int64_t)a.T / kStep + a.n_docs) * a.Hkv;
+    ka.seg_steps = max(kMinSegSteps, (int)((units + 2 * cus - 1) / (2 * cus)));
+  }
   const int n_seg = (ka.n_steps + ka.seg_steps - 1) / ka.seg_steps;
   const int n_blocks = ka.n_hb * n_seg;
   e = set_smem<true>();

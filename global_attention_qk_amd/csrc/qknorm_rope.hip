@@ -51,7 +51,10 @@ __global__ __launch_bounds__(kRowsPerBlock) void qknorm_rope_kernel(const NormRo
     float* x = rows + t * RS;
     if (row < n_rows) {
       const int64_t bt = row / p.H;  // b * T + t
-      const int pos = p.pos ? p.pos[bt] : p.pos_offset + (int)(bt % p.T);
+      const int tt = (int)(bt % p.T);
+      const int pos = p.pos ? p.pos[bt]
+                    : p.cu ? p.pos_offset + tt - p.cu[doc_of(p.cu, p.n_docs, tt)]
+                           : p.pos_offset + tt;
       float ss = 0.f;
 #pragma unroll 8
       for (int c = 0; c < D; ++c) ss = __builtin_fmaf(x[c], x[c], ss);

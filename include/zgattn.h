@@ -106,6 +106,34 @@ int zgattn_global_prefill(const zgattn_desc* desc, const void* q, const void* k,
 size_t zgattn_global_prefill_workspace_bytes(const zgattn_desc* desc);
 
 /*
+ * Packed variable-length prefill (the 256K fine-tuning variant trains on packed tokens:
+ * "ZGCM-1-7B 完全解説" explainer, section 事後訓練 — SFTと混合RL、think/no-thinkの共存;
+ * that documents do not attend across their boundaries and restart their positions is this
+ * library's reading, the pages do not say). The batch is
+ * one packed sequence of desc->seq_len tokens: q, g, out [seq_len, Hq, d]; k, v
+ * [seq_len, Hkv, d] (desc->batch must be 1). cu_seqlens: DEVICE int32 [n_docs + 1],
+ * non-decreasing, cu_seqlens[0] = 0 and cu_seqlens[n_docs] = seq_len; document i is
+ * tokens [cu_seqlens[i], cu_seqlens[i+1]) and is attended as an independent sequence:
+ * keys of other documents are never visible, and positions restart at pos_offset at each
+ * document's first token (RoPE). max_seqlen (host) bounds every document's length and sizes
+ * the grid. The table lives on the device and is not validated on the host: out-of-range
+ * entries are clamped (no access leaves the tensors) and give unspecified outputs.
+ * bf16 only, on the MFMA paths (ZGATTN_EUNSUPPORTED otherwise). The global form takes the
+ * same optional workspace as zgattn_global_prefill, sized by
+ * zgattn_global_prefill_varlen_workspace_bytes(desc, n_docs).
+ */
+int zgattn_swa_prefill_varlen(const zgattn_desc* desc, const int32_t* cu_seqlens,
+                              int32_t n_docs, int32_t max_seqlen, const void* q,
+                              const void* k, const void* v, const void* g, const float* wq,
+                              const float* wk, void* out, void* stream);
+int zgattn_global_prefill_varlen(const zgattn_desc* desc, const int32_t* cu_seqlens,
+                                 int32_t n_docs, int32_t max_seqlen, const void* q,
+                                 const void* k, const void* v, const float* wq,
+                                 const float* wk, void* workspace, size_t workspace_bytes,
+                                 void* out, void* stream);
+size_t zgattn_global_prefill_varlen_workspace_bytes(const zgattn_desc* desc, int32_t n_docs);
+
+/*
  * Gated SWA decode: one new token per sequence against a ring of `window` entries
  * (explainer, section アーキテクチャ: the SWA layers keep only a fixed 128 tokens).
  *   q, g, out: [B, Hq, d];  k_new, v_new: [B, Hkv, d] (raw, before norm/RoPE);

@@ -28,6 +28,13 @@ What each function follows, and how it is pinned (tests in ``tests/test_oracle_*
   section アーキテクチャ). Pinned: the worked gate example, pure-Python brute force,
   torch SDPA in fp64 for rotary_dim 0, gate limits, SWA(W >= T) == global, V == c.
   The softmax scale 1/sqrt(d) is the textbook reading (*parity unpinned* by the pages).
+* ``prefill_varlen`` -- packed documents, each its own sequence (explainer, section 事後訓練:
+  the 256K fine-tuning variant trains on packed tokens). Pinned: equal-length documents ==
+  the batched layer, one-hot brute force of the document boundary, independence from the
+  other documents' contents. No attention across documents is a reading (*parity
+  unpinned* by the pages); restarting positions per document is one too, but with the
+  masking in place it cannot change the outputs (RoPE attention depends on position
+  differences only, pinned by the relative-position pin), only the rounding of angles.
 * ``decode_global`` / ``decode_swa`` -- one new token against a full cache or a 128-entry
   ring (explainer, section アーキテクチャ: SWA layers keep a fixed 128 tokens, global layers
   the whole sequence). Pinned: decode at step t == prefill row t, ring-rotation invariance,
@@ -206,6 +213,37 @@ def _decode_one(q, k_new, v_new, wq, wk, k_cache, v_cache, pos, slots, *, rotary
             p = np.exp(s - s.max())
             out[h] = (p / p.sum()) @ vs
     return out, kt
+
+
+def prefill_varlen(q, k, v, g, wq, wk, cu_seqlens, *, rows=None, window=None,
+                   rotary_dim=None, rope_base=10000.0, eps=1e-6, scale=None, pos_offset=0,
+                   threads=1):
+    """Packed documents: q, g [T, Hq, d]; k, v [T, Hkv, d]; cu_seqlens [n_docs + 1].
+
+    Document i (tokens cu[i] .. cu[i+1]-1) is its own sequence: the layer of ``prefill``
+    with positions pos_offset, pos_offset + 1, .. from its first token, and no key of
+    another document visible (the pages say only that the 256K fine-tuning trains on
+    packed tokens, explainer section 事後訓練; blocking attention across documents and
+    restarting positions are the reading adopted). Returns float64 [len(rows), Hq, d] for
+    the packed rows ``rows`` (all rows when None).
+    """
+    q, k, v = np.asarray(q), np.asarray(k), np.asarray(v)
+    T = q.shape[0]
+    cu = [int(x) for x in cu_seqlens]
+    rows = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.zeros((len(rows), q.shape[1], q.shape[2]), dtype=F64)
+    for i in range(len(cu) - 1):
+        s0, s1 = cu[i], cu[i + 1]
+        sel = np.nonzero((rows >= s0) & (rows < s1))[0]
+        if len(sel) == 0:
+            continue
+        local = rows[sel] - s0
+        gd = None if g is None else np.asarray(g)[None, s0:s1]
+        out[sel] = prefill_rows(q[None, s0:s1], k[None, s0:s1], v[None, s0:s1], gd, wq, wk,
+                                local, window=window, rotary_dim=rotary_dim,
+                                rope_base=rope_base, eps=eps, scale=scale,
+                                pos_offset=pos_offset, threads=threads)[0]
+    return out
 
 
 def decode_global(q, k_new, v_new, wq, wk, k_cache, v_cache, pos, *, rotary_dim=None,

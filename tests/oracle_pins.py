@@ -287,3 +287,68 @@ def pin_decode_is_prefill_row():
         out2, _ = O.decode_swa(q[:, t], k[:, t], v[:, t], g[:, t], wq, wk, kr, vr, pos,
                                window=W, rotary_dim=r)
         assert np.allclose(out2, pre_s[:, t], atol=1e-12), t
+
+
+def pin_varlen_brute_force():
+    """Packed documents == the independent pure-Python layer run on each document alone
+    (positions restarting at pos_offset), for every packed row; documents of length 1,
+    shorter and longer than the window."""
+    lens = [1, 5, 9, 2, 7]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T, Hq, Hkv, d, r = int(cu[-1]), 4, 2, 8, 4
+    q, k, v = _rand((T, Hq, d), 71), _rand((T, Hkv, d), 72), _rand((T, Hkv, d), 73)
+    g = _rand((T, Hq, d), 74)
+    wq, wk = 1 + 0.1 * _rand((d,), 75), 1 + 0.1 * _rand((d,), 76)
+    for W, gg, po in ((None, None, 0), (3, g, 2)):
+        got = O.prefill_varlen(q, k, v, gg, wq, wk, cu, window=W, rotary_dim=r, pos_offset=po)
+        for i in range(len(lens)):
+            s0, s1 = int(cu[i]), int(cu[i + 1])
+            want = brute_prefill(q[None, s0:s1], k[None, s0:s1], v[None, s0:s1],
+                                 None if gg is None else gg[None, s0:s1], wq, wk, W, r,
+                                 pos_offset=po)[0]
+            assert np.allclose(got[s0:s1], want, rtol=0, atol=1e-12), (W, i)
+    # a subset of rows in scrambled order gives the same rows
+    rows = np.array([17, 0, 6, 23, 5, 15])
+    sub = O.prefill_varlen(q, k, v, g, wq, wk, cu, rows=rows, window=3, rotary_dim=r)
+    full = O.prefill_varlen(q, k, v, g, wq, wk, cu, window=3, rotary_dim=r)
+    assert np.allclose(sub, full[rows], rtol=0, atol=1e-13)
+
+
+def pin_varlen_equal_documents_are_a_batch():
+    """n equal-length packed documents == the batched layer with B = n."""
+    n, L, Hq, Hkv, d, r = 3, 11, 4, 1, 8, 4
+    q, k, v = _rand((n, L, Hq, d), 81), _rand((n, L, Hkv, d), 82), _rand((n, L, Hkv, d), 83)
+    wq, wk = 1 + 0.1 * _rand((d,), 84), 1 + 0.1 * _rand((d,), 85)
+    cu = np.arange(n + 1) * L
+    got = O.prefill_varlen(q.reshape(n * L, Hq, d), k.reshape(n * L, Hkv, d),
+                           v.reshape(n * L, Hkv, d), None, wq, wk, cu, rotary_dim=r)
+    want = O.prefill(q, k, v, None, wq, wk, rotary_dim=r).reshape(n * L, Hq, d)
+    assert np.allclose(got, want, rtol=0, atol=1e-13)
+
+
+def pin_varlen_isolation():
+    """No key of another document contributes: one-hot V per packed token puts weight only
+    on the row's own document (exactly min(i - start + 1, W) nonzero weights), and
+    changing the other documents' tokens leaves a document's rows unchanged."""
+    lens = [4, 6, 3]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T, d = int(cu[-1]), 16
+    q, k = _rand((T, 1, d), 91), _rand((T, 1, d), 92)
+    v = np.zeros((T, 1, d))
+    v[np.arange(T), 0, np.arange(T)] = 1.0           # token t carries unit vector e_t
+    w = np.ones(d)
+    for W in (None, 2):
+        out = O.prefill_varlen(q, k, v, None, w, w, cu, window=W, rotary_dim=4)[:, 0]
+        for i in range(len(lens)):
+            s0, s1 = int(cu[i]), int(cu[i + 1])
+            for t in range(s0, s1):
+                nz = np.nonzero(out[t, :T] > 0)[0]
+                lo = s0 if W is None else max(s0, t - W + 1)
+                assert list(nz) == list(range(lo, t + 1)), (W, t, nz)
+    k2, v2 = k.copy(), v.copy()
+    k2[:4] = _rand((4, 1, d), 93)
+    v2[4:] *= 1.0
+    v2[:4] = _rand((4, 1, d), 94)
+    a = O.prefill_varlen(q, k, v, None, w, w, cu, rotary_dim=4)
+    b = O.prefill_varlen(q, k2, v2, None, w, w, cu, rotary_dim=4)
+    assert np.array_equal(a[4:], b[4:]) and not np.array_equal(a[:4], b[:4])

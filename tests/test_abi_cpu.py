@@ -18,7 +18,7 @@ FAKE = ctypes.c_void_p(4096)  # never dereferenced: every call below fails valid
 def test_exports_every_declared_symbol():
     lib = L.lib()
     declared = L.header_symbols()
-    assert len(declared) == 11
+    assert len(declared) == 14
     for name in declared:
         assert hasattr(lib, name), name
     assert set(declared) == set(L.SIGNATURES)
@@ -150,3 +150,24 @@ def test_model_decode_checks():
     assert call(tab=bad) == -1
     assert call(d=_d(batch=4, seq_len=1, n_q_heads=32, n_kv_heads=8, window=129)) == -4
     assert call(d=_d(batch=4, seq_len=1, n_q_heads=32, n_kv_heads=8, dtype=L.F32)) == -4
+
+
+def test_varlen_prefill_checks():
+    lib = L.lib()
+    d = _d(batch=1, seq_len=1000, n_q_heads=8, n_kv_heads=2)
+    call = lambda **kw: lib.zgattn_swa_prefill_varlen(
+        ctypes.byref(kw.get("d", d)), kw.get("cu", FAKE), kw.get("n", 3), kw.get("mx", 600),
+        FAKE, FAKE, FAKE, kw.get("g", FAKE), FAKE, FAKE, FAKE, None)
+    assert call(d=_d(batch=2, seq_len=1000, n_q_heads=8, n_kv_heads=2)) == -1   # B must be 1
+    assert call(n=0) == -1
+    assert call(mx=1001) == -1
+    assert call(cu=None) == -2
+    assert call(g=None) == -2
+    assert call(d=_d(batch=1, seq_len=1000, n_q_heads=8, n_kv_heads=2, dtype=L.F32)) == -4
+    assert call(mx=0, cu=None, g=None) == 0                     # every document empty
+    ws = lib.zgattn_global_prefill_varlen_workspace_bytes(ctypes.byref(d), 3)
+    kbytes = 2 * 1000 * 128 * 2
+    assert ws == ((kbytes + 255) // 256) * 256 + 2 * (1000 // 64 + 3) * 64 * 128 * 2
+    st = lib.zgattn_global_prefill_varlen(ctypes.byref(d), FAKE, 3, 600, FAKE, FAKE, FAKE,
+                                          FAKE, FAKE, FAKE, ws - 1, FAKE, None)
+    assert st == -5

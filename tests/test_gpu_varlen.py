@@ -1,0 +1,108 @@
+"""Packed variable-length prefill and RoPE base 1e7 against the fp64 oracle (GPU).
+
+Documents of a packed sequence are independent sequences (oracle ``prefill_varlen``);
+lengths cover a single token, tile boundaries (63, 64, 65, 128, 129), and documents longer
+than several tiles, so boundaries fall inside K/V tiles and query tiles.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import attn as O
+from tests.gpu_util import TOL_BF16, host64, maxabs, need_gpu, say, threads
+from workloads import host_tensor, norm_weight
+
+pytestmark = pytest.mark.gpu
+
+
+def _zg():
+    need_gpu()
+    import global_attention_qk_amd as zg
+    return zg
+
+
+def _packed(lens, Hq, Hkv, d, seed):
+    import torch
+    T = int(sum(lens))
+    q = host_tensor((T, Hq, d), seed, "bf16")
+    k = host_tensor((T, Hkv, d), seed + 1, "bf16")
+    v = host_tensor((T, Hkv, d), seed + 2, "bf16")
+    g = host_tensor((T, Hq, d), seed + 3, "bf16", 2 ** 0.5)
+    wq = torch.from_numpy(norm_weight(d, seed + 4))
+    wk = torch.from_numpy(norm_weight(d, seed + 5))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return q, k, v, g, wq, wk, cu
+
+
+def _run(kind, lens, Hq, Hkv, d, seed, *, window=128, workspace="auto", rope_base=10000.0,
+         pos_offset=0, rows=None):
+    zg = _zg()
+    import torch
+    q, k, v, g, wq, wk, cu = _packed(lens, Hq, Hkv, d, seed)
+    r = zg.rotary_dim_for(d)
+    dv = [t.cuda() for t in (q, k, v, g, wq, wk)]
+    cud = torch.from_numpy(cu).cuda()
+    mx = int(max(lens))
+    if kind == "swa":
+        out = zg.swa_prefill_varlen(dv[0], dv[1], dv[2], dv[3], dv[4], dv[5], cud, mx,
+                                    window=window, rotary_dim=r, rope_base=rope_base,
+                                    pos_offset=pos_offset)
+    else:
+        out = zg.global_prefill_varlen(dv[0], dv[1], dv[2], dv[4], dv[5], cud, mx,
+                                       rotary_dim=r, rope_base=rope_base,
+                                       pos_offset=pos_offset, workspace=workspace)
+    torch.cuda.synchronize()
+    want = O.prefill_varlen(host64(q), host64(k), host64(v),
+                            host64(g) if kind == "swa" else None, host64(wq), host64(wk), cu,
+                            rows=rows, window=window if kind == "swa" else None, rotary_dim=r,
+                            rope_base=rope_base, pos_offset=pos_offset, threads=threads())
+    got = host64(out) if rows is None else host64(out)[rows]
+    err = maxabs(got, want)
+    say("varlen", kind, d, Hq, Hkv, lens[:8], f"W={window} base={rope_base} err={err:.3e}")
+    assert err <= TOL_BF16, err
+
+
+LENS = [1, 63, 64, 65, 300, 7, 129, 200, 128]
+
+
+@pytest.mark.parametrize("ws", ["auto", None])
+def test_global_varlen(ws):
+    _run("global", LENS, 8, 2, 128, 500, workspace=ws)
+
+
+def test_global_varlen_head_dim_64():
+    _run("global", [70, 1, 190, 64], 4, 1, 64, 510)
+
+
+@pytest.mark.parametrize("window", [128, 50])
+def test_swa_varlen_model_shape(window):
+    # d 128, four query heads per KV head, rotary 42: the streaming SWA kernel
+    _run("swa", LENS, 8, 2, 128, 520, window=window)
+
+
+def test_swa_varlen_other_shape():
+    # d 64: the tiled SWA kernel
+    _run("swa", [70, 1, 190, 64], 4, 1, 64, 530)
+
+
+def test_varlen_single_document_and_empty_documents():
+    # empty documents (repeated offsets) are skipped; one long document is the dense layer
+    _run("global", [0, 300, 0, 0, 45, 0], 8, 2, 128, 540)
+    _run("swa", [0, 300, 0, 0, 45, 0], 8, 2, 128, 550)
+
+
+@pytest.mark.parametrize("kind", ["swa", "global"])
+def test_rope_base_ten_million(kind):
+    # the 256K training stage's RoPE base (explainer, section 中訓練), large positions
+    _run(kind, [200, 333], 8, 2, 128, 560, rope_base=1e7, pos_offset=200000)
+
+
+def test_global_varlen_long_documents_sampled_rows():
+    lens = [40000, 1, 20000, 5535]
+    T = sum(lens)
+    rng = np.random.default_rng(570)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    edges = np.concatenate([cu[:-1], cu[1:] - 1, cu[:-1] + 63, cu[:-1] + 64])
+    rows = np.unique(np.concatenate([edges[(edges >= 0) & (edges < T)],
+                                     rng.integers(0, T, 256)]))
+    _run("global", lens, 8, 2, 128, 570, rows=rows)

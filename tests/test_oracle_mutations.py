@@ -88,8 +88,26 @@ def _layer_kinds_shifted(n=32, period=6):
     return ["global" if i % period == 0 else "swa" for i in range(n)]
 
 
+def _varlen_boundary_shifted(q, k, v, g, wq, wk, cu_seqlens, **kw):
+    # every interior document boundary one token late
+    cu = [int(x) for x in cu_seqlens]
+    moved = [cu[0]] + [min(c + 1, cu[-1]) for c in cu[1:-1]] + [cu[-1]]
+    return _ORIG["prefill_varlen"](q, k, v, g, wq, wk, moved, **kw)
+
+
+def _varlen_sees_previous_document(q, k, v, g, wq, wk, cu_seqlens, **kw):
+    # each document also attends to the document before it
+    cu = [int(x) for x in cu_seqlens]
+    out = _ORIG["prefill_varlen"](q, k, v, g, wq, wk, cu_seqlens, **kw)
+    if len(cu) > 2 and kw.get("rows") is None:
+        merged = [cu[0]] + cu[2:]
+        out2 = _ORIG["prefill_varlen"](q, k, v, g, wq, wk, merged, **kw)
+        out[cu[1]:cu[2]] = out2[cu[1]:cu[2]]
+    return out
+
+
 _ORIG = {n: getattr(O, n) for n in ("partial_rope", "rmsnorm", "visible_mask", "sigmoid",
-                                     "kv_bytes_per_token", "layer_kinds")}
+                                     "kv_bytes_per_token", "layer_kinds", "prefill_varlen")}
 
 MUTANTS = {
     "rope_sign": ("partial_rope", _rope_sign_flipped),
@@ -102,6 +120,8 @@ MUTANTS = {
     "gate_without_sigmoid": ("sigmoid", _sigmoid_wrong),
     "kv_bytes_k_only": ("kv_bytes_per_token", _kv_bytes_no_factor2),
     "schedule_shifted": ("layer_kinds", _layer_kinds_shifted),
+    "varlen_boundary_shifted": ("prefill_varlen", _varlen_boundary_shifted),
+    "varlen_crosses_documents": ("prefill_varlen", _varlen_sees_previous_document),
 }
 
 PINS = [getattr(P, n) for n in dir(P) if n.startswith("pin_")]
