@@ -352,3 +352,66 @@ def pin_varlen_isolation():
     a = O.prefill_varlen(q, k, v, None, w, w, cu, rotary_dim=4)
     b = O.prefill_varlen(q, k2, v2, None, w, w, cu, rotary_dim=4)
     assert np.array_equal(a[4:], b[4:]) and not np.array_equal(a[:4], b[:4])
+
+
+def pin_grad_forward_is_the_layer():
+    """The differentiable restatement of the layer equals the oracle's forward, and its
+    log-sum-exp equals the brute-force sum over each row's visible scores."""
+    from oracle import grad as OG
+    import torch
+    B, T, Hq, Hkv, d, r = 2, 9, 4, 2, 8, 4
+    q, k, v = _rand((B, T, Hq, d), 101), _rand((B, T, Hkv, d), 102), _rand((B, T, Hkv, d), 103)
+    g = _rand((B, T, Hq, d), 104)
+    wq, wk = 1 + 0.1 * _rand((d,), 105), 1 + 0.1 * _rand((d,), 106)
+    for W, gg in ((None, None), (3, g)):
+        want = O.prefill(q, k, v, gg, wq, wk, window=W, rotary_dim=r, pos_offset=7)
+        out, lse = OG.layer_torch(*(torch.as_tensor(x) for x in (q, k, v)),
+                                  None if gg is None else torch.as_tensor(gg),
+                                  torch.as_tensor(wq), torch.as_tensor(wk), window=W,
+                                  rotary_dim=r, pos_offset=7)
+        assert np.allclose(out.numpy(), want, rtol=0, atol=1e-12), W
+        qt = O.qknorm_rope(q, wq, 7 + np.arange(T)[None, :, None], r)
+        kt = O.qknorm_rope(k, wk, 7 + np.arange(T)[None, :, None], r)
+        for b in range(B):
+            for h in range(Hq):
+                for i in range(T):
+                    js = [j for j in range(T) if j <= i and (W is None or j > i - W)]
+                    s = [float(qt[b, i, h] @ kt[b, j, h // 2]) / math.sqrt(d) for j in js]
+                    ref = math.log(sum(math.exp(x) for x in s))
+                    assert abs(lse.numpy()[b, h, i] - ref) < 1e-12
+
+
+def pin_grad_finite_differences():
+    """Every gradient (q, k, v, g, w_q, w_k) equals central differences of the forward
+    sum(dout * out) at sampled coordinates, for a gated window layer and a global layer."""
+    from oracle import grad as OG
+    B, T, Hq, Hkv, d, r = 1, 7, 4, 2, 8, 4
+    q, k, v = _rand((B, T, Hq, d), 111), _rand((B, T, Hkv, d), 112), _rand((B, T, Hkv, d), 113)
+    g, dout = _rand((B, T, Hq, d), 114), _rand((B, T, Hq, d), 115)
+    wq, wk = 1 + 0.1 * _rand((d,), 116), 1 + 0.1 * _rand((d,), 117)
+    rng = np.random.default_rng(118)
+    h = 1e-5
+    for W, gg in ((3, g), (None, None)):
+        args = dict(q=q, k=k, v=v, g=gg, wq=wq, wk=wk)
+        gr = OG.prefill_grads(q, k, v, gg, wq, wk, dout, window=W, rotary_dim=r, pos_offset=3)
+
+        def loss(**kw):
+            a = dict(args)
+            a.update(kw)
+            o = O.prefill(a["q"], a["k"], a["v"], a["g"], a["wq"], a["wk"], window=W,
+                          rotary_dim=r, pos_offset=3)
+            return float(np.sum(o * dout))
+
+        for name in ("q", "k", "v", "g", "wq", "wk"):
+            if args[name] is None:
+                assert gr["dg"] is None
+                continue
+            x = args[name]
+            for _ in range(6):
+                idx = tuple(int(rng.integers(0, n)) for n in x.shape)
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                fd = (loss(**{name: xp}) - loss(**{name: xm})) / (2 * h)
+                an = gr["d" + name][idx]
+                assert abs(fd - an) <= 1e-6 * max(1.0, abs(fd)), (W, name, idx, fd, an)

@@ -106,6 +106,25 @@ def _varlen_sees_previous_document(q, k, v, g, wq, wk, cu_seqlens, **kw):
     return out
 
 
+from oracle import grad as OG
+
+_ORIG_GRADS = OG.prefill_grads
+
+
+def _grads_wk_forgotten(*a, **kw):
+    r = _ORIG_GRADS(*a, **kw)
+    r["dwk"] = np.zeros_like(r["dwk"])          # the norm weight of k left out
+    return r
+
+
+def _grads_dk_not_summed_over_group(*a, **kw):
+    r = _ORIG_GRADS(*a, **kw)
+    q = np.asarray(a[0])
+    grp = q.shape[2] // r["dk"].shape[2]
+    r["dk"] = r["dk"] / grp                     # one query head's share instead of the sum
+    return r
+
+
 _ORIG = {n: getattr(O, n) for n in ("partial_rope", "rmsnorm", "visible_mask", "sigmoid",
                                      "kv_bytes_per_token", "layer_kinds", "prefill_varlen")}
 
@@ -121,6 +140,8 @@ MUTANTS = {
     "kv_bytes_k_only": ("kv_bytes_per_token", _kv_bytes_no_factor2),
     "schedule_shifted": ("layer_kinds", _layer_kinds_shifted),
     "varlen_boundary_shifted": ("prefill_varlen", _varlen_boundary_shifted),
+    "grad_wk_forgotten": (OG, "prefill_grads", _grads_wk_forgotten),
+    "grad_dk_one_head": (OG, "prefill_grads", _grads_dk_not_summed_over_group),
     "varlen_crosses_documents": ("prefill_varlen", _varlen_sees_previous_document),
 }
 
@@ -129,8 +150,9 @@ PINS = [getattr(P, n) for n in dir(P) if n.startswith("pin_")]
 
 @pytest.mark.parametrize("mutant", sorted(MUTANTS))
 def test_some_pin_catches(mutant, monkeypatch):
-    attr, fn = MUTANTS[mutant]
-    monkeypatch.setattr(O, attr, fn)
+    spec = MUTANTS[mutant]
+    mod, attr, fn = spec if len(spec) == 3 else (O, *spec)
+    monkeypatch.setattr(mod, attr, fn)
     caught = []
     for pin in PINS:
         try:
