@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--varlen", action="store_true",
                     help="packed-document prefill: 262144 tokens in 16 documents of 16K and "
                          "in 24 documents of mixed length (one JSON line per packing)")
+    ap.add_argument("--backward", action="store_true",
+                    help="backward pass of one SWA and one global layer at B=1, T=65536 "
+                         "(the 32-layer stack's per-layer size)")
     ap.add_argument("--sweep", action="store_true",
                     help="attention-stack sweep: 32-layer hybrid / SWA 3:1 / full-attention "
                          "stacks at T = 4K .. 256K (one JSON line per T)")
@@ -115,6 +118,8 @@ def main():
         return run_model_decode(args)
     if args.varlen:
         return run_varlen(args)
+    if args.backward:
+        return run_backward(args)
     T, B, Hq, Hkv, d, W = C4.T, C4.B, C4.Hq, C4.Hkv, C4.d, C4.window
     r = C4.rotary_dim
     # ---- inputs (seeded, generated on the device, outside the timed region) -----------
@@ -317,6 +322,51 @@ def run_model_decode(args):
                          * el * 2) / 2 ** 30,
     }
     print(json.dumps(rec), flush=True)
+
+
+def run_backward(args):
+    """Backward pass of a gated SWA layer and a global layer at B=1, T=65,536, Hq=32, Hkv=8,
+    d=128 (seeded inputs, dout ~ N(0,1)); HIP events around each call (median of the
+    steps). FLOPs count the five products of the standard backward (S, dP, dV, dK, dQ) on
+    the visible pairs: 2.5x the forward's."""
+    import torch
+
+    import global_attention_qk_amd as zg
+    from workloads import C3, device_tensor, prefill_inputs, seed_for
+
+    dev = "cuda"
+    r, W, T = C3.rotary_dim, C3.window, C3.T
+    q, k, v, g, wq, wk = prefill_inputs(C3, device=dev)
+    dout = device_tensor(q.shape, seed_for(3, 0, "k_new"), "bf16", dev)
+    ws = torch.empty(zg.prefill_backward_workspace_bytes(q, k), dtype=torch.uint8, device=dev)
+    cnt = alg_counts(T, C3.B, C3.Hq, C3.Hkv, C3.d, W, 1, 1)
+    res = {}
+    for kind in ("swa", "global"):
+        gg = g if kind == "swa" else None
+        if kind == "swa":
+            out = zg.swa_prefill(q, k, v, g, wq, wk, window=W, rotary_dim=r)
+        else:
+            out = zg.global_prefill(q, k, v, wq, wk, rotary_dim=r)
+        fn = lambda: zg.prefill_backward(q, k, v, gg, wq, wk, out, dout, window=W,
+                                         rotary_dim=r, workspace=ws)
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(max(args.steps, 1)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = sorted(ts)[len(ts) // 2]
+        flops = 2.5 * cnt["swa_flops" if kind == "swa" else "glob_flops"]
+        res[kind] = {"ms": round(ms, 3), "tokens_per_s": T / (ms / 1e3),
+                     "tflops": flops / (ms / 1e3) / 1e12,
+                     "mfma_frac": flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS}
+        print(f"[backward] {kind}: {ms:.3f} ms", file=sys.stderr, flush=True)
+    print(json.dumps({"backward": "B=1 T=65536 Hq=32 Hkv=8 d=128 rotary 42 bf16", **res}),
+          flush=True)
 
 
 def varlen_packings(T: int = 262144):

@@ -15,6 +15,8 @@ from .api import (  # noqa: F401
     make_desc,
     model_decode,
     model_decode_workspace_bytes,
+    prefill_backward,
+    prefill_backward_workspace_bytes,
     qknorm_rope,
     rotary_dim_for,
     swa_decode,

@@ -62,6 +62,9 @@ SIGNATURES = {
     "zgattn_global_decode_workspace_bytes": (SZ, [DP, I32]),
     "zgattn_qknorm_rope": (ctypes.c_int, [DP, I32, P, P, P, P, I64, I64, I64, P]),
     "zgattn_swa_prefill_varlen": (ctypes.c_int, [DP, P, I32, I32, P, P, P, P, P, P, P, P]),
+    "zgattn_prefill_backward_workspace_bytes": (SZ, [DP]),
+    "zgattn_swa_prefill_backward": (ctypes.c_int, [DP] + [P] * 15 + [SZ, P]),
+    "zgattn_global_prefill_backward": (ctypes.c_int, [DP] + [P] * 13 + [SZ, P]),
     "zgattn_global_prefill_varlen": (ctypes.c_int, [DP, P, I32, I32, P, P, P, P, P, P, SZ, P,
                                                     P]),
     "zgattn_global_prefill_varlen_workspace_bytes": (SZ, [DP, I32]),

@@ -283,3 +283,37 @@ def model_decode(layers, pos, *, window=128, capacity=None, rotary_dim=None,
                                     _ptr(workspace), workspace.numel(), _stream()),
           "zgattn_model_decode")
     return [L["out"] for L in layers]
+
+
+def prefill_backward_workspace_bytes(q, k) -> int:
+    d = _prefill_desc(q, k, 1, None, 0, 10000.0, 1e-6, 0.0)
+    return int(lib().zgattn_prefill_backward_workspace_bytes(ctypes.byref(d)))
+
+
+def prefill_backward(q, k, v, g, wq, wk, out, dout, *, window=None, rotary_dim=None,
+                     pos_offset=0, rope_base=10000.0, eps=1e-6, scale=0.0, workspace=None):
+    """Gradients of sum(dout * out) for the layer that produced ``out``: a gated SWA layer
+    when ``g`` is given (``window`` its width), else the global layer. Returns dq, dk, dv,
+    dg (None for the global layer), dwq, dwk."""
+    _dev(q, k, v, g, wq, wk, out, dout)
+    swa = g is not None
+    d = _prefill_desc(q, k, window if swa else 1, rotary_dim, pos_offset, rope_base, eps, scale)
+    if workspace is None:
+        n = int(lib().zgattn_prefill_backward_workspace_bytes(ctypes.byref(d)))
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dg = torch.empty_like(g) if swa else None
+    dwq = torch.empty(q.shape[-1], dtype=torch.float32, device=q.device)
+    dwk = torch.empty_like(dwq)
+    nb = workspace.numel() * workspace.element_size()
+    if swa:
+        check(lib().zgattn_swa_prefill_backward(
+            ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(wq), _ptr(wk), _ptr(out),
+            _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dwq), _ptr(dwk),
+            _ptr(workspace), nb, _stream()), "zgattn_swa_prefill_backward")
+    else:
+        check(lib().zgattn_global_prefill_backward(
+            ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(wq), _ptr(wk), _ptr(out),
+            _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dwq), _ptr(dwk), _ptr(workspace), nb,
+            _stream()), "zgattn_global_prefill_backward")
+    return dq, dk, dv, dg, dwq, dwk

@@ -23,7 +23,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libzgattn.so")
 OBJDIR = os.path.join(PKG, "_build")
 
-SOURCES = ["prefill_bf16.hip", "prefill_swa_stream.hip", "prefill_f32.hip", "qknorm_rope.hip", "decode.hip", "api.cpp"]
+SOURCES = ["prefill_bf16.hip", "prefill_swa_stream.hip", "prefill_f32.hip", "qknorm_rope.hip", "decode.hip",
+           "backward.hip", "api.cpp"]
 
 
 def hipcc() -> str:

@@ -362,6 +362,80 @@ int zgattn_global_prefill_varlen(const zgattn_desc* d, const int32_t* cu_seqlens
   return hip_status(launch_prefill_bf16(a, s));
 }
 
+size_t zgattn_prefill_backward_workspace_bytes(const zgattn_desc* d) {
+  if (check_desc(d) || d->seq_len < 0 || d->dtype != ZGATTN_BF16) return 0;
+  return backward_workspace_bytes(d->batch, d->seq_len, d->n_q_heads, d->n_kv_heads,
+                                  d->head_dim);
+}
+
+int backward_common(const zgattn_desc* d, int swa, const void* q, const void* k, const void* v,
+                    const void* g, const float* wq, const float* wk, const void* out,
+                    const void* dout, void* dq, void* dk, void* dv, void* dg, float* dwq,
+                    float* dwk, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = prefill_common(d, q, k, v, wq, wk, const_cast<void*>(out));
+  if (st) return st;
+  if (swa && d->window < 1) return ZGATTN_EINVAL;
+  if (d->seq_len == 0) return ZGATTN_OK;
+  if (!dout || !dq || !dk || !dv || !dwq || !dwk || (swa && (!g || !dg))) return ZGATTN_ENULL;
+  if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+      (swa && (!aligned16(g) || !aligned16(dg))))
+    return ZGATTN_EINVAL;
+  if (d->dtype != ZGATTN_BF16) return ZGATTN_EUNSUPPORTED;
+  const int G = d->n_q_heads / d->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return ZGATTN_EUNSUPPORTED;
+  if (!workspace || !aligned16(workspace) ||
+      workspace_bytes < zgattn_prefill_backward_workspace_bytes(d))
+    return ZGATTN_EWORKSPACE;
+  BackwardArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = swa ? g : nullptr;
+  a.out = out;
+  a.dout = dout;
+  a.wq = wq;
+  a.wk = wk;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dg = swa ? dg : nullptr;
+  a.dwq = dwq;
+  a.dwk = dwk;
+  a.ws = workspace;
+  a.B = d->batch;
+  a.T = d->seq_len;
+  a.Hq = d->n_q_heads;
+  a.Hkv = d->n_kv_heads;
+  a.d = d->head_dim;
+  a.window = d->window;
+  a.rdim = d->rotary_dim;
+  a.pos_offset = d->pos_offset;
+  a.swa = swa;
+  a.eps = d->rms_eps;
+  a.scale = scale_of(d);
+  a.fr = rope_freq(d->rotary_dim, d->rope_base);
+  return hip_status(launch_prefill_backward(a, (hipStream_t)stream));
+}
+
+int zgattn_swa_prefill_backward(const zgattn_desc* d, const void* q, const void* k,
+                                const void* v, const void* g, const float* wq, const float* wk,
+                                const void* out, const void* dout, void* dq, void* dk,
+                                void* dv, void* dg, float* dwq, float* dwk, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (!g && d && d->seq_len > 0) return check_desc(d) ? check_desc(d) : ZGATTN_ENULL;
+  return backward_common(d, 1, q, k, v, g, wq, wk, out, dout, dq, dk, dv, dg, dwq, dwk,
+                         workspace, workspace_bytes, stream);
+}
+
+int zgattn_global_prefill_backward(const zgattn_desc* d, const void* q, const void* k,
+                                   const void* v, const float* wq, const float* wk,
+                                   const void* out, const void* dout, void* dq, void* dk,
+                                   void* dv, float* dwq, float* dwk, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  return backward_common(d, 0, q, k, v, nullptr, wq, wk, out, dout, dq, dk, dv, nullptr, dwq,
+                         dwk, workspace, workspace_bytes, stream);
+}
+
 int zgattn_model_decode(const zgattn_desc* d, int32_t n_layers, const int32_t* is_global,
                         const zgattn_decode_layer* layers, int32_t capacity,
                         const int32_t* pos, void* workspace, size_t workspace_bytes,

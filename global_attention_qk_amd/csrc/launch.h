@@ -62,6 +62,30 @@ struct NormRopeArgs {
 };
 hipError_t launch_qknorm_rope(const NormRopeArgs& a, hipStream_t s);
 
+// Backward pass of a prefill call (bf16, d 64 or 128): gradients of sum(dout * out).
+struct BackwardArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* g;       // gate pre-activation (SWA) or nullptr
+  const void* out;     // the forward's output
+  const void* dout;
+  const float* wq;
+  const float* wk;
+  void* dq;
+  void* dk;
+  void* dv;
+  void* dg;            // SWA only
+  float* dwq;
+  float* dwk;
+  void* ws;            // workspace of backward_workspace_bytes()
+  int B, T, Hq, Hkv, d, window, rdim, pos_offset, swa;
+  float eps, scale;
+  RopeFreq fr;
+};
+size_t backward_workspace_bytes(int B, int T, int Hq, int Hkv, int d);
+hipError_t launch_prefill_backward(const BackwardArgs& a, hipStream_t s);
+
 // One decode step (either layer kind), bf16.
 struct DecodeArgs {
   const void* q;       // [B][Hq][d]

@@ -134,6 +134,29 @@ int zgattn_global_prefill_varlen(const zgattn_desc* desc, const int32_t* cu_seql
 size_t zgattn_global_prefill_varlen_workspace_bytes(const zgattn_desc* desc, int32_t n_docs);
 
 /*
+ * Backward pass of a prefill call: the gradients of sum(dout * out) with respect to q, k,
+ * v, g (SWA), w_q and w_k, where out is the layer of zgattn_swa_prefill /
+ * zgattn_global_prefill on the same inputs (the pages train the model end to end, explainer
+ * training sections, but print no backward formula: this is the gradient of the forward
+ * stated above). out is the forward's output (its log-sum-exp is recomputed, so only out is
+ * needed from the forward). dq, dg: [B, T, Hq, d]; dk, dv: [B, T, Hkv, d] (bf16, written,
+ * not accumulated); dwq, dwk: fp32 [d] (written). workspace (device, >=
+ * zgattn_prefill_backward_workspace_bytes(desc) bytes) holds the transformed q~/k~, the
+ * row statistics and the fp32 gradients of q~ and k~. bf16 only; head groups 1, 2, 4, 8.
+ */
+size_t zgattn_prefill_backward_workspace_bytes(const zgattn_desc* desc);
+int zgattn_swa_prefill_backward(const zgattn_desc* desc, const void* q, const void* k,
+                                const void* v, const void* g, const float* wq, const float* wk,
+                                const void* out, const void* dout, void* dq, void* dk,
+                                void* dv, void* dg, float* dwq, float* dwk, void* workspace,
+                                size_t workspace_bytes, void* stream);
+int zgattn_global_prefill_backward(const zgattn_desc* desc, const void* q, const void* k,
+                                   const void* v, const float* wq, const float* wk,
+                                   const void* out, const void* dout, void* dq, void* dk,
+                                   void* dv, float* dwq, float* dwk, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/*
  * Gated SWA decode: one new token per sequence against a ring of `window` entries
  * (explainer, section アーキテクチャ: the SWA layers keep only a fixed 128 tokens).
  *   q, g, out: [B, Hq, d];  k_new, v_new: [B, Hkv, d] (raw, before norm/RoPE);

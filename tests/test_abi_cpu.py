@@ -18,7 +18,7 @@ FAKE = ctypes.c_void_p(4096)  # never dereferenced: every call below fails valid
 def test_exports_every_declared_symbol():
     lib = L.lib()
     declared = L.header_symbols()
-    assert len(declared) == 14
+    assert len(declared) == 17
     for name in declared:
         assert hasattr(lib, name), name
     assert set(declared) == set(L.SIGNATURES)
@@ -170,4 +170,31 @@ def test_varlen_prefill_checks():
     assert ws == ((kbytes + 255) // 256) * 256 + 2 * (1000 // 64 + 3) * 64 * 128 * 2
     st = lib.zgattn_global_prefill_varlen(ctypes.byref(d), FAKE, 3, 600, FAKE, FAKE, FAKE,
                                           FAKE, FAKE, FAKE, ws - 1, FAKE, None)
+    assert st == -5
+
+
+def test_backward_checks():
+    lib = L.lib()
+    d = _d(batch=2, seq_len=300, n_q_heads=8, n_kv_heads=2)
+    need = lib.zgattn_prefill_backward_workspace_bytes(ctypes.byref(d))
+    nq, nk = 2 * 300 * 8, 2 * 300 * 2
+    a256 = lambda x: (x + 255) // 256 * 256
+    nb = lambda n: (n + 63) // 64
+    assert need == (a256(nq * 128 * 2) + a256(nk * 128 * 2) + a256(nq * 128 * 2) + 2 * a256(nq * 4)
+                    + a256(nq * 128 * 4) + a256(nk * 128 * 4) + a256((nb(nq) + nb(nk)) * 128 * 4))
+    call = lambda **kw: lib.zgattn_swa_prefill_backward(
+        ctypes.byref(kw.get("d", d)), FAKE, FAKE, FAKE, kw.get("g", FAKE), FAKE, FAKE, FAKE,
+        kw.get("dout", FAKE), FAKE, FAKE, FAKE, kw.get("dg", FAKE), FAKE, FAKE,
+        kw.get("ws", FAKE), kw.get("nb", need), None)
+    assert call(ws=None) == -5
+    assert call(nb=need - 1) == -5
+    assert call(g=None) == -2
+    assert call(dg=None) == -2
+    assert call(dout=None) == -2
+    assert call(dout=ctypes.c_void_p(4100)) == -1
+    assert call(d=_d(batch=2, seq_len=300, n_q_heads=8, n_kv_heads=2, dtype=L.F32)) == -4
+    assert call(d=_d(batch=2, seq_len=300, n_q_heads=48, n_kv_heads=3)) == -4
+    assert call(d=_d(batch=2, seq_len=0, n_q_heads=8, n_kv_heads=2)) == 0
+    st = lib.zgattn_global_prefill_backward(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                            FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, need, None)
     assert st == -5
