@@ -27,7 +27,6 @@ constexpr int kT = 256;         // threads per workgroup (4 waves)
 constexpr int kKB = 64;         // keys per tile (dQ) / per workgroup (dK, dV)
 constexpr int kQB = 64;         // queries per tile (dK, dV)
 constexpr int kRowsDQ = 128;    // query rows per dQ workgroup (4 waves x 32)
-constexpr int kNormRows = 64;   // rows per norm/RoPE backward workgroup
 
 // Swap bits 2 and 3 of an index within its 16-group: the order in which a lane-half holds
 // rows of a 32x32 accumulator (rows 8 (r/4) + 4 hi + r%4), used as the k-slot order of the
@@ -58,6 +57,9 @@ struct BArgs {
   bf16* da;           // dA [B][T][Hq][D] (workspace; dout itself for the global layer)
   float* dsum;        // D [B][Hq][T]
   float* lse;         // row log-sum-exp, log2 units [B][Hq][T]
+  const bf16* ktT;    // K~^T tiles [B][Hkv][n64][D][64], keys in slot order (workspace)
+  const bf16* qtT;    // Q~^T tiles [B][Hq][n64][D][64]
+  const bf16* daT;    // dA^T tiles [B][Hq][n64][D][64]
   float* dqt;         // dq~ [B][T][Hq][D] fp32
   float* dkt;         // dk~ [B][T][Hkv][D] fp32
   bf16* dv;           // dV [B][T][Hkv][D]
@@ -117,35 +119,71 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(const BArgs p) {
   }
 }
 
+// ---- transposed 64-position tiles --------------------------------------------------------
+// src row (b, h, pos) at src + b * sb + h * sh + pos * sp (elements); dst tile
+// ((b * H + h) * n_tiles + tile) is [D][64] with column s holding position 64 tile +
+// slot_row(s) (positions past T are zero).
+template <int D>
+__global__ __launch_bounds__(kT) void bwd_tiles_kernel(const bf16* src, int64_t sb, int64_t sh,
+                                                       int64_t sp, int H, int T, int n_tiles,
+                                                       bf16* dst) {
+  __shared__ __attribute__((aligned(16))) bf16 t[64][D + 8];
+  const int tile = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / H, h = bh % H;
+  const bf16* base = src + b * sb + h * sh;
+  for (int c = threadIdx.x; c < 64 * (D / 8); c += kT) {
+    const int r = c / (D / 8), dc = c % (D / 8);
+    const int pos = tile * 64 + r;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (pos < T) val = *(const u32x4*)(base + pos * sp + dc * 8);
+    *(u32x4*)&t[r][dc * 8] = val;
+  }
+  __syncthreads();
+  bf16* out = dst + ((size_t)bh * n_tiles + tile) * (64 * D);
+  for (int c = threadIdx.x; c < D * 8; c += kT) {
+    const int d = c / 8, sc = c % 8;
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = t[slot_row(sc * 8 + e)][d];
+    *(bf16x8*)(out + d * 64 + sc * 8) = o;
+  }
+}
+
 // ---- dQ: one workgroup per (batch, KV head, 128 query rows of the group's heads) --------
+// LDS tiles are unpadded and filled by LDS DMA, their 16-byte chunks XOR-swizzled as in
+// the forward kernel (chunk_pos): a key-tile buffer holds K~ rows [64][D], V rows [64][D]
+// and K~^T [D][64]; tiles are fetched kDQAhead tiles ahead into kDQAhead + 1 buffers.
+constexpr int kDQAhead = 2;
+
 template <int D, bool SWA>
 __global__ __launch_bounds__(kT) void bwd_dq_kernel(const BArgs p) {
   constexpr int KS = D / 16;             // k-steps over d
   constexpr int DB = D / 32;             // 32-row d blocks
-  constexpr int RW = D + 8;              // padded row (elements)
-  constexpr int TW = kKB + 8;            // padded transposed row (elements)
+  constexpr int RB = D * 2;              // row bytes
+  constexpr int TILE = kKB * RB;         // bytes of one [64][D] (or [D][64]) tile
+  constexpr int BUF = 3 * TILE;
+  constexpr int NB = kDQAhead + 1;
+  constexpr int KPW = D / 32;            // 1 KiB DMA blocks per wave per tile
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  bf16* sK = (bf16*)smem;                        // [64][RW] K~ rows
-  bf16* sV = sK + kKB * RW;                      // [64][RW] V rows
-  bf16* sKT = sV + kKB * RW;                     // [D][TW] K~^T, keys in slot order
+  const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int G = p.group, bmp = kRowsDQ / G, T = p.T;
   const int n_qt = (T + bmp - 1) / bmp;
+  const int n_kt = (T + kKB - 1) / kKB;
   const int qt = blockIdx.x % n_qt;
   const int hb = blockIdx.x / n_qt;
   const int b = hb / p.Hkv, kvh = hb % p.Hkv;
   const int i0 = qt * bmp;
-  const int row = wave * 32 + l32;                // this lane's query row in the tile
+  const int row = wave * 32 + l32;
   const int hg = row / bmp, pi = row % bmp;
   const int h = kvh * G + hg;
   const int qpos = i0 + pi;
   const bool qvalid = qpos < T;
   const int qc = min(qpos, T - 1);
 
-  // Q~ and dA of this lane's query as B operands (k = d)
   bf16x8 qreg[KS], dreg[KS];
   {
     const bf16* qrow = p.qt + (((size_t)b * p.Hq + h) * T + qc) * D;
@@ -161,48 +199,83 @@ __global__ __launch_bounds__(kT) void bwd_dq_kernel(const BArgs p) {
   const int q_last = min(i0 + bmp, T) - 1;
   const int k_lo = SWA ? max(0, i0 - p.window + 1) : 0;
   const int kt_lo = k_lo / kKB, kt_hi = q_last / kKB;
+  const int n_tiles = kt_hi - kt_lo + 1;
   const bf16* kbase = p.kt + ((size_t)b * p.Hkv + kvh) * T * D;
   const bf16* vbase = p.v + ((size_t)b * T * p.Hkv + kvh) * D;
+  const bf16* tbase = p.ktT + ((size_t)b * p.Hkv + kvh) * n_kt * (size_t)(kKB * D);
 
-  auto stage = [&](int kt, bool with_v) {
+  // DMA piece j of tile kt (with_v: K rows, V rows, K^T; else K rows only)
+  auto dma = [&](int kt, int buf, bool with_v) {
+    const uint32_t dst = lds0 + buf * BUF;
     const int k0 = kt * kKB;
-    for (int c = tid; c < kKB * (D / 8); c += kT) {
-      const int r = c / (D / 8), dc = c % (D / 8);
-      const int key = min(k0 + r, T - 1);
-      *(u32x4*)(sK + r * RW + dc * 8) = *(const u32x4*)(kbase + (size_t)key * D + dc * 8);
+#pragma unroll
+    for (int j = 0; j < KPW; ++j) {
+      constexpr int CPR = D / 8, RPB = 1024 / RB;
+      const int blk = wave * KPW + j;
+      const int r = blk * RPB + lane / CPR;
+      const int c = chunk_pos<CPR>(r, lane % CPR);
+      const int rr = min(r, T - 1 - k0);
+      dma16(kbase + (size_t)k0 * D, (uint32_t)(rr * RB + c * 16), dst + blk * 1024);
       if (with_v)
-        *(u32x4*)(sV + r * RW + dc * 8) =
-            *(const u32x4*)(vbase + (size_t)key * p.Hkv * D + dc * 8);
+        dma16(vbase + (size_t)k0 * p.Hkv * D, (uint32_t)(rr * p.Hkv * RB + c * 16),
+              dst + TILE + blk * 1024);
     }
-    __syncthreads();
     if (with_v) {
-      for (int c = tid; c < D * kKB; c += kT) {
-        const int dd = c / kKB, s = c % kKB;
-        sKT[dd * TW + s] = sK[slot_row(s) * RW + dd];
+#pragma unroll
+      for (int j = 0; j < KPW; ++j) {
+        const int blk = wave * KPW + j;
+        const int d = blk * 8 + (lane >> 3);
+        const int c = chunk_pos<8>(d, lane & 7);
+        dma16(tbase + (size_t)kt * (kKB * D), (uint32_t)(d * 128 + c * 16),
+              dst + 2 * TILE + blk * 1024);
       }
-      __syncthreads();
     }
   };
+  // per-lane operand offsets within a buffer (row swizzle depends on l32 & 15 only)
+  int roff[KS], toff[4];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) roff[ks] = l32 * RB + chunk_pos<D / 8>(l32, 2 * ks + hi) * 16;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) toff[x] = 2 * TILE + l32 * 128 + chunk_pos<8>(l32, 2 * x + hi) * 16;
+
   auto visible = [&](int key) {
     return qvalid && key <= qpos && (!SWA || key > qpos - p.window);
   };
-  auto scores = [&](int kb, f32x16& acc) {
+  auto run = [&](bool second, auto&& body) {
+    const int nd = second ? 3 * KPW : KPW;   // DMA instructions per wave per tile
+#pragma unroll
+    for (int a = 0; a < kDQAhead; ++a) dma(kt_lo + min(a, n_tiles - 1), a, second);
+    if (second) vm_wait<(kDQAhead - 1) * 3 * KPW>(); else vm_wait<(kDQAhead - 1) * KPW>();
+    __syncthreads();
+    int cur = 0;
+    for (int i = 0; i < n_tiles; ++i) {
+      const int ahead = (cur + kDQAhead) % NB;
+      dma(kt_lo + min(i + kDQAhead, n_tiles - 1), ahead, second);
+      body(kt_lo + i, smem + cur * BUF);
+      if (second) vm_wait<(kDQAhead - 1) * 3 * KPW>(); else vm_wait<(kDQAhead - 1) * KPW>();
+      __syncthreads();
+      cur = cur == NB - 1 ? 0 : cur + 1;
+    }
+    vm_wait<0>();
+    __syncthreads();
+    (void)nd;
+  };
+  auto scores = [&](const char* tb, int kb, f32x16& acc) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      acc = mfma32(*(const bf16x8*)(sK + (kb * 32 + l32) * RW + ks * 16 + hi * 8), qreg[ks], acc);
+      acc = mfma32(*(const bf16x8*)(tb + roff[ks] + kb * 32 * RB), qreg[ks], acc);
   };
 
-  // pass 1: row log-sum-exp (log2 units), online over the key tiles
+  // pass 1: row log-sum-exp (log2 units)
   float m = -INFINITY, l = 0.f;
-  for (int kt = kt_lo; kt <= kt_hi; ++kt) {
-    stage(kt, false);
+  run(false, [&](int kt, const char* tb) {
     const int k0 = kt * kKB;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x16 s;
-      scores(kb, s);
+      scores(tb, kb, s);
       float tm = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -219,14 +292,13 @@ __global__ __launch_bounds__(kT) void bwd_dq_kernel(const BArgs p) {
         m = mn;
       }
     }
-    __syncthreads();
-  }
+  });
   {
     const float mo = __shfl_xor(m, 32), lo = __shfl_xor(l, 32);
     const float ma = fmaxf(m, mo);
     const float la = (m == -INFINITY ? 0.f : l * fast_exp2(m - ma)) +
                      (mo == -INFINITY ? 0.f : lo * fast_exp2(mo - ma));
-    m = ma == -INFINITY ? 0.f : ma + __log2f(la);   // m now holds the row's log2 LSE
+    m = ma == -INFINITY ? 0.f : ma + __log2f(la);
   }
   const float lse2 = m;
 
@@ -236,35 +308,32 @@ __global__ __launch_bounds__(kT) void bwd_dq_kernel(const BArgs p) {
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
-  for (int kt = kt_lo; kt <= kt_hi; ++kt) {
-    stage(kt, true);
+  run(true, [&](int kt, const char* tb) {
     const int k0 = kt * kKB;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x16 s, dp;
-      scores(kb, s);
+      scores(tb, kb, s);
 #pragma unroll
       for (int r = 0; r < 16; ++r) dp[r] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        dp = mfma32(*(const bf16x8*)(sV + (kb * 32 + l32) * RW + ks * 16 + hi * 8), dreg[ks], dp);
+        dp = mfma32(*(const bf16x8*)(tb + TILE + roff[ks] + kb * 32 * RB), dreg[ks], dp);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
         const float pr = visible(key) ? fast_exp2(s[r] * p.qscale - lse2) : 0.f;
-        s[r] = pr * (dp[r] - drow_sum);               // dS^T
+        s[r] = pr * (dp[r] - drow_sum);
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const bf16x8 bo = pack8(s, j);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-          acc[db] = mfma32(*(const bf16x8*)(sKT + (db * 32 + l32) * TW + kb * 32 + 16 * j + hi * 8),
-                           bo, acc[db]);
+          acc[db] = mfma32(*(const bf16x8*)(tb + toff[2 * kb + j] + db * 32 * 128), bo, acc[db]);
       }
     }
-    __syncthreads();
-  }
+  });
   if (qvalid) {
     float* dst = p.dqt + (((size_t)b * T + qpos) * p.Hq + h) * D;
 #pragma unroll
@@ -283,31 +352,30 @@ __global__ __launch_bounds__(kT) void bwd_dq_kernel(const BArgs p) {
 }
 
 // ---- dK, dV: one workgroup per (batch, KV head, 64 keys) --------------------------------
+// A query-tile buffer holds Q~ rows [64][D], dA rows [64][D], Q~^T and dA^T [D][64] (all
+// unpadded, swizzled, filled by LDS DMA one tile ahead) and the tile's log-sum-exp and D.
 template <int D, bool SWA>
 __global__ __launch_bounds__(kT) void bwd_dkdv_kernel(const BArgs p) {
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int RW = D + 8;
-  constexpr int TW = kQB + 8;
+  constexpr int RB = D * 2;
+  constexpr int TILE = kQB * RB;
+  constexpr int BUF = 4 * TILE + 2 * kQB * 4;
+  constexpr int KPW = D / 32;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  bf16* sQ = (bf16*)smem;                  // [64][RW] Q~ rows
-  bf16* sA = sQ + kQB * RW;                // [64][RW] dA rows
-  bf16* sQT = sA + kQB * RW;               // [D][TW] Q~^T, queries in slot order
-  bf16* sAT = sQT + D * TW;                // [D][TW] dA^T
-  float* sL = (float*)(sAT + D * TW);      // [64] log2 LSE
-  float* sD = sL + kQB;                    // [64] D
+  const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int kb = wave & 1, qh = wave >> 1;
   const int T = p.T, G = p.group;
-  const int n_kt = (T + kKB - 1) / kKB;
-  const int kt = blockIdx.x % n_kt;
-  const int hb = blockIdx.x / n_kt;
+  const int n64 = (T + 63) / 64;
+  const int kt = blockIdx.x % n64;
+  const int hb = blockIdx.x / n64;
   const int b = hb / p.Hkv, kvh = hb % p.Hkv;
   const int k0 = kt * kKB;
-  const int key = k0 + kb * 32 + l32;      // this lane's key (column of S, dP)
+  const int key = k0 + kb * 32 + l32;
   const int kc = min(key, T - 1);
 
   bf16x8 kreg[KS], vreg[KS];
@@ -332,63 +400,99 @@ __global__ __launch_bounds__(kT) void bwd_dkdv_kernel(const BArgs p) {
   const int k_last = min(k0 + kKB, T) - 1;
   const int q_hi = SWA ? min(T - 1, k_last + p.window - 1) : T - 1;
   const int qt_lo = k0 / kQB, qt_hi = q_hi / kQB;
-  for (int hg = 0; hg < G; ++hg) {
-    const int h = kvh * G + hg;
-    const bf16* qbase = p.qt + ((size_t)b * p.Hq + h) * T * D;
-    const bf16* abase = p.da + ((size_t)b * T * p.Hq + h) * D;
-    for (int qt = qt_lo; qt <= qt_hi; ++qt) {
-      const int i0 = qt * kQB;
-      for (int c = tid; c < kQB * (D / 8); c += kT) {
-        const int r = c / (D / 8), dc = c % (D / 8);
-        const int qi = min(i0 + r, T - 1);
-        *(u32x4*)(sQ + r * RW + dc * 8) = *(const u32x4*)(qbase + (size_t)qi * D + dc * 8);
-        *(u32x4*)(sA + r * RW + dc * 8) =
-            *(const u32x4*)(abase + (size_t)qi * p.Hq * D + dc * 8);
-      }
-      if (tid < kQB) {
-        const int qi = min(i0 + tid, T - 1);
-        sL[tid] = p.lse[((size_t)b * p.Hq + h) * T + qi];
-        sD[tid] = p.dsum[((size_t)b * p.Hq + h) * T + qi];
-      }
-      __syncthreads();
-      for (int c = tid; c < D * kQB; c += kT) {
-        const int dd = c / kQB, s = c % kQB;
-        sQT[dd * TW + s] = sQ[slot_row(s) * RW + dd];
-        sAT[dd * TW + s] = sA[slot_row(s) * RW + dd];
-      }
-      __syncthreads();
-      f32x16 s, dp;
+  const int n_q = qt_hi - qt_lo + 1;
+  const int n_it = G * n_q;             // (head of the group, query tile) pairs
+
+  int roff[KS], toff[4];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = 0.f;
-        dp[r] = 0.f;
-      }
+  for (int ks = 0; ks < KS; ++ks) roff[ks] = l32 * RB + chunk_pos<D / 8>(l32, 2 * ks + hi) * 16;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s = mfma32(*(const bf16x8*)(sQ + (qh * 32 + l32) * RW + ks * 16 + hi * 8), kreg[ks], s);
-        dp = mfma32(*(const bf16x8*)(sA + (qh * 32 + l32) * RW + ks * 16 + hi * 8), vreg[ks], dp);
-      }
+  for (int x = 0; x < 4; ++x) toff[x] = l32 * 128 + chunk_pos<8>(l32, 2 * x + hi) * 16;
+
+  // tile `it` into buffer `buf`: DMA of the four tiles; the row statistics go through
+  // registers (lsr, dsr), written into the buffer by `put_stats` at the end of the step
+  float lsr = 0.f, dsr = 0.f;
+  auto fetch = [&](int it, int buf) {
+    const int hg = it / n_q, qt = qt_lo + it % n_q;
+    const int h = kvh * G + hg, i0 = qt * kQB;
+    const uint32_t dst = lds0 + buf * BUF;
+    const bf16* qbase = p.qt + (((size_t)b * p.Hq + h) * T + i0) * D;
+    const bf16* abase = p.da + (((size_t)b * T + i0) * p.Hq + h) * D;
+    const size_t tb = (((size_t)b * p.Hq + h) * n64 + qt) * (size_t)(kQB * D);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qr = qh * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        const int qi = i0 + qr;
-        const bool vis = key < T && qi < T && key <= qi && (!SWA || key > qi - p.window);
-        const float pr = vis ? fast_exp2(s[r] * p.qscale - sL[qr]) : 0.f;
-        s[r] = pr;
-        dp[r] = pr * (dp[r] - sD[qr]);              // dS
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const bf16x8 pp = pack8(s, j), dd = pack8(dp, j);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int off = (db * 32 + l32) * TW + qh * 32 + 16 * j + hi * 8;
-          dvt[db] = mfma32(*(const bf16x8*)(sAT + off), pp, dvt[db]);
-          dkt[db] = mfma32(*(const bf16x8*)(sQT + off), dd, dkt[db]);
-        }
-      }
-      __syncthreads();
+    for (int j = 0; j < KPW; ++j) {
+      constexpr int CPR = D / 8, RPB = 1024 / RB;
+      const int blk = wave * KPW + j;
+      const int r = blk * RPB + lane / CPR;
+      const int c = chunk_pos<CPR>(r, lane % CPR);
+      const int rr = min(r, T - 1 - i0);
+      dma16(qbase, (uint32_t)(rr * RB + c * 16), dst + blk * 1024);
+      dma16(abase, (uint32_t)(rr * p.Hq * RB + c * 16), dst + TILE + blk * 1024);
+      const int d = blk * 8 + (lane >> 3);
+      const int c8 = chunk_pos<8>(d, lane & 7);
+      dma16(p.qtT + tb, (uint32_t)(d * 128 + c8 * 16), dst + 2 * TILE + blk * 1024);
+      dma16(p.daT + tb, (uint32_t)(d * 128 + c8 * 16), dst + 3 * TILE + blk * 1024);
     }
+    if (tid < kQB) {
+      const size_t si = ((size_t)b * p.Hq + h) * T + min(i0 + tid, T - 1);
+      lsr = p.lse[si];
+      dsr = p.dsum[si];
+    }
+  };
+  auto put_stats = [&](int buf) {
+    if (tid < kQB) {
+      float* st = (float*)(smem + buf * BUF + 4 * TILE);
+      st[tid] = lsr;
+      st[kQB + tid] = dsr;
+    }
+  };
+
+  fetch(0, 0);
+  put_stats(0);
+  vm_wait<0>();
+  __syncthreads();
+  int cur = 0;
+  for (int it = 0; it < n_it; ++it) {
+    const int nxt = cur ^ 1;
+    fetch(min(it + 1, n_it - 1), nxt);
+    const char* tb = smem + cur * BUF;
+    const float* sL = (const float*)(tb + 4 * TILE);
+    const float* sD = sL + kQB;
+    const int i0 = (qt_lo + it % n_q) * kQB;
+    f32x16 s, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[r] = 0.f;
+      dp[r] = 0.f;
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s = mfma32(*(const bf16x8*)(tb + roff[ks] + qh * 32 * RB), kreg[ks], s);
+      dp = mfma32(*(const bf16x8*)(tb + TILE + roff[ks] + qh * 32 * RB), vreg[ks], dp);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qr = qh * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+      const int qi = i0 + qr;
+      const bool vis = key < T && qi < T && key <= qi && (!SWA || key > qi - p.window);
+      const float pr = vis ? fast_exp2(s[r] * p.qscale - sL[qr]) : 0.f;
+      s[r] = pr;
+      dp[r] = pr * (dp[r] - sD[qr]);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const bf16x8 pp = pack8(s, j), dd = pack8(dp, j);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int off = toff[2 * qh + j] + db * 32 * 128;
+        dvt[db] = mfma32(*(const bf16x8*)(tb + 3 * TILE + off), pp, dvt[db]);
+        dkt[db] = mfma32(*(const bf16x8*)(tb + 2 * TILE + off), dd, dkt[db]);
+      }
+    }
+    put_stats(nxt);
+    vm_wait<0>();
+    __syncthreads();
+    cur = nxt;
   }
   // the two query halves of each key block: qh 1 hands its sums to qh 0 through LDS
   float* red = (float*)smem;               // [2 kb][DB][2][16][64]
@@ -424,96 +528,127 @@ __global__ __launch_bounds__(kT) void bwd_dkdv_kernel(const BArgs p) {
 }
 
 // ---- norm/RoPE backward: dx~ -> dx and per-block weight partials ------------------------
+// 16 lanes per row (8 dims each), 16 rows per pass, grid-stride over the rows; the rotated
+// pair partners are exchanged through LDS. Each workgroup leaves one partial of the
+// weight gradient (sum over its rows of u * x^, u = R^T dx~).
 struct NArgs {
   const bf16* x;       // raw q or k [B][T][H][D]
   const float* w;
   const float* dxt;    // dx~ [B][T][H][D] fp32
   bf16* dx;            // [B][T][H][D]
-  float* part;         // [n_blocks][D] sum over the block's rows of u * x^
+  float* part;         // [gridDim.x][D]
   int B, T, H, rdim, pos_offset;
   float eps;
   RopeFreq fr;
 };
+constexpr int kNormBlocks = 1024;
 
 template <int D>
-__global__ __launch_bounds__(kNormRows) void bwd_norm_rope_kernel(const NArgs p) {
-  constexpr int RS = D + 1;
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  float* xs = (float*)smem;                 // [rows][RS]
-  float* us = xs + kNormRows * RS;          // [rows][RS]
+__global__ __launch_bounds__(kT) void bwd_norm_rope_kernel(const NArgs p) {
+  constexpr int LPR = D / 8;                 // lanes per row
+  constexpr int RPP = kT / LPR;              // rows per pass
+  __shared__ float su[RPP][D + 4];
+  __shared__ float sw[RPP][D];               // column partials at the end
   const int t = threadIdx.x;
+  const int rl = t / LPR, sub = t % LPR;     // row slot, lane in the row
+  const int half = p.rdim >> 1;
   const int64_t n_rows = (int64_t)p.B * p.T * p.H;
-  const int64_t r0 = (int64_t)blockIdx.x * kNormRows;
-  for (int c = t; c < kNormRows * D; c += kNormRows) {
-    const int rr = c / D, cc = c % D;
-    const int64_t row = r0 + rr;
-    xs[rr * RS + cc] = row < n_rows ? (float)p.x[row * D + cc] : 0.f;
-    us[rr * RS + cc] = row < n_rows ? p.dxt[row * D + cc] : 0.f;
+  float wv[8], acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    wv[e] = p.w[sub * 8 + e];
+    acc[e] = 0.f;
   }
-  __syncthreads();
-  {
-    const int64_t row = r0 + t;
-    float* x = xs + t * RS;
-    float* u = us + t * RS;
-    if (row < n_rows) {
-      const int pos = p.pos_offset + (int)((row / p.H) % p.T);
-      float ss = 0.f;
-      for (int c = 0; c < D; ++c) ss = __builtin_fmaf(x[c], x[c], ss);
-      const float rn = 1.0f / sqrtf(ss / D + p.eps);
-      // u = R^T dx~ (rotate each pair back)
-      const int half = p.rdim >> 1;
-      for (int j = 0; j < half; ++j) {
+  for (int64_t r0 = (int64_t)blockIdx.x * RPP; r0 < n_rows; r0 += (int64_t)gridDim.x * RPP) {
+    const int64_t row = r0 + rl;
+    const bool ok = row < n_rows;
+    const int64_t rc = ok ? row : n_rows - 1;
+    float x[8], g[8];
+    {
+      const u32x4 xw = *(const u32x4*)(p.x + rc * D + sub * 8);
+      const uint32_t x4[4] = {xw.x, xw.y, xw.z, xw.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[2 * e] = bf16_lo_to_f32(x4[e]);
+        x[2 * e + 1] = bf16_hi_to_f32(x4[e]);
+      }
+      const float4 g0 = *(const float4*)(p.dxt + rc * D + sub * 8);
+      const float4 g1 = *(const float4*)(p.dxt + rc * D + sub * 8 + 4);
+      g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w;
+      g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
+#pragma unroll
+    for (int o = 1; o < LPR; o <<= 1) ss += __shfl_xor(ss, o);
+    const float rn = 1.0f / sqrtf(ss / D + p.eps);
+    // u = R^T dx~: pair (j, j + half) for j < half
+    __syncthreads();   // su free (previous pass done)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) su[rl][sub * 8 + e] = g[e];
+    __syncthreads();
+    const int pos = p.pos_offset + (int)((rc / p.H) % p.T);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int c = sub * 8 + e;
+      if (c < p.rdim) {
+        const int j = c < half ? c : c - half;
         float cs, sn;
         rope_cos_sin(pos, p.fr.hi[j], p.fr.lo[j], cs, sn);
-        const float ga = u[j], gb = u[j + half];
-        u[j] = ga * cs + gb * sn;
-        u[j + half] = gb * cs - ga * sn;
-      }
-      float dot = 0.f;
-      for (int c = 0; c < D; ++c) {
-        const float xh = x[c] * rn;
-        const float dxh = u[c] * p.w[c];
-        dot = __builtin_fmaf(dxh, xh, dot);
-        u[c] = u[c] * xh;                  // weight-gradient contribution of this row
-        x[c] = dxh;                        // keep dx^ (x^ is recomputed below)
-      }
-      dot *= 1.0f / D;
-      for (int c = 0; c < D; ++c) {
-        const float xh = (float)p.x[row * D + c] * rn;
-        x[c] = rn * (x[c] - xh * dot);     // dx
-      }
-    } else {
-      for (int c = 0; c < D; ++c) {
-        x[c] = 0.f;
-        u[c] = 0.f;
+        const float partner = su[rl][c < half ? c + half : c - half];
+        g[e] = c < half ? g[e] * cs + partner * sn : g[e] * cs - partner * sn;
       }
     }
+    float dot = 0.f, xh[8], dxh[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      xh[e] = x[e] * rn;
+      dxh[e] = g[e] * wv[e];
+      dot = __builtin_fmaf(dxh[e], xh[e], dot);
+      if (ok) acc[e] = __builtin_fmaf(g[e], xh[e], acc[e]);
+    }
+#pragma unroll
+    for (int o = 1; o < LPR; o <<= 1) dot += __shfl_xor(dot, o);
+    dot *= 1.0f / D;
+    if (ok) {
+      bf16x8 o8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o8[e] = (bf16)(rn * (dxh[e] - xh[e] * dot));
+      *(bf16x8*)(p.dx + row * D + sub * 8) = o8;
+    }
   }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sw[rl][sub * 8 + e] = acc[e];
   __syncthreads();
-  for (int c = t; c < kNormRows * D; c += kNormRows) {
-    const int rr = c / D, cc = c % D;
-    const int64_t row = r0 + rr;
-    if (row < n_rows) p.dx[row * D + cc] = (bf16)xs[rr * RS + cc];
-  }
-  for (int c = t; c < D; c += kNormRows) {
-    float s = 0.f;
-    for (int rr = 0; rr < kNormRows; ++rr) s += us[rr * RS + c];
-    p.part[(size_t)blockIdx.x * D + c] = s;
+  for (int c = t; c < D; c += kT) {
+    float sacc = 0.f;
+    for (int r = 0; r < RPP; ++r) sacc += sw[r][c];
+    p.part[(size_t)blockIdx.x * D + c] = sacc;
   }
 }
 
+// dw[c] = sum over the n partials: one workgroup per column
 template <int D>
-__global__ __launch_bounds__(D) void bwd_dw_reduce_kernel(const float* part, int n, float* dw) {
-  const int c = threadIdx.x;
+__global__ __launch_bounds__(kT) void bwd_dw_reduce_kernel(const float* part, int n, float* dw) {
+  __shared__ float red[kT / 64];
+  const int c = blockIdx.x;
   float s = 0.f;
-  for (int i = 0; i < n; ++i) s += part[(size_t)i * D + c];
-  dw[c] = s;
+  for (int i = threadIdx.x; i < n; i += kT) s += part[(size_t)i * D + c];
+  s = wave_sum(s);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float tot = 0.f;
+    for (int i = 0; i < kT / 64; ++i) tot += red[i];
+    dw[c] = tot;
+  }
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t qt, kt, da, dsum, lse, dqt, dkt, part, total;
+  size_t qt, kt, da, dsum, lse, dqt, dkt, part, qtT, daT, ktT, total;
   int nq_blk, nk_blk;
 };
 
@@ -528,9 +663,13 @@ WsLayout ws_layout(int B, int T, int Hq, int Hkv, int d) {
   L.lse = o;  o += align256(nq * 4);
   L.dqt = o;  o += align256(nq * d * 4);
   L.dkt = o;  o += align256(nk * d * 4);
-  L.nq_blk = (int)((nq + kNormRows - 1) / kNormRows);
-  L.nk_blk = (int)((nk + kNormRows - 1) / kNormRows);
+  L.nq_blk = kNormBlocks;
+  L.nk_blk = kNormBlocks;
   L.part = o; o += align256((size_t)(L.nq_blk + L.nk_blk) * d * 4);
+  const size_t n64 = (size_t)(T + 63) / 64;
+  L.qtT = o;  o += align256((size_t)B * Hq * n64 * 64 * d * 2);
+  L.daT = o;  o += align256((size_t)B * Hq * n64 * 64 * d * 2);
+  L.ktT = o;  o += align256((size_t)B * Hkv * n64 * 64 * d * 2);
   L.total = o;
   return L;
 }
@@ -610,16 +749,33 @@ hipError_t backward_t(const BackwardArgs& a, hipStream_t s) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
+  // transposed tiles of K~, Q~ and dA (slot order) for the operands taken along positions
+  const int n64 = (a.T + 63) / 64;
+  p.ktT = (const bf16*)(ws + L.ktT);
+  p.qtT = (const bf16*)(ws + L.qtT);
+  p.daT = (const bf16*)(ws + L.daT);
+  hipLaunchKernelGGL(bwd_tiles_kernel<D>, dim3(n64, a.B * a.Hkv), dim3(kT), 0, s, p.kt,
+                     (int64_t)a.Hkv * a.T * D, (int64_t)a.T * D, (int64_t)D, a.Hkv, a.T, n64,
+                     (bf16*)(ws + L.ktT));
+  hipLaunchKernelGGL(bwd_tiles_kernel<D>, dim3(n64, a.B * a.Hq), dim3(kT), 0, s, p.qt,
+                     (int64_t)a.Hq * a.T * D, (int64_t)a.T * D, (int64_t)D, a.Hq, a.T, n64,
+                     (bf16*)(ws + L.qtT));
+  hipLaunchKernelGGL(bwd_tiles_kernel<D>, dim3(n64, a.B * a.Hq), dim3(kT), 0, s,
+                     (const bf16*)p.da, (int64_t)a.T * a.Hq * D, (int64_t)D,
+                     (int64_t)a.Hq * D, a.Hq, a.T, n64, (bf16*)(ws + L.daT));
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
   const int bmp = kRowsDQ / p.group;
   const int n_qt = (a.T + bmp - 1) / bmp;
-  const int dq_smem = (2 * kKB * (D + 8) + D * (kKB + 8)) * 2;
+  const int dq_smem = (kDQAhead + 1) * 3 * kKB * D * 2;
   const dim3 gq((unsigned)(n_qt * a.B * a.Hkv));
   e = a.swa ? launch_big(bwd_dq_kernel<D, true>, gq, dim3(kT), dq_smem, s, p)
             : launch_big(bwd_dq_kernel<D, false>, gq, dim3(kT), dq_smem, s, p);
   if (e != hipSuccess) return e;
 
   const int n_kt = (a.T + kKB - 1) / kKB;
-  const int stage = (2 * kQB * (D + 8) + 2 * D * (kQB + 8)) * 2 + 2 * kQB * 4;
+  const int stage = 2 * (4 * kQB * D * 2 + 2 * kQB * 4);
   const int red = 2 * (D / 32) * 2 * 16 * 64 * 4;
   const int kv_smem = stage > red ? stage : red;
   const dim3 gk((unsigned)(n_kt * a.B * a.Hkv));
@@ -634,7 +790,6 @@ hipError_t backward_t(const BackwardArgs& a, hipStream_t s) {
   nb.pos_offset = a.pos_offset;
   nb.eps = a.eps;
   nb.fr = a.fr;
-  const int nsm = 2 * kNormRows * (D + 1) * 4;
   float* part = (float*)(ws + L.part);
   nb.x = (const bf16*)a.q;
   nb.w = a.wq;
@@ -642,19 +797,17 @@ hipError_t backward_t(const BackwardArgs& a, hipStream_t s) {
   nb.dx = (bf16*)a.dq;
   nb.part = part;
   nb.H = a.Hq;
-  e = launch_big(bwd_norm_rope_kernel<D>, dim3(L.nq_blk), dim3(kNormRows), nsm, s, nb);
-  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_norm_rope_kernel<D>, dim3(L.nq_blk), dim3(kT), 0, s, nb);
   nb.x = (const bf16*)a.k;
   nb.w = a.wk;
   nb.dxt = p.dkt;
   nb.dx = (bf16*)a.dk;
   nb.part = part + (size_t)L.nq_blk * D;
   nb.H = a.Hkv;
-  e = launch_big(bwd_norm_rope_kernel<D>, dim3(L.nk_blk), dim3(kNormRows), nsm, s, nb);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dw_reduce_kernel<D>, dim3(1), dim3(D), 0, s, (const float*)part,
+  hipLaunchKernelGGL(bwd_norm_rope_kernel<D>, dim3(L.nk_blk), dim3(kT), 0, s, nb);
+  hipLaunchKernelGGL(bwd_dw_reduce_kernel<D>, dim3(D), dim3(kT), 0, s, (const float*)part,
                      L.nq_blk, a.dwq);
-  hipLaunchKernelGGL(bwd_dw_reduce_kernel<D>, dim3(1), dim3(D), 0, s,
+  hipLaunchKernelGGL(bwd_dw_reduce_kernel<D>, dim3(D), dim3(kT), 0, s,
                      (const float*)(part + (size_t)L.nq_blk * D), L.nk_blk, a.dwk);
   return hipGetLastError();
 }

@@ -135,37 +135,6 @@ __device__ __forceinline__ void set_prio() {
 // mixed register class).
 __device__ __forceinline__ void pin_agpr(f32x16& v) { asm volatile("" : "+a"(v)); }
 
-// Position of 16-byte chunk c within row r of an unpadded LDS tile with CPR (16 or 8)
-// chunks per row. The XOR swizzle sends the 16 consecutive rows read by one operand load
-// (same chunk) to 16 distinct 16-byte bank groups, and any 8 of them to distinct groups
-// of a 128-byte bank row, so the reads are conflict-free with 32 or 64 banks.
-template <int CPR>
-__device__ __forceinline__ int chunk_pos(int r, int c) {
-  return c ^ (CPR == 16 ? (r & 15) : ((r & 7) ^ ((r >> 3) & 1)));
-}
-
-// LDS DMA of 16 bytes per lane: lane L's bytes from gbase + voff land at LDS byte
-// address lds + 16 L. gbase and lds must be wave-uniform (scalar base, M0). Completion is counted by vmcnt
-// and left to the caller (vm_wait): the compiler does not see these loads and inserts
-// no wait for them. One wait state separates the M0 write from the DMA that reads it.
-__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds) {
-  // (readfirstlane returns int: each half goes through uint32_t so that it is
-  // zero-extended, never sign-extended, into the 64-bit address)
-  const uint64_t g = (uint64_t)(uintptr_t)gbase;
-  const uint32_t glo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)g);
-  const uint32_t ghi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(g >> 32));
-  const uint64_t gu = ((uint64_t)ghi << 32) | (uint64_t)glo;
-  const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :: "s"(m0), "v"(voff), "s"(gu) : "memory", "m0");
-}
-// Wait until at most N vector-memory operations of this wave are outstanding (they
-// complete in issue order).
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
-}
-
 // Wait states between the last MFMA that wrote the accumulators and any other access.
 template <int QB, int DB>
 __device__ __forceinline__ void acc_fence(f32x16 (&o)[QB][DB]) {

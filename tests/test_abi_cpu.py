@@ -179,9 +179,10 @@ def test_backward_checks():
     need = lib.zgattn_prefill_backward_workspace_bytes(ctypes.byref(d))
     nq, nk = 2 * 300 * 8, 2 * 300 * 2
     a256 = lambda x: (x + 255) // 256 * 256
-    nb = lambda n: (n + 63) // 64
+    n64 = (300 + 63) // 64
     assert need == (a256(nq * 128 * 2) + a256(nk * 128 * 2) + a256(nq * 128 * 2) + 2 * a256(nq * 4)
-                    + a256(nq * 128 * 4) + a256(nk * 128 * 4) + a256((nb(nq) + nb(nk)) * 128 * 4))
+                    + a256(nq * 128 * 4) + a256(nk * 128 * 4) + a256(2 * 1024 * 128 * 4)
+                    + 2 * a256(2 * 8 * n64 * 64 * 128 * 2) + a256(2 * 2 * n64 * 64 * 128 * 2))
     call = lambda **kw: lib.zgattn_swa_prefill_backward(
         ctypes.byref(kw.get("d", d)), FAKE, FAKE, FAKE, kw.get("g", FAKE), FAKE, FAKE, FAKE,
         kw.get("dout", FAKE), FAKE, FAKE, FAKE, kw.get("dg", FAKE), FAKE, FAKE,
