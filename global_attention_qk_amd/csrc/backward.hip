@@ -351,30 +351,38 @@ __global__ __launch_bounds__(kT) void bwd_dq_kernel(const BArgs p) {
   }
 }
 
-// ---- dK, dV: one workgroup per (batch, KV head, 64 keys) --------------------------------
-// A query-tile buffer holds Q~ rows [64][D], dA rows [64][D], Q~^T and dA^T [D][64] (all
-// unpadded, swizzled, filled by LDS DMA one tile ahead) and the tile's log-sum-exp and D.
+// ---- dK, dV: one workgroup per (batch, KV head, 128 keys) -------------------------------
+// Eight waves: wave w owns keys 32 (w % 4) .. of the workgroup and half of the head dims
+// (w / 4) of their dK / dV. Every query tile streamed through LDS (Q~ rows, dA rows,
+// Q~^T and dA^T tiles, unpadded and swizzled, fetched by LDS DMA one tile ahead, and the
+// tile's log-sum-exp and D) thus serves 128 keys; the two waves of a key block both form
+// S and dP (over all head dims), which costs a third more MFMA work than splitting the
+// queries but halves the bytes streamed per key, the bound of this kernel.
+constexpr int kKV = 128;           // keys per dK/dV workgroup
+constexpr int kTKV = 512;          // its threads
+
 template <int D, bool SWA>
-__global__ __launch_bounds__(kT) void bwd_dkdv_kernel(const BArgs p) {
+__global__ __launch_bounds__(kTKV) void bwd_dkdv_kernel(const BArgs p) {
   constexpr int KS = D / 16;
-  constexpr int DB = D / 32;
+  constexpr int DBH = D / 64;              // 32-row d blocks per wave (half the dims)
   constexpr int RB = D * 2;
   constexpr int TILE = kQB * RB;
   constexpr int BUF = 4 * TILE + 2 * kQB * 4;
-  constexpr int KPW = D / 32;
+  constexpr int DPW = TILE / 1024 / 8;     // DMA blocks per wave per tile
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
-  const int kb = wave & 1, qh = wave >> 1;
+  const int kb = wave & 3, dh = wave >> 2;
   const int T = p.T, G = p.group;
   const int n64 = (T + 63) / 64;
-  const int kt = blockIdx.x % n64;
-  const int hb = blockIdx.x / n64;
+  const int nkt = (T + kKV - 1) / kKV;
+  const int kt = blockIdx.x % nkt;
+  const int hb = blockIdx.x / nkt;
   const int b = hb / p.Hkv, kvh = hb % p.Hkv;
-  const int k0 = kt * kKB;
+  const int k0 = kt * kKV;
   const int key = k0 + kb * 32 + l32;
   const int kc = min(key, T - 1);
 
@@ -388,20 +396,20 @@ __global__ __launch_bounds__(kT) void bwd_dkdv_kernel(const BArgs p) {
       vreg[ks] = *(const bf16x8*)(vrow + ks * 16 + hi * 8);
     }
   }
-  f32x16 dvt[DB], dkt[DB];
+  f32x16 dvt[DBH], dkt[DBH];
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int db = 0; db < DBH; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       dvt[db][r] = 0.f;
       dkt[db][r] = 0.f;
     }
 
-  const int k_last = min(k0 + kKB, T) - 1;
+  const int k_last = min(k0 + kKV, T) - 1;
   const int q_hi = SWA ? min(T - 1, k_last + p.window - 1) : T - 1;
   const int qt_lo = k0 / kQB, qt_hi = q_hi / kQB;
   const int n_q = qt_hi - qt_lo + 1;
-  const int n_it = G * n_q;             // (head of the group, query tile) pairs
+  const int n_it = G * n_q;             // (head of the group, query tile) steps
 
   int roff[KS], toff[4];
 #pragma unroll
@@ -409,8 +417,8 @@ __global__ __launch_bounds__(kT) void bwd_dkdv_kernel(const BArgs p) {
 #pragma unroll
   for (int x = 0; x < 4; ++x) toff[x] = l32 * 128 + chunk_pos<8>(l32, 2 * x + hi) * 16;
 
-  // tile `it` into buffer `buf`: DMA of the four tiles; the row statistics go through
-  // registers (lsr, dsr), written into the buffer by `put_stats` at the end of the step
+  // step `it` into buffer `buf`: DMA of the four tiles; the row statistics go through
+  // registers (lsr, dsr), written into the buffer by put_stats at the end of the step
   float lsr = 0.f, dsr = 0.f;
   auto fetch = [&](int it, int buf) {
     const int hg = it / n_q, qt = qt_lo + it % n_q;
@@ -420,9 +428,9 @@ __global__ __launch_bounds__(kT) void bwd_dkdv_kernel(const BArgs p) {
     const bf16* abase = p.da + (((size_t)b * T + i0) * p.Hq + h) * D;
     const size_t tb = (((size_t)b * p.Hq + h) * n64 + qt) * (size_t)(kQB * D);
 #pragma unroll
-    for (int j = 0; j < KPW; ++j) {
+    for (int j = 0; j < DPW; ++j) {
       constexpr int CPR = D / 8, RPB = 1024 / RB;
-      const int blk = wave * KPW + j;
+      const int blk = wave * DPW + j;
       const int r = blk * RPB + lane / CPR;
       const int c = chunk_pos<CPR>(r, lane % CPR);
       const int rr = min(r, T - 1 - i0);
@@ -459,34 +467,37 @@ __global__ __launch_bounds__(kT) void bwd_dkdv_kernel(const BArgs p) {
     const float* sL = (const float*)(tb + 4 * TILE);
     const float* sD = sL + kQB;
     const int i0 = (qt_lo + it % n_q) * kQB;
-    f32x16 s, dp;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s[r] = 0.f;
-      dp[r] = 0.f;
-    }
+    for (int qb = 0; qb < 2; ++qb) {
+      f32x16 s, dp;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      s = mfma32(*(const bf16x8*)(tb + roff[ks] + qh * 32 * RB), kreg[ks], s);
-      dp = mfma32(*(const bf16x8*)(tb + TILE + roff[ks] + qh * 32 * RB), vreg[ks], dp);
-    }
+      for (int r = 0; r < 16; ++r) {
+        s[r] = 0.f;
+        dp[r] = 0.f;
+      }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int qr = qh * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-      const int qi = i0 + qr;
-      const bool vis = key < T && qi < T && key <= qi && (!SWA || key > qi - p.window);
-      const float pr = vis ? fast_exp2(s[r] * p.qscale - sL[qr]) : 0.f;
-      s[r] = pr;
-      dp[r] = pr * (dp[r] - sD[qr]);
-    }
+      for (int ks = 0; ks < KS; ++ks) {
+        s = mfma32(*(const bf16x8*)(tb + roff[ks] + qb * 32 * RB), kreg[ks], s);
+        dp = mfma32(*(const bf16x8*)(tb + TILE + roff[ks] + qb * 32 * RB), vreg[ks], dp);
+      }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const bf16x8 pp = pack8(s, j), dd = pack8(dp, j);
+      for (int r = 0; r < 16; ++r) {
+        const int qr = qb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        const int qi = i0 + qr;
+        const bool vis = key < T && qi < T && key <= qi && (!SWA || key > qi - p.window);
+        const float pr = vis ? fast_exp2(s[r] * p.qscale - sL[qr]) : 0.f;
+        s[r] = pr;
+        dp[r] = pr * (dp[r] - sD[qr]);
+      }
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int off = toff[2 * qh + j] + db * 32 * 128;
-        dvt[db] = mfma32(*(const bf16x8*)(tb + 3 * TILE + off), pp, dvt[db]);
-        dkt[db] = mfma32(*(const bf16x8*)(tb + 2 * TILE + off), dd, dkt[db]);
+      for (int j = 0; j < 2; ++j) {
+        const bf16x8 pp = pack8(s, j), dd = pack8(dp, j);
+#pragma unroll
+        for (int db = 0; db < DBH; ++db) {
+          const int off = toff[2 * qb + j] + (dh * DBH + db) * 32 * 128;
+          dvt[db] = mfma32(*(const bf16x8*)(tb + 3 * TILE + off), pp, dvt[db]);
+          dkt[db] = mfma32(*(const bf16x8*)(tb + 2 * TILE + off), dd, dkt[db]);
+        }
       }
     }
     put_stats(nxt);
@@ -494,35 +505,19 @@ __global__ __launch_bounds__(kT) void bwd_dkdv_kernel(const BArgs p) {
     __syncthreads();
     cur = nxt;
   }
-  // the two query halves of each key block: qh 1 hands its sums to qh 0 through LDS
-  float* red = (float*)smem;               // [2 kb][DB][2][16][64]
-  if (qh == 1) {
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        red[(((kb * DB + db) * 2 + 0) * 16 + r) * 64 + lane] = dvt[db][r];
-        red[(((kb * DB + db) * 2 + 1) * 16 + r) * 64 + lane] = dkt[db][r];
-      }
-  }
-  __syncthreads();
-  if (qh == 0 && key < T) {
+  if (key < T) {
     bf16* vdst = p.dv + (((size_t)b * T + key) * p.Hkv + kvh) * D;
     float* kdst = p.dkt + (((size_t)b * T + key) * p.Hkv + kvh) * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DBH; ++db)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        float vv[4], kk[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * r4 + e;
-          vv[e] = dvt[db][r] + red[(((kb * DB + db) * 2 + 0) * 16 + r) * 64 + lane];
-          kk[e] = (dkt[db][r] + red[(((kb * DB + db) * 2 + 1) * 16 + r) * 64 + lane]) * p.scale;
-        }
-        const int d0 = db * 32 + 8 * r4 + 4 * hi;
-        *(bf16x4*)(vdst + d0) = (bf16x4){(bf16)vv[0], (bf16)vv[1], (bf16)vv[2], (bf16)vv[3]};
-        *(float4*)(kdst + d0) = make_float4(kk[0], kk[1], kk[2], kk[3]);
+        const int d0 = (dh * DBH + db) * 32 + 8 * r4 + 4 * hi;
+        const int r = 4 * r4;
+        *(bf16x4*)(vdst + d0) = (bf16x4){(bf16)dvt[db][r], (bf16)dvt[db][r + 1],
+                                         (bf16)dvt[db][r + 2], (bf16)dvt[db][r + 3]};
+        *(float4*)(kdst + d0) = make_float4(dkt[db][r] * p.scale, dkt[db][r + 1] * p.scale,
+                                            dkt[db][r + 2] * p.scale, dkt[db][r + 3] * p.scale);
       }
   }
 }
@@ -774,13 +769,11 @@ hipError_t backward_t(const BackwardArgs& a, hipStream_t s) {
             : launch_big(bwd_dq_kernel<D, false>, gq, dim3(kT), dq_smem, s, p);
   if (e != hipSuccess) return e;
 
-  const int n_kt = (a.T + kKB - 1) / kKB;
-  const int stage = 2 * (4 * kQB * D * 2 + 2 * kQB * 4);
-  const int red = 2 * (D / 32) * 2 * 16 * 64 * 4;
-  const int kv_smem = stage > red ? stage : red;
+  const int n_kt = (a.T + kKV - 1) / kKV;
+  const int kv_smem = 2 * (4 * kQB * D * 2 + 2 * kQB * 4);
   const dim3 gk((unsigned)(n_kt * a.B * a.Hkv));
-  e = a.swa ? launch_big(bwd_dkdv_kernel<D, true>, gk, dim3(kT), kv_smem, s, p)
-            : launch_big(bwd_dkdv_kernel<D, false>, gk, dim3(kT), kv_smem, s, p);
+  e = a.swa ? launch_big(bwd_dkdv_kernel<D, true>, gk, dim3(kTKV), kv_smem, s, p)
+            : launch_big(bwd_dkdv_kernel<D, false>, gk, dim3(kTKV), kv_smem, s, p);
   if (e != hipSuccess) return e;
 
   NArgs nb;
