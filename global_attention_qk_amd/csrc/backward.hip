@@ -26,7 +26,8 @@ namespace {
 constexpr int kT = 256;         // threads per workgroup (4 waves)
 constexpr int kKB = 64;         // keys per tile (dQ) / per workgroup (dK, dV)
 constexpr int kQB = 64;         // queries per tile (dK, dV)
-constexpr int kRowsDQ = 128;    // query rows per dQ workgroup (4 waves x 32)
+constexpr int kRowsDQ = 256;    // query rows per dQ workgroup (8 waves x 32)
+constexpr int kTDQ = 512;       // its threads
 
 // Swap bits 2 and 3 of an index within its 16-group: the order in which a lane-half holds
 // rows of a 32x32 accumulator (rows 8 (r/4) + 4 hi + r%4), used as the k-slot order of the
@@ -149,21 +150,21 @@ __global__ __launch_bounds__(kT) void bwd_tiles_kernel(const bf16* src, int64_t 
   }
 }
 
-// ---- dQ: one workgroup per (batch, KV head, 128 query rows of the group's heads) --------
+// ---- dQ: one workgroup per (batch, KV head, 256 query rows of the group's heads) --------
 // LDS tiles are unpadded and filled by LDS DMA, their 16-byte chunks XOR-swizzled as in
 // the forward kernel (chunk_pos): a key-tile buffer holds K~ rows [64][D], V rows [64][D]
 // and K~^T [D][64]; tiles are fetched kDQAhead tiles ahead into kDQAhead + 1 buffers.
 constexpr int kDQAhead = 2;
 
 template <int D, bool SWA>
-__global__ __launch_bounds__(kT) void bwd_dq_kernel(const BArgs p) {
+__global__ __launch_bounds__(kTDQ) void bwd_dq_kernel(const BArgs p) {
   constexpr int KS = D / 16;             // k-steps over d
   constexpr int DB = D / 32;             // 32-row d blocks
   constexpr int RB = D * 2;              // row bytes
   constexpr int TILE = kKB * RB;         // bytes of one [64][D] (or [D][64]) tile
   constexpr int BUF = 3 * TILE;
   constexpr int NB = kDQAhead + 1;
-  constexpr int KPW = D / 32;            // 1 KiB DMA blocks per wave per tile
+  constexpr int KPW = D / 64;            // 1 KiB DMA blocks per wave per tile
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
 
@@ -765,8 +766,8 @@ hipError_t backward_t(const BackwardArgs& a, hipStream_t s) {
   const int n_qt = (a.T + bmp - 1) / bmp;
   const int dq_smem = (kDQAhead + 1) * 3 * kKB * D * 2;
   const dim3 gq((unsigned)(n_qt * a.B * a.Hkv));
-  e = a.swa ? launch_big(bwd_dq_kernel<D, true>, gq, dim3(kT), dq_smem, s, p)
-            : launch_big(bwd_dq_kernel<D, false>, gq, dim3(kT), dq_smem, s, p);
+  e = a.swa ? launch_big(bwd_dq_kernel<D, true>, gq, dim3(kTDQ), dq_smem, s, p)
+            : launch_big(bwd_dq_kernel<D, false>, gq, dim3(kTDQ), dq_smem, s, p);
   if (e != hipSuccess) return e;
 
   const int n_kt = (a.T + kKV - 1) / kKV;
