@@ -36,6 +36,8 @@ def parse():
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="approximate CPU time budget of the oracle sample")
+    ap.add_argument("--workload", choices=["c4", "c2"], default="c4",
+                    help="prefill shape of --only: c4 = B=1 T=262144 (default), c2 = B=4 T=4096")
     ap.add_argument("--only", choices=["swa_prefill", "global_prefill", "global_decode",
                                        "swa_decode", "copy"], default=None,
                     help="run just this call (warmup + steps launches, for profilers); "
@@ -515,7 +517,9 @@ def run_only(args):
         y = torch.empty_like(x)
         call = lambda: y.copy_(x)
     elif args.only in ("swa_prefill", "global_prefill"):
-        q, k, v, g, wq, wk = prefill_inputs(C4, device=dev, gated=args.only == "swa_prefill")
+        from workloads import C2
+        wl = C2 if args.workload == "c2" else C4
+        q, k, v, g, wq, wk = prefill_inputs(wl, device=dev, gated=args.only == "swa_prefill")
         out = torch.empty_like(q)
         if args.only == "swa_prefill":
             call = lambda: zg.swa_prefill(q, k, v, g, wq, wk, window=W, rotary_dim=r, out=out)

@@ -109,6 +109,20 @@ __device__ __forceinline__ void vm_wait() {
   asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
 
+// Sum over each aligned group of N (2, 4, 8 or 16) lanes, the result in every lane of the
+// group: cross-lane moves within a row of 16 lanes (DPP), no LDS traffic. The pairings
+// (swap neighbours, swap pairs, mirror within 8, mirror within 16) each join two disjoint
+// halves of the group summed so far.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(N == 2 || N == 4 || N == 8 || N == 16, "group of 2..16 lanes");
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+  if (N >= 4) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+  if (N >= 8) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+  if (N >= 16) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
+  return v;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

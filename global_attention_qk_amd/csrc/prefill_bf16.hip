@@ -60,6 +60,7 @@ constexpr int kDmaBufs = ZG_DMA_BUFS;
 #endif
 constexpr int kDmaPhase = ZG_DMA_PHASE;
 constexpr int kBN = 64;           // keys per tile
+constexpr int kXcds = 8;          // accelerator complex dies (one L2 each)
 constexpr int kMaxHalfMfma = 32;  // rotary_dim <= 64 on this path
 constexpr float kStaticShiftMax = 96.0f;  // largest score bound (log2 units) without a max
 
@@ -83,9 +84,10 @@ struct Smem {
   static constexpr int kDBuf = kDK + D * kBN * 2;
   static constexpr int kDLoop = kDmaBufs * kDBuf;
   static constexpr int kW = 2 * D * 4;  // wq, wk
+  static constexpr int kFr = 2 * kMaxHalfMfma * 4;  // RoPE phase steps (head, tail)
   static constexpr int kMain = kLoop > kDLoop ? kLoop : kDLoop;
   static constexpr int kUnion = (kQ + kQtrig) > kMain ? (kQ + kQtrig) : kMain;
-  static constexpr int kTotal = kUnion + kW;
+  static constexpr int kTotal = kUnion + kW + kFr;
 };
 
 struct KArgs {
@@ -206,6 +208,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
   float2* sKtrig = (float2*)(smem + 2 * S::kBuf + S::kKraw);
   float* sWq = (float*)(smem + S::kUnion);
   float* sWk = sWq + D;
+  float* sFr = sWk + D;   // [0, 32): phase step heads, [32, 64): tails
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -216,6 +219,11 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
   for (int i = tid; i < D; i += kThreads) {
     sWq[i] = p.wq[i];
     sWk[i] = p.wk[i];
+  }
+  // (a lane-dependent index into the kernel arguments would be a memory load per use)
+  for (int i = tid; i < kMaxHalfMfma; i += kThreads) {
+    sFr[i] = p.fr.hi[i];
+    sFr[kMaxHalfMfma + i] = p.fr.lo[i];
   }
   __syncthreads();
   // ---- Score bound and variant selection (uniform over the grid) ---------------------
@@ -235,11 +243,19 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
     if (use_static != STATIC) return;
   }
 
-  // Heavy query tiles first (global layers); consecutive workgroups cover different
-  // (batch, kv-head) pairs so that one pair's tiles share an XCD's L2.
+  // Heavy query tiles first (global layers). Workgroup i runs on XCD i % 8 (round-robin
+  // dispatch); when the (batch, kv-head) pairs divide evenly, each XCD takes its pairs one
+  // after another, so that its L2 holds the K~ / V tiles of one or two pairs at a time.
   const int lin = blockIdx.x;
-  const int hb = lin % p.n_hb;
-  const int tile_rank = lin / p.n_hb;
+  int hb, tile_rank;
+  if (p.n_hb % kXcds == 0) {
+    const int x = lin % kXcds, slot = lin / kXcds;
+    hb = (slot / p.n_qtiles) * kXcds + x;
+    tile_rank = slot % p.n_qtiles;
+  } else {
+    hb = lin % p.n_hb;
+    tile_rank = lin / p.n_hb;
+  }
   const int b = hb / p.Hkv;        // batch element, or document of a packed batch
   const int kvh = hb % p.Hkv;
   // Sequence of this workgroup: `seq0` is its first row in the [B*T] (or packed) token
@@ -263,49 +279,95 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
   const int half = p.rdim >> 1;
   const int bpp = p.bmp >> 5;  // 32-row blocks per head in the tile
 
-  // ---- Phase 1: Q tile -> LDS (coalesced), trig table for its positions -------------
+  // ---- Phase 1: Q tile -> LDS, QK-norm + RoPE + scale in place ----------------------
+  // The tile is bmp * group = kRows rows of DC 16-byte chunks. Thread t always holds chunk
+  // dc = t % DC (kThreads is a multiple of DC) of rows qrow[it], so its 8 weights and the
+  // RoPE partners of its 8 dims are fixed; the DC lanes holding one row sum its squares
+  // with shuffles. All loads are issued before the first LDS write.
   {
+    constexpr int QIT = kRows * DC / kThreads;
+    static_assert(QIT * kThreads == kRows * DC && kThreads % DC == 0, "Q chunks per thread");
     const int g = p.group;
     const int chunks_per_pos = g * DC;
-    const int n_chunks = p.bmp * chunks_per_pos;
+    const int dc = tid % DC;
     const bf16* qbase = p.q + (seq0 * p.Hq + (size_t)kvh * g) * D;
-    for (int c = tid; c < n_chunks; c += kThreads) {
+    u32x4 qv[QIT];
+    int qrow[QIT], qpi[QIT];
+#pragma unroll
+    for (int it = 0; it < QIT; ++it) {
+      const int c = tid + it * kThreads;
       const int pi = c / chunks_per_pos;
-      const int rem = c - pi * chunks_per_pos;
-      const int hg = rem / DC;
-      const int dc = rem - hg * DC;
-      const int pos = i0 + pi;
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if (pos < T) val = *(const u32x4*)(qbase + (size_t)pos * p.Hq * D + hg * D + dc * 8);
-      *(u32x4*)(sQ + (hg * p.bmp + pi) * RW + dc * 8) = val;
+      const int hg = (c - pi * chunks_per_pos) / DC;
+      const int pos = min(i0 + pi, T - 1);   // rows past the end read a valid row, then zero
+      qv[it] = *(const u32x4*)(qbase + (size_t)pos * p.Hq * D + hg * D + dc * 8);
+      qrow[it] = hg * p.bmp + pi;
+      qpi[it] = pi;
     }
     for (int e = tid; e < p.bmp * half; e += kThreads) {
       const int pi = e / half, j = e - pi * half;
       float c, s;
-      rope_cos_sin(p.pos_offset + i0 + pi, p.fr.hi[j], p.fr.lo[j], c, s);
+      rope_cos_sin(p.pos_offset + i0 + pi, sFr[j], sFr[kMaxHalfMfma + j], c, s);
       sQtrig[pi * kMaxHalfMfma + j] = make_float2(c, s);
     }
-  }
-  __syncthreads();
-  // Thread-per-row RMSNorm + RoPE + scale, in place.
-  if (tid < kRows) {
-    const int row = tid;
-    const int pi = row % p.bmp;
-    bf16* r = sQ + row * RW;
-    float ss = 0.f;
 #pragma unroll
-    for (int c = 0; c < DC; ++c) {
-      const u32x4 v = *(const u32x4*)(r + c * 8);
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+    for (int it = 0; it < QIT; ++it) {
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      if (i0 + qpi[it] >= T) qv[it] = zero;
+      *(u32x4*)(sQ + qrow[it] * RW + dc * 8) = qv[it];
+    }
+    // Per-dim constants of this thread's chunk: weight, RoPE partner (dim k pairs with
+    // k + r/2), the partner's weight with the sign of its term (minus in the lower half),
+    // and the pair index. Dims past rotary_dim take partner 0 and pair 0 (read, then
+    // discarded): the loop below has no branches, so its LDS reads overlap.
+    float wv[8], wp[8];
+    int part[8], tj[8];
+    bool rot[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int c = dc * 8 + e;
+      const bool lower = c < half;
+      rot[e] = c < p.rdim;
+      part[e] = rot[e] ? (lower ? c + half : c - half) : 0;
+      tj[e] = rot[e] ? (lower ? c : c - half) : 0;
+      wv[e] = sWq[c];
+      wp[e] = lower ? -sWq[part[e]] : sWq[part[e]];
+    }
+    __syncthreads();   // raw rows and the trig table are in LDS
+    u32x4 res[QIT];
+#pragma unroll
+    for (int it = 0; it < QIT; ++it) {
+      const uint32_t w4[4] = {qv[it].x, qv[it].y, qv[it].z, qv[it].w};
+      float x[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float a = bf16_lo_to_f32(w4[e]), bb = bf16_hi_to_f32(w4[e]);
-        ss = __builtin_fmaf(a, a, ss);
-        ss = __builtin_fmaf(bb, bb, ss);
+        x[2 * e] = bf16_lo_to_f32(w4[e]);
+        x[2 * e + 1] = bf16_hi_to_f32(w4[e]);
+      }
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
+      ss = group_sum<DC>(ss);
+      const float rs = __builtin_amdgcn_rsqf(ss * (1.0f / D) + p.eps) * p.qscale;
+      const bf16* row = sQ + qrow[it] * RW;
+      const float2* trig = sQtrig + qpi[it] * kMaxHalfMfma;
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float a = x[e] * wv[e];
+        const float b = (float)row[part[e]] * wp[e];
+        const float2 cs = trig[tj[e]];
+        const float r = __builtin_fmaf(a, cs.x, b * cs.y);
+        y[e] = (rot[e] ? r : a) * rs;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2 pr = {(bf16)y[2 * e], (bf16)y[2 * e + 1]};
+        res[it][e] = __builtin_bit_cast(uint32_t, pr);
       }
     }
-    const float rn = __builtin_amdgcn_rsqf(ss * (1.0f / D) + p.eps);
-    transform_row<D>(r, r, sWq, sQtrig + pi * kMaxHalfMfma, rn, p.qscale, p.rdim, 0, 1);
+    __syncthreads();   // every partner read of the raw rows is done
+#pragma unroll
+    for (int it = 0; it < QIT; ++it) *(u32x4*)(sQ + qrow[it] * RW + dc * 8) = res[it];
   }
   __syncthreads();
   // Q~ into registers as the B operand: lane holds query row l32 of its block and the
@@ -448,7 +510,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
       for (int e = tid; e < kBN * half; e += kThreads) {
         const int kr = e / half, j = e - kr * half;
         float c, s;
-        rope_cos_sin(p.pos_offset + k0 + kr, p.fr.hi[j], p.fr.lo[j], c, s);
+        rope_cos_sin(p.pos_offset + k0 + kr, sFr[j], sFr[kMaxHalfMfma + j], c, s);
         sKtrig[kr * kMaxHalfMfma + j] = make_float2(c, s);
       }
     }
@@ -835,16 +897,20 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
   }
 
   // ---- Epilogue: O = acc / l (* sigmoid(G)), bf16 store ------------------------------
+  // Each wave stages its QB * 32 rows in its own slice of the (now idle) Q region, then
+  // stores whole 16-byte chunks of contiguous rows (a lane of the accumulator layout
+  // holds 4 consecutive dims of a row; stored as they are, every store instruction
+  // would touch 32 rows).
   acc_fence<QB, DB>(oacc);
+  __syncthreads();   // every wave is done reading the tile buffers
+  bf16* sO = sQ + wave * (QB * 32) * RW;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32);
-    const int pos = qpos[qb];
-    if (pos >= T) continue;
     const float inv = 1.0f / lt;
+    const int pos = min(qpos[qb], T - 1);   // rows past the end are staged, never stored
     const int hg = (wave * QB + qb) / bpp;
-    const int h = kvh * p.group + hg;
-    const size_t rowoff = ((seq0 + pos) * p.Hq + h) * D;
+    const size_t rowoff = ((seq0 + pos) * p.Hq + kvh * p.group + hg) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -860,9 +926,25 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
           o[2] *= sigmoidf_(bf16_lo_to_f32(gw.y));
           o[3] *= sigmoidf_(bf16_hi_to_f32(gw.y));
         }
-        bf16x4 ov = {(bf16)o[0], (bf16)o[1], (bf16)o[2], (bf16)o[3]};
-        *(bf16x4*)(p.out + rowoff + d0) = ov;
+        const bf16x4 ov = {(bf16)o[0], (bf16)o[1], (bf16)o[2], (bf16)o[3]};
+        *(bf16x4*)(sO + (qb * 32 + l32) * RW + d0) = ov;
       }
+    }
+  }
+  // The slice is this wave's own: its LDS operations complete in order, so a wait for
+  // its writes is all the reads below need.
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  constexpr int OIT = QB * 32 * DC / 64;
+#pragma unroll
+  for (int it = 0; it < OIT; ++it) {
+    const int c = lane + it * 64;
+    const int r = c / DC, dc = c % DC;
+    const int blk = wave * QB + r / 32;
+    const int pos = i0 + (blk % bpp) * 32 + r % 32;
+    const u32x4 v = *(const u32x4*)(sO + r * RW + dc * 8);
+    if (pos < T) {
+      const int h = kvh * p.group + blk / bpp;
+      *(u32x4*)(p.out + ((seq0 + pos) * p.Hq + h) * D + dc * 8) = v;
     }
   }
 }

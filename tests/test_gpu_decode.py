@@ -21,19 +21,21 @@ def _w(d, seed):
     return torch.from_numpy(norm_weight(d, seed))
 
 
-@pytest.mark.parametrize("dtype,tol,pos0", [("bf16", TOL_BF16, 1000), ("f32", 2e-5, 1000),
-                                            ("f32", 2e-5, 262100)])
-def test_qknorm_rope_into_cache_layout(dtype, tol, pos0):
+@pytest.mark.parametrize("dtype,tol,pos0,d", [("bf16", TOL_BF16, 1000, 128), ("f32", 2e-5, 1000, 128),
+                                              ("f32", 2e-5, 262100, 128), ("f32", 2e-5, 7, 64),
+                                              ("bf16", TOL_BF16, 0, 64)])
+def test_qknorm_rope_into_cache_layout(dtype, tol, pos0, d):
     zg = _zg()
     import torch
-    B, T, H, d, S = 2, 37, 3, 128, 64
+    B, T, H, S = 2, 37, 3, 64
     x = host_tensor((B, T, H, d), 11, dtype)
     w = _w(d, 12)
     cache = torch.full((B, H, S, d), float("nan"), dtype=x.dtype, device="cuda")
     view = cache.permute(0, 2, 1, 3)[:, 5:5 + T]          # rows 5..5+T of each head
     zg.qknorm_rope(x.cuda(), w.cuda(), out=view, pos_offset=pos0)
     torch.cuda.synchronize()
-    want = O.qknorm_rope(host64(x), host64(w), pos0 + np.arange(T)[None, :, None], 42)
+    want = O.qknorm_rope(host64(x), host64(w), pos0 + np.arange(T)[None, :, None],
+                         42 if d == 128 else 20)
     got = host64(cache).transpose(0, 2, 1, 3)[:, 5:5 + T]
     err = maxabs(got, want)
     say("qknorm_rope", dtype, err)
