@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="attention-stack sweep: 32-layer hybrid / SWA 3:1 / full-attention "
                          "stacks at T = 4K .. 256K (one JSON line per T)")
+    ap.add_argument("--sweep-t", default="",
+                    help="comma-separated sequence lengths for --sweep (default: all)")
     return ap.parse_args()
 
 
@@ -453,7 +455,8 @@ def run_sweep(args):
     r, W = C4.rotary_dim, C4.window
     kv_tok = {n: 2 * stack_kinds(p).count("global") * C4.Hkv * C4.d * 2
               for n, p in STACKS.items()}
-    for T in SWEEP_T:
+    Ts = tuple(int(x) for x in args.sweep_t.split(",") if x) or SWEEP_T
+    for T in Ts:
         q, k, v, g, wq, wk = prefill_inputs(C4, device=dev, T=T)
         out_s, out_g = torch.empty_like(q), torch.empty_like(q)
         ws = torch.empty(zg.global_prefill_workspace_bytes(q, k, rotary_dim=r),

@@ -108,6 +108,7 @@ struct KArgs {
   // n_qtiles sized by max_len; nullptr for dense batches
   const int32_t* cu;
   int max_len, vt_slots;
+  int n_blocks;       // query tiles in all: n_qtiles * n_hb
 };
 
 // Swap bits 2 and 3 of a key index within its 16-key group: keys {0-3, 8-11} then
@@ -186,8 +187,9 @@ __device__ __forceinline__ void transform_row(const bf16* raw, bf16* dst, const 
   }
 }
 
+// One query tile (blockIdx-independent: `lin` names the tile).
 template <int D, bool SWA, bool KPRE, bool STATIC, int NW>
-__global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p) {
+__device__ __forceinline__ void prefill_tile(const KArgs& p, const int lin) {
   using S = Smem<D>;
   constexpr int kThreads = NW * 64;
   constexpr int QB = kRows / 32 / NW;  // 32-row query blocks per wave
@@ -226,27 +228,10 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
     sFr[kMaxHalfMfma + i] = p.fr.lo[i];
   }
   __syncthreads();
-  // ---- Score bound and variant selection (uniform over the grid) ---------------------
-  // After RMSNorm, ||q^|| <= sqrt(d) max|wq| and ||k^|| <= sqrt(d) max|wk|, so every
-  // log2-domain score obeys |s| <= qscale * d * max|wq| * max|wk| (2% margin for the
-  // bf16 rounding of q~ and k~).
-  {
-    float wqm = 0.f, wkm = 0.f;
-    for (int c = lane; c < D; c += 64) {
-      wqm = fmaxf(wqm, fabsf(sWq[c]));
-      wkm = fmaxf(wkm, fabsf(sWk[c]));
-    }
-    wqm = wave_max(wqm);
-    wkm = wave_max(wkm);
-    const float bound = p.qscale * (float)D * wqm * wkm * 1.02f;
-    const bool use_static = bound <= kStaticShiftMax;  // false for NaN weights
-    if (use_static != STATIC) return;
-  }
 
   // Heavy query tiles first (global layers). Workgroup i runs on XCD i % 8 (round-robin
   // dispatch); when the (batch, kv-head) pairs divide evenly, each XCD takes its pairs one
   // after another, so that its L2 holds the K~ / V tiles of one or two pairs at a time.
-  const int lin = blockIdx.x;
   int hb, tile_rank;
   if (p.n_hb % kXcds == 0) {
     const int x = lin % kXcds, slot = lin / kXcds;
@@ -949,12 +934,42 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p)
   }
 }
 
+// Score bound and variant selection (uniform over the grid): after RMSNorm,
+// ||q^|| <= sqrt(d) max|wq| and ||k^|| <= sqrt(d) max|wk|, so every log2-domain score obeys
+// |s| <= qscale * d * max|wq| * max|wk| (2% margin for the bf16 rounding of q~ and k~).
+// False for NaN weights.
+template <int D>
+__device__ __forceinline__ bool static_shift_ok(const KArgs& p) {
+  const int lane = threadIdx.x & 63;
+  float wqm = 0.f, wkm = 0.f;
+  for (int c = lane; c < D; c += 64) {
+    wqm = fmaxf(wqm, fabsf(p.wq[c]));
+    wkm = fmaxf(wkm, fabsf(p.wk[c]));
+  }
+  wqm = wave_max(wqm);
+  wkm = wave_max(wkm);
+  return p.qscale * (float)D * wqm * wkm * 1.02f <= kStaticShiftMax;
+}
+
+// Both variants are launched and each returns at once unless the bound selects it. The
+// static-shift variant takes one query tile per workgroup. The online variant, selected
+// only for large norm weights, runs one workgroup per CU looping over the tiles, so that
+// when it is not selected it costs a single short round of workgroups.
+template <int D, bool SWA, bool KPRE, bool STATIC, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p) {
+  if (static_shift_ok<D>(p) != STATIC) return;
+  if (STATIC) {
+    prefill_tile<D, SWA, KPRE, STATIC, NW>(p, blockIdx.x);
+  } else {
+    for (int lin = blockIdx.x; lin < p.n_blocks; lin += gridDim.x)
+      prefill_tile<D, SWA, KPRE, STATIC, NW>(p, lin);
+  }
+}
+
 template <int D, bool SWA, bool KPRE, int NW = kWavesPerBlock>
 hipError_t launch_t(const KArgs& ka, int n_blocks, hipStream_t s) {
   constexpr int smem = Smem<D>::kTotal;
   constexpr int kThreads = NW * 64;
-  // Both variants are launched; each returns immediately unless the score bound
-  // (computed on the device from the norm weights) selects it.
   auto k_static = prefill_bf16_kernel<D, SWA, KPRE, true, NW>;
   auto k_online = prefill_bf16_kernel<D, SWA, KPRE, false, NW>;
   hipError_t e = hipFuncSetAttribute((const void*)k_static,
@@ -963,8 +978,14 @@ hipError_t launch_t(const KArgs& ka, int n_blocks, hipStream_t s) {
   e = hipFuncSetAttribute((const void*)k_online, hipFuncAttributeMaxDynamicSharedMemorySize,
                           smem);
   if (e != hipSuccess) return e;
+  int dev = 0, cus = 0;
+  e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_static, dim3(n_blocks), dim3(kThreads), smem, s, ka);
-  hipLaunchKernelGGL(k_online, dim3(n_blocks), dim3(kThreads), smem, s, ka);
+  hipLaunchKernelGGL(k_online, dim3(std::min(n_blocks, std::max(cus, 1))), dim3(kThreads), smem,
+                     s, ka);
   return hipGetLastError();
 }
 
@@ -1054,6 +1075,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
   }
   const int n_blocks = ka.n_qtiles * ka.n_hb;
   if (n_blocks == 0) return hipSuccess;
+  ka.n_blocks = n_blocks;
   if (swa_stream_supported(a)) return launch_swa_stream(a, s);
   const bool kpre = (a.kt != nullptr);
   if (a.d == 128) {

@@ -187,3 +187,20 @@ def test_deterministic_and_overwrites_poisoned_output():
         torch.cuda.synchronize()
         assert torch.isfinite(outs[0].float()).all()
         assert torch.equal(outs[0], outs[1])
+
+
+@pytest.mark.parametrize("kind,ws,d", [("swa", None, 128), ("global", "auto", 128),
+                                       ("global", None, 128), ("swa", None, 64),
+                                       ("global", "auto", 64)])
+def test_bf16_running_max_variant(kind, ws, d):
+    # One large norm weight per branch lifts the score bound (qscale * d * max|wq| * max|wk|,
+    # 2% margin) above the static-shift limit of 96 log2 units, so the kernels take their
+    # running-max (online softmax) variant; the scores themselves stay moderate, because
+    # RMSNorm scales the whole row and only one dim is amplified.
+    q, k, v, g, wq, wk = _inputs(2, 300, 8, 2, d, "bf16", 950 + d, g_std=2 ** 0.5)
+    wq[5] = 3.2
+    wk[7] = -3.2
+    qscale = d ** -0.5 * 1.4426950408889634
+    bound = qscale * d * float(wq.abs().max()) * float(wk.abs().max()) * 1.02
+    assert bound > 96.0, bound
+    _check(kind, q, k, v, g, wq, wk, tol=TOL_BF16, workspace=ws)
