@@ -24,7 +24,7 @@
 //   * Loads run one step ahead: Q and G of the next step go straight into registers in
 //     the MFMA operand / accumulator layouts, the next K and V tiles into registers, and
 //     every load of a step is consumed at the top of the next step, before that step's
-//     own loads and stores are issued.
+//     own loads are issued; a step's outputs are stored as soon as its epilogue is done.
 //   * Head dims are permuted inside the products (the same permutation on both operands
 //     of each product): lane group g (lanes 16 g .. 16 g + 15) holds dims [32 g, 32 g + 32)
 //     of its query in Q~ and in O^T, so Q and G are loaded and O stored with 16-byte
@@ -565,18 +565,18 @@ __global__ __launch_bounds__(kThreads, 1) void swa_stream_kernel(const SArgs p) 
 
   // ---- steady state -------------------------------------------------------------------
   // Loads run one step ahead. At the top of step s the loads issued at the top of step
-  // s - 1 are consumed (Q of s, V of s + 1, K of s + 2), the outputs of step s - 1 are
-  // stored and the next loads issued; G of s, issued after the previous epilogue, is
-  // consumed by this step's epilogue. Loads past the segment are clamped and unused.
-  bf16x8 ob[4];
+  // s - 1 are consumed (Q of s, V of s + 1, K of s + 2) and the next loads issued; G of s,
+  // issued after the previous epilogue, is consumed by this step's epilogue, whose
+  // outputs are stored right away (before the next G load, so that waiting for that load
+  // a step later also finds the stores done). Loads past the segment are clamped and
+  // unused.
   for (int s = s_begin; s < s_end; ++s) {
     bf16x8 qreg[4];
     q_transform(qraw, s, qreg);
     // V of block s + 1 into the slot of block s - 5 (last read in step s - 1), raw K of
-    // s + 2; then the outputs of step s - 1 leave, and the registers take the next loads
+    // s + 2; then the registers take the next loads
     stage_v(vr, s + 1);
     stage_k(kr, s + 2);
-    if (s > s_begin) store_out(s - 1, ob);
     load_row(qbase, s + 1, qraw);
     load_v(s + 2, vr);
     load_k(s + 3, kr);
@@ -588,14 +588,15 @@ __global__ __launch_bounds__(kThreads, 1) void swa_stream_kernel(const SArgs p) 
       reset_acc();
       blocks(s, qreg);
     }
+    bf16x8 ob[4];
     epilogue(graw, ob);
+    store_out(s, ob);
     // G of the next step, consumed by the next epilogue
     load_row(gbase, s + 1, graw);
     // Block s + 1, raw K of s + 2 and trig of s + 2 are visible to every wave; every wave
     // is done with block s - 4 (its slot takes block s + 2 next).
     __syncthreads();
   }
-  store_out(s_end - 1, ob);
 }
 
 template <bool STATIC>
