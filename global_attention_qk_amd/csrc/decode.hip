@@ -15,7 +15,8 @@
 //               Partial (max, sum, acc) per split go to the workspace.
 //   3. combine: log-sum-exp merge of the splits per (sequence, query head).
 // SWA layers: one workgroup per (sequence, kv head) does the whole step over the ring
-// (staged in LDS when it holds at most 128 slots).
+// (MFMA scores with the ring in registers when it holds at most 128 slots, the model's
+// window; a per-slot kernel for larger rings).
 #include "launch.h"
 
 namespace zg {
@@ -391,156 +392,286 @@ __global__ __launch_bounds__(kThreads) void swa_decode_kernel(const DecodeArgs p
   }
 }
 
-// Ring of at most 128 slots (the model's window): the whole ring is staged in LDS with
-// 16-byte loads issued together (one memory round trip instead of one per slot), and the
-// scores, softmax and P.V run from LDS. The 16-byte chunks of a K row are XOR-swizzled by
-// the row index so that the 64 lanes of a wave, one slot each, read distinct banks while
-// the ring stays unpadded (two workgroups fit a CU's LDS).
-constexpr int kRingMax = 128;
+constexpr int kRingMax = 128;   // ring slots of the MFMA kernel (the model's window)
 
-template <int D>
-__device__ __forceinline__ void swa_decode_ring_kernel_body(const DecodeArgs& p, const LayerIO& io, int kvh, int b) {
-  constexpr int KRB = D * 2;                       // K row (bytes)
-  constexpr int CPR = D / 8;                       // 16-byte chunks per row
-  // byte offset of chunk ch of K row s
-  auto kpos = [](int s, int ch) { return s * KRB + ((ch ^ (s & (CPR - 1))) << 4); };
-  constexpr int RIT = kRingMax * CPR / kThreads;   // chunks per thread per ring tensor
+// ---------------------------------------------------------------------------------------
+// SWA decode, rings of at most 128 slots and at most 8 query heads per KV head (the
+// model's shape). One workgroup (4 waves) per (sequence, KV head); wave w owns ring slots
+// 32 w .. 32 w + 31. At the start every wave loads its slots' K rows straight into MFMA
+// A-operand registers and its V rows into registers (the whole ring is one memory round
+// trip and nothing of it goes through LDS), while the workgroup normalises and rotates the
+// g query rows and k_new into LDS. Scores of the g heads against the wave's 32 slots come
+// from v_mfma_f32_16x16x32_bf16 (slots on M, heads on N); the wave's softmax statistics
+// and its partial P.V (vector ALUs: 8 dims and a quarter of the slots per lane) are merged
+// across the waves by log-sum-exp, and the gate is applied to the result. The new entry
+// replaces its slot's old contents in the registers (scores and P.V see the ring as it is
+// after the step) and reaches the ring in HBM at the end.
+constexpr int kMfmaDecodeMaxG = 8;
+
+template <int D, int GM>
+struct SwaDecSmem {
+  static constexpr int kQ = 0;                          // bf16 [16][D]: q~ (rows >= g zero)
+  static constexpr int kKn = kQ + 16 * D * 2;           // bf16 [D]: k~_new as the ring holds it
+  static constexpr int kVn = kKn + D * 2;               // bf16 [D]
+  static constexpr int kTrig = kVn + D * 2;             // float2 [kMaxHalfRot]
+  static constexpr int kRaw = kTrig + kMaxHalfRot * 8;  // float [g + 1][D]: normalised rows
+  static constexpr int kP = kRaw + (GM + 1) * D * 4;     // float [4][GM][32]
+  static constexpr int kO = kP + 4 * GM * 32 * 4;        // float [4][GM][D]
+  static constexpr int kML = kO + 4 * GM * D * 4;        // float [4][GM][2]
+  static constexpr int kTotal = kML + 4 * GM * 2 * 4;
+};
+
+// GM: the most query heads per KV head the instance handles (4, or 8).
+template <int D, int GM>
+__device__ __forceinline__ void swa_decode_mfma_body(const DecodeArgs& p, const LayerIO& io,
+                                                     int kvh, int b) {
+  using S = SwaDecSmem<D, GM>;
+  constexpr int KS = D / 32;       // k-steps of the score products
+  constexpr int DL = D / 8;        // lanes per row (8 dims each) in the P.V layout
+  constexpr int KG = 64 / DL;      // slot groups in the P.V layout
+  constexpr int KPL = 32 / KG;     // slots per lane in P.V
   const int G = p.Hq / p.Hkv;
   const int W = p.window;
   const int pos = p.pos[b];
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   bf16* out = (bf16*)io.out + ((size_t)b * p.Hq + kvh * G) * D;
   if (!pos_valid(pos, ZGATTN_POS_LIMIT)) {
     for (int i = t; i < G * D; i += kThreads) out[i] = (bf16)__builtin_nanf("");
     return;
   }
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  char* sK = smem;                                  // [W][KRB], swizzled chunks
-  bf16* sV = (bf16*)(smem + kRingMax * KRB);        // [W][D]
-  float* buf = (float*)(smem + kRingMax * KRB + kRingMax * D * 2);   // G q rows + k_new
-  float* tmp = buf + (G + 1) * D;
-  float* sv = tmp + (G + 1) * D;                    // v_new
-  float* sS = sv + D;                               // [G][W]
+  bf16* sQ = (bf16*)(smem + S::kQ);
+  bf16* sKn = (bf16*)(smem + S::kKn);
+  bf16* sVn = (bf16*)(smem + S::kVn);
+  float2* sTrig = (float2*)(smem + S::kTrig);
+  float* sRaw = (float*)(smem + S::kRaw);
+  float* sP = (float*)(smem + S::kP);
+  float* sO = (float*)(smem + S::kO);
+  float* sML = (float*)(smem + S::kML);
   bf16* kr = (bf16*)io.k_cache + ((size_t)b * p.Hkv + kvh) * W * D;
   bf16* vr = (bf16*)io.v_cache + ((size_t)b * p.Hkv + kvh) * W * D;
-  // ring -> registers (all loads in flight together), then the new token's rows
-  const int nch = W * CPR;
-  u32x4 kc[RIT], vc[RIT];
+
+  // ---- 1. the wave's ring slots -> registers (slots past the ring are clamped, masked) ---
+  u32x4 ka[2][KS], va[KPL];
 #pragma unroll
-  for (int it = 0; it < RIT; ++it) {
-    const int c = t + it * kThreads;
-    if (c < nch) {
-      kc[it] = *(const u32x4*)(kr + (size_t)c * 8);
-      vc[it] = *(const u32x4*)(vr + (size_t)c * 8);
-    }
+  for (int kb = 0; kb < 2; ++kb) {
+    const int slot = min(32 * wave + 16 * kb + (lane & 15), W - 1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      ka[kb][ks] = *(const u32x4*)(kr + (size_t)slot * D + 32 * ks + 8 * (lane >> 4));
   }
-  const bf16* q = (const bf16*)io.q + ((size_t)b * p.Hq + kvh * G) * D;
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    const int slot = min(32 * wave + lane / DL + KG * i, W - 1);
+    va[i] = *(const u32x4*)(vr + (size_t)slot * D + 8 * (lane % DL));
+  }
+
+  // ---- 2. q~ (g rows, scaled by softmax_scale * log2 e) and k~_new into LDS ------------
+  const int half = p.rdim >> 1;
+  for (int j = t; j < half; j += kThreads) {
+    float cs, sn;
+    rope_cos_sin(pos, p.fr.hi[j], p.fr.lo[j], cs, sn);
+    sTrig[j] = make_float2(cs, sn);
+  }
+  const bf16* qg = (const bf16*)io.q + ((size_t)b * p.Hq + kvh * G) * D;
   const bf16* kn = (const bf16*)io.k_new + ((size_t)b * p.Hkv + kvh) * D;
   const bf16* vn = (const bf16*)io.v_new + ((size_t)b * p.Hkv + kvh) * D;
-  for (int i = t; i < (G + 1) * D; i += kThreads)
-    buf[i] = i < G * D ? (float)q[i] : (float)kn[i - G * D];
-  for (int c = t; c < D; c += kThreads) sv[c] = (float)vn[c];
-  const float* wrow[9];
-  for (int r = 0; r < 9; ++r) wrow[r] = r < G ? io.wq : io.wk;
-  __syncthreads();
-  norm_rope_rows_lds<D>(buf, wrow, G + 1, pos, p.rdim, p.eps, p.fr, tmp);
-  const int slot = pos % W;
+  const int sub = t % DL;   // 8 dims of a row per lane
+  for (int r = t / DL; r <= G; r += kThreads / DL) {
+    const bf16* src = r < G ? qg + r * D : kn;
+    const float* w = r < G ? io.wq : io.wk;
+    const u32x4 raw = *(const u32x4*)(src + sub * 8);
+    const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+    float x[8], ss = 0.f;
 #pragma unroll
-  for (int it = 0; it < RIT; ++it) {
-    const int c = t + it * kThreads;
-    if (c < nch) {
-      const int row = c / CPR, ch = c % CPR;
-      *(u32x4*)(sK + kpos(row, ch)) = kc[it];
-      *(u32x4*)(sV + (size_t)c * 8) = vc[it];
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = bf16_lo_to_f32(w4[e]);
+      x[2 * e + 1] = bf16_hi_to_f32(w4[e]);
     }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
+    ss = group_sum<DL>(ss);
+    const float rn = 1.0f / sqrtf(ss / D + p.eps);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sRaw[r * D + sub * 8 + e] = x[e] * rn * w[sub * 8 + e];
   }
+  for (int c = t; c < (16 - G) * D; c += kThreads) sQ[G * D + c] = (bf16)0.0f;
+  if (t < DL) *(u32x4*)(sVn + t * 8) = *(const u32x4*)(vn + t * 8);
   __syncthreads();
-  // the new entry as the ring will hold it (bf16), over the slot's old contents
-  for (int c = t; c < D; c += kThreads) {
-    const bf16 kb = (bf16)buf[G * D + c];
-    buf[G * D + c] = (float)kb;
-    *(bf16*)(sK + kpos(slot, c >> 3) + (c & 7) * 2) = kb;
-    sV[slot * D + c] = (bf16)sv[c];
-  }
-  __syncthreads();
-  // scores: one (head, slot) per thread and pass; four partial sums per dot product
   const float qs = p.scale * 1.4426950408889634f;
-  for (int idx = t; idx < G * W; idx += kThreads) {
-    const int h = idx / W, s = idx - h * W;
-    float d = -INFINITY;
-    if (pos >= W - 1 || s <= pos) {
-      const float* qh = buf + h * D;
-      float a4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-      for (int ch = 0; ch < CPR; ++ch) {
-        const u32x4 raw = *(const u32x4*)(sK + kpos(s, ch));
-        const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+  for (int r = t / DL; r <= G; r += kThreads / DL) {
+    const float* row = sRaw + r * D;
+    bf16x8 o;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          a4[e] = __builtin_fmaf(qh[ch * 8 + 2 * e], bf16_lo_to_f32(w4[e]), a4[e]);
-          a4[e] = __builtin_fmaf(qh[ch * 8 + 2 * e + 1], bf16_hi_to_f32(w4[e]), a4[e]);
-        }
+    for (int e = 0; e < 8; ++e) {
+      // dims past rotary_dim read pair 0 and partner 0 and keep their value
+      const int c = sub * 8 + e;
+      const bool rot = c < p.rdim, lower = c < half;
+      const float2 cs = sTrig[rot ? (lower ? c : c - half) : 0];
+      const float pr = row[rot ? (lower ? c + half : c - half) : 0];
+      const float y = lower ? row[c] * cs.x - pr * cs.y : row[c] * cs.x + pr * cs.y;
+      const float v = rot ? y : row[c];
+      o[e] = (bf16)(r < G ? v * qs : v);
+    }
+    *(bf16x8*)((r < G ? sQ + r * D : sKn) + sub * 8) = o;
+  }
+  __syncthreads();
+
+  // ---- 3. the new entry over its slot's old contents ------------------------------------
+  const int sn = pos % W;
+  if (sn / 32 == wave) {
+    const int sl = sn % 32;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      if (sl / 16 == kb && (lane & 15) == sl % 16) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          ka[kb][ks] = *(const u32x4*)(sKn + 32 * ks + 8 * (lane >> 4));
       }
-      d = ((a4[0] + a4[1]) + (a4[2] + a4[3])) * qs;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i)
+      if (lane / DL == sl % KG && i == sl / KG) va[i] = *(const u32x4*)(sVn + 8 * (lane % DL));
+  }
+
+  // ---- 4. scores and the wave's softmax statistics -------------------------------------
+  // lane: head n = lane % 16, slots 16 kb + 4 (lane / 16) + r of the wave
+  bf16x8 qb[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    qb[ks] = *(const bf16x8*)(sQ + (lane & 15) * D + 32 * ks + 8 * (lane >> 4));
+  f32x4 sc[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    sc[kb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[kb][ks]),
+                                                       qb[ks], sc[kb], 0, 0, 0);
+  }
+  const bool full = pos >= W - 1;
+  float m = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int slot = 32 * wave + 16 * kb + 4 * (lane >> 4) + r;
+      const bool ok = slot < W && (full || slot <= pos);
+      sc[kb][r] = ok ? sc[kb][r] : -INFINITY;
+      m = fmaxf(m, sc[kb][r]);
     }
-    sS[idx] = d;
+  m = fmaxf(m, __shfl_xor(m, 16));
+  m = fmaxf(m, __shfl_xor(m, 32));
+  const float mu = m == -INFINITY ? 0.f : m;   // a wave with no visible slot adds nothing
+  float l = 0.f;
+  const int n = lane & 15;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float pr = fast_exp2(sc[kb][r] - mu);
+      l += pr;
+      // P stored per (head, slot group, index within the group) for the P.V lanes
+      const int sl = 16 * kb + 4 * (lane >> 4) + r;
+      if (n < G) sP[(wave * GM + n) * 32 + (sl % KG) * KPL + sl / KG] = pr;
+    }
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (lane < 16 && n < G) {
+    sML[(wave * GM + n) * 2] = mu;
+    sML[(wave * GM + n) * 2 + 1] = l;
   }
   __syncthreads();
-  for (int h = wave; h < G; h += kThreads / 64) {
-    float m = -INFINITY;
-    for (int s = lane; s < W; s += 64) m = fmaxf(m, sS[h * W + s]);
-    m = wave_max(m);
-    float l = 0.f;
-    for (int s = lane; s < W; s += 64) {
-      const float e = fast_exp2(sS[h * W + s] - m);
-      sS[h * W + s] = e;
-      l += e;
+
+  // ---- 5. partial P.V of the wave: lane holds dims 8 (lane % DL) .. + 7, slot group lane / DL
+  float acc[GM][8];
+#pragma unroll
+  for (int h = 0; h < GM; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  const int kg = lane / DL;
+#pragma unroll
+  for (int h = 0; h < GM; ++h) {
+    if (h >= G) break;
+    float pv[KPL];
+    const float* ph = sP + (wave * GM + h) * 32 + kg * KPL;
+#pragma unroll
+    for (int i = 0; i < KPL; i += 4) {
+      const float4 p4 = *(const float4*)(ph + i);
+      pv[i] = p4.x; pv[i + 1] = p4.y; pv[i + 2] = p4.z; pv[i + 3] = p4.w;
     }
-    l = wave_sum(l);
-    const float inv = 1.0f / l;
-    for (int s = lane; s < W; s += 64) sS[h * W + s] *= inv;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+      const uint32_t w4[4] = {va[i].x, va[i].y, va[i].z, va[i].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[h][2 * e] = __builtin_fmaf(pv[i], bf16_lo_to_f32(w4[e]), acc[h][2 * e]);
+        acc[h][2 * e + 1] = __builtin_fmaf(pv[i], bf16_hi_to_f32(w4[e]), acc[h][2 * e + 1]);
+      }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < GM; ++h) {
+    if (h >= G) break;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = acc[h][e];
+#pragma unroll
+      for (int o = DL; o < 64; o <<= 1) v += __shfl_xor(v, o);
+      acc[h][e] = v;
+    }
+    if (kg == 0) {
+      float* dst = sO + (wave * GM + h) * D + 8 * lane;
+      *(float4*)dst = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+      *(float4*)(dst + 4) = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+    }
   }
   __syncthreads();
-  // P.V: two adjacent dims of one head per thread and pass
-  const bf16* g = (const bf16*)io.g + ((size_t)b * p.Hq + kvh * G) * D;
-  const int ns = pos >= W - 1 ? W : pos + 1;
+
+  // ---- 6. merge the four waves, gate, store; then the ring slot -------------------------
+  const bf16* gg = (const bf16*)io.g + ((size_t)b * p.Hq + kvh * G) * D;
   for (int idx = t; idx < G * D / 2; idx += kThreads) {
     const int h = idx / (D / 2), c = 2 * (idx - h * (D / 2));
-    const float* ph = sS + h * W;
-    float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
-    int s = 0;
-    for (; s + 1 < ns; s += 2) {
-      const uint32_t v0 = *(const uint32_t*)(sV + s * D + c);
-      const uint32_t v1 = *(const uint32_t*)(sV + (s + 1) * D + c);
-      o0 = __builtin_fmaf(ph[s], bf16_lo_to_f32(v0), o0);
-      o1 = __builtin_fmaf(ph[s], bf16_hi_to_f32(v0), o1);
-      o2 = __builtin_fmaf(ph[s + 1], bf16_lo_to_f32(v1), o2);
-      o3 = __builtin_fmaf(ph[s + 1], bf16_hi_to_f32(v1), o3);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      if (sML[(w * GM + h) * 2 + 1] > 0.f) mx = fmaxf(mx, sML[(w * GM + h) * 2]);
+    float o0 = 0.f, o1 = 0.f, lt = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float lw = sML[(w * GM + h) * 2 + 1];
+      if (lw > 0.f) {
+        const float f = fast_exp2(sML[(w * GM + h) * 2] - mx);
+        lt = __builtin_fmaf(lw, f, lt);
+        o0 = __builtin_fmaf(sO[(w * GM + h) * D + c], f, o0);
+        o1 = __builtin_fmaf(sO[(w * GM + h) * D + c + 1], f, o1);
+      }
     }
-    if (s < ns) {
-      const uint32_t v0 = *(const uint32_t*)(sV + s * D + c);
-      o0 = __builtin_fmaf(ph[s], bf16_lo_to_f32(v0), o0);
-      o1 = __builtin_fmaf(ph[s], bf16_hi_to_f32(v0), o1);
-    }
-    const uint32_t gw = *(const uint32_t*)(g + h * D + c);
-    const bf16x2 ov = {(bf16)((o0 + o2) * sigmoidf_(bf16_lo_to_f32(gw))),
-                       (bf16)((o1 + o3) * sigmoidf_(bf16_hi_to_f32(gw)))};
+    const float inv = 1.0f / lt;
+    const uint32_t gw = *(const uint32_t*)(gg + h * D + c);
+    const bf16x2 ov = {(bf16)(o0 * inv * sigmoidf_(bf16_lo_to_f32(gw))),
+                       (bf16)(o1 * inv * sigmoidf_(bf16_hi_to_f32(gw)))};
     *(bf16x2*)(out + h * D + c) = ov;
   }
-  // the ring slot last (every read of the old ring came from the staged copy)
-  for (int c = t; c < D; c += kThreads) {
-    kr[(size_t)slot * D + c] = (bf16)buf[G * D + c];
-    vr[(size_t)slot * D + c] = (bf16)sv[c];
+  // every wave's ring loads were consumed before the last barrier
+  if (t < DL) {
+    *(u32x4*)(kr + (size_t)sn * D + t * 8) = *(const u32x4*)(sKn + t * 8);
+    *(u32x4*)(vr + (size_t)sn * D + t * 8) = *(const u32x4*)(sVn + t * 8);
   }
 }
-template <int D>
-__global__ __launch_bounds__(kThreads) void swa_decode_ring_kernel(const DecodeArgs p) {
-  swa_decode_ring_kernel_body<D>(p, layer_io(p), (int)blockIdx.x, (int)blockIdx.y);
+template <int D, int GM>
+__global__ __launch_bounds__(kThreads) void swa_decode_mfma_kernel(const DecodeArgs p) {
+  swa_decode_mfma_body<D, GM>(p, layer_io(p), (int)blockIdx.x, (int)blockIdx.y);
 }
-template <int D>
-__global__ __launch_bounds__(kThreads) void swa_decode_ring_kernel_layers(const DecodeBatchArgs pb) {
+template <int D, int GM>
+__global__ __launch_bounds__(kThreads) void swa_decode_mfma_kernel_layers(const DecodeBatchArgs pb) {
   const int layer = blockIdx.z;
-  swa_decode_ring_kernel_body<D>(pb.a, pb.io[layer], (int)blockIdx.x, (int)blockIdx.y);
+  swa_decode_mfma_body<D, GM>(pb.a, pb.io[layer], (int)blockIdx.x, (int)blockIdx.y);
+}
+__host__ __forceinline__ bool swa_decode_mfma_ok(const DecodeArgs& a) {
+  const int G = a.Hq / a.Hkv;
+  return a.window >= 1 && a.window <= kRingMax && G >= 1 && G <= kMfmaDecodeMaxG &&
+         (a.d == 64 || a.d == 128) && a.rdim <= a.d;
 }
 
 template <typename K>
@@ -608,20 +739,38 @@ hipError_t launch_layers(K kern, dim3 grid, dim3 block, int smem, hipStream_t s,
   return hipGetLastError();
 }
 
+// Launch of the single-layer (LAYERS false) or batched kernel for the call's head dim and
+// head group (at most 4 query heads per KV head take the smaller instance).
+template <bool LAYERS, typename A>
+hipError_t launch_swa_mfma(dim3 grid, hipStream_t s, const DecodeArgs& a, const A& args) {
+  const bool g4 = a.Hq / a.Hkv <= 4;
+  auto go = [&](auto kern, int smem) -> hipError_t {
+    if constexpr (LAYERS) return launch_layers(kern, grid, dim3(kThreads), smem, s, args);
+    else return launch_dyn(kern, grid, dim3(kThreads), smem, s, args);
+  };
+  if constexpr (LAYERS) {
+    if (a.d == 128)
+      return g4 ? go(swa_decode_mfma_kernel_layers<128, 4>, SwaDecSmem<128, 4>::kTotal)
+                : go(swa_decode_mfma_kernel_layers<128, 8>, SwaDecSmem<128, 8>::kTotal);
+    return g4 ? go(swa_decode_mfma_kernel_layers<64, 4>, SwaDecSmem<64, 4>::kTotal)
+              : go(swa_decode_mfma_kernel_layers<64, 8>, SwaDecSmem<64, 8>::kTotal);
+  } else {
+    if (a.d == 128)
+      return g4 ? go(swa_decode_mfma_kernel<128, 4>, SwaDecSmem<128, 4>::kTotal)
+                : go(swa_decode_mfma_kernel<128, 8>, SwaDecSmem<128, 8>::kTotal);
+    return g4 ? go(swa_decode_mfma_kernel<64, 4>, SwaDecSmem<64, 4>::kTotal)
+              : go(swa_decode_mfma_kernel<64, 8>, SwaDecSmem<64, 8>::kTotal);
+  }
+}
+
 hipError_t launch_swa_decode_layers(const DecodeArgs& a, const LayerIO* io, int n, hipStream_t s) {
-  if (a.window > kRingMax) return hipErrorInvalidValue;
-  const int G = a.Hq / a.Hkv;
-  const int smem = 2 * kRingMax * a.d * 2 +
-                   (2 * (G + 1) * a.d + a.d + G * a.window) * 4;
+  if (!swa_decode_mfma_ok(a)) return hipErrorInvalidValue;
   DecodeBatchArgs pb;
   pb.a = a;
   for (int l0 = 0; l0 < n; l0 += kMaxDecodeLayers) {
     const int m = min(kMaxDecodeLayers, n - l0);
     for (int i = 0; i < m; ++i) pb.io[i] = io[l0 + i];
-    const dim3 grid(a.Hkv, a.B, m);
-    hipError_t e = a.d == 128
-        ? launch_layers(swa_decode_ring_kernel_layers<128>, grid, dim3(kThreads), smem, s, pb)
-        : launch_layers(swa_decode_ring_kernel_layers<64>, grid, dim3(kThreads), smem, s, pb);
+    hipError_t e = launch_swa_mfma<true>(dim3(a.Hkv, a.B, m), s, a, pb);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -662,16 +811,10 @@ hipError_t launch_global_decode_layers(const DecodeArgs& a, const LayerIO* io, i
 }
 
 hipError_t launch_swa_decode(const DecodeArgs& a, hipStream_t s) {
+  if (swa_decode_mfma_ok(a)) return launch_swa_mfma<false>(dim3(a.Hkv, a.B), s, a, a);
+  // rings of more than 128 slots: the per-slot kernel
   const int G = a.Hq / a.Hkv;
   const int smem = (2 * (G + 1) * a.d + a.d + G * a.window) * 4;
-  if (a.window <= kRingMax) {
-    const int ring = 2 * kRingMax * a.d * 2;
-    if (a.d == 128)
-      return launch_dyn(swa_decode_ring_kernel<128>, dim3(a.Hkv, a.B), dim3(kThreads),
-                        ring + smem, s, a);
-    return launch_dyn(swa_decode_ring_kernel<64>, dim3(a.Hkv, a.B), dim3(kThreads), ring + smem,
-                      s, a);
-  }
   if (a.d == 128) return launch_dyn(swa_decode_kernel<128>, dim3(a.Hkv, a.B), dim3(kThreads), smem, s, a);
   return launch_dyn(swa_decode_kernel<64>, dim3(a.Hkv, a.B), dim3(kThreads), smem, s, a);
 }

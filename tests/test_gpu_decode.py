@@ -96,9 +96,11 @@ def test_global_decode_vs_oracle(B, Hq, Hkv, d, S, pos):
         assert np.array_equal(kc2[b, :, mask], host64(kc)[b, :, mask])
 
 
-# Rings of at most 128 slots are staged in LDS; larger rings take the per-slot kernel.
+# Rings of at most 128 slots take the MFMA kernel (instances for at most 4 and for 8 query
+# heads per KV head); larger rings take the per-slot kernel.
 @pytest.mark.parametrize("W,d,Hq,Hkv", [(128, 128, 8, 2), (128, 64, 8, 1), (50, 128, 2, 2),
-                                        (77, 64, 16, 2), (1, 128, 4, 1), (300, 128, 8, 2)])
+                                        (77, 64, 16, 2), (1, 128, 4, 1), (300, 128, 8, 2),
+                                        (128, 128, 16, 2), (100, 128, 8, 1), (33, 64, 2, 1)])
 def test_swa_decode_vs_oracle(W, d, Hq, Hkv):
     zg = _zg()
     import torch
