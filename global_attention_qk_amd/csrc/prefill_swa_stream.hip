@@ -112,7 +112,9 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
 }
 
 // A value the optimiser must treat as recomputed here: keeps lane-derived indices from
-// being hoisted out of the step loop and held in registers for its whole length.
+// being hoisted out of the step loop and held in registers for its whole length (used
+// where the registers matter more than the few instructions; the block products' indices
+// are left hoistable).
 __device__ __forceinline__ int opaque(int x) {
   asm volatile("" : "+v"(x));
   return x;
@@ -399,7 +401,7 @@ __global__ __launch_bounds__(kThreads, 1) void swa_stream_kernel(const SArgs p) 
   // Scores of ring block kb for this wave's 16 queries: two 16-key halves; lane group g
   // holds keys 16 kh + 4 g + r.
   auto scores = [&](int kb, const bf16x8 (&qreg)[4], f32x4 (&sacc)[2]) {
-    const int ln = opaque(lane);
+    const int ln = lane;
     const int nn = ln & 15, gg = ln >> 4;
     const char* sK = smem + kOffK + ring_slot(kb) * kKBlkB;
 #pragma unroll
@@ -413,7 +415,7 @@ __global__ __launch_bounds__(kThreads, 1) void swa_stream_kernel(const SArgs p) 
     }
   };
   auto pv_block = [&](int kb, const bf16x8& pb, bool first) {
-    const int ln = opaque(lane);
+    const int ln = lane;
     const int nn = ln & 15, gg = ln >> 4;
     const char* sV = smem + kOffV + ring_slot(kb) * kVBlkB;
 #pragma unroll
@@ -440,7 +442,7 @@ __global__ __launch_bounds__(kThreads, 1) void swa_stream_kernel(const SArgs p) 
   // in its block) and the diagonal block (keys at or below it); the first block starts the
   // accumulators from zero.
   auto blocks_full = [&](int s, const bf16x8 (&qreg)[4]) {
-    const int ln = opaque(lane);
+    const int ln = lane;
     const int nn = ln & 15, gg = ln >> 4;
     const int qo = 16 * ph + nn;   // query offset within the step's 32 positions
     float ls = 0.f;
