@@ -55,6 +55,11 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="attention-stack sweep: 32-layer hybrid / SWA 3:1 / full-attention "
                          "stacks at T = 4K .. 256K (one JSON line per T)")
+    ap.add_argument("--configs", action="store_true",
+                    help="every configuration of the measurement table (C1-C5) with the "
+                         "per-call protocol: 5 warm-ups, median/min/p90 of >= 20 calls "
+                         "(>= 5 for the 256K global layer and the stack), caches flushed "
+                         "before each call; one JSON line per configuration and layer")
     ap.add_argument("--sweep-t", default="",
                     help="comma-separated sequence lengths for --sweep (default: all)")
     return ap.parse_args()
@@ -118,6 +123,8 @@ def main():
         return run_only(args)
     if args.sweep:
         return run_sweep(args)
+    if args.configs:
+        return run_configs(args)
     if args.model_decode:
         return run_model_decode(args)
     if args.varlen:
@@ -503,6 +510,136 @@ def run_sweep(args):
         print(json.dumps(rec), flush=True)
         del q, k, v, g, out_s, out_g, ws
         torch.cuda.empty_cache()
+
+
+# Targets of the measurement table: (configuration, layer) -> ms per call.
+CONFIG_TARGETS_MS = {
+    ("C2", "swa"): 0.0979, ("C2", "global"): 0.440,
+    ("C3", "swa"): 0.392, ("C3", "global"): 28.15, ("C3", "stack"): 151.3,
+    ("C4", "swa"): 1.566, ("C4", "global"): 450.4,
+    ("C5", "global_decode"): 7.16, ("C5", "swa_decode_batched_per_layer"): 0.0037,
+}
+
+
+def run_configs(args):
+    """The measurement table's configurations, each call timed on its own: 5 untimed
+    warm-ups, then >= 20 timed calls (>= 5 for the 256K global layer and the 32-layer
+    stack), with a 1 GiB buffer written before every call so that neither L2 nor the
+    256 MB Infinity Cache still holds the inputs; HIP events around the call only. Prints
+    one JSON line per (configuration, layer) with median, min and p90, tokens/s, the
+    roofline fraction and the target."""
+    import torch
+
+    import global_attention_qk_amd as zg
+    from workloads import C1, C2, C3, C4, C5, STACKS, decode_inputs, prefill_inputs, stack_kinds
+
+    dev = "cuda"
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def timed(fn, reps):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            flush.fill_(7)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ts.sort()
+        return ts
+
+    def emit(cfg, layer, ts, tokens, bound, work):
+        med = ts[len(ts) // 2]
+        rec = {"config": cfg, "layer": layer, "reps": len(ts), "median_ms": med,
+               "min_ms": ts[0], "p90_ms": ts[min(len(ts) - 1, (9 * len(ts)) // 10)],
+               "tokens_per_s": tokens / (med / 1e3) if tokens else None}
+        if bound == "mfma":
+            rec.update(bound="mfma", achieved_TFLOPs=work / (med / 1e3) / 1e12,
+                       frac=work / (med / 1e3) / 1e12 / PEAK_BF16_TFLOPS)
+        elif bound == "hbm":
+            rec.update(bound="hbm", achieved_GBs=work / (med / 1e3) / 1e9,
+                       frac=work / (med / 1e3) / 1e9 / PEAK_HBM_GBS)
+        tgt = CONFIG_TARGETS_MS.get((cfg, layer))
+        if tgt is not None:
+            rec.update(target_ms=tgt, met=med <= tgt)
+        print(json.dumps(rec), flush=True)
+
+    def pair(cfg, wl, reps_swa, reps_glob, T=None):
+        T = wl.T if T is None else T
+        q, k, v, g, wq, wk = prefill_inputs(wl, device=dev, T=T)
+        r, W = wl.rotary_dim, wl.window
+        out = torch.empty_like(q)
+        cnt = alg_counts(T, wl.B, wl.Hq, wl.Hkv, wl.d, W, 1, 1)
+        ts = timed(lambda: zg.swa_prefill(q, k, v, g, wq, wk, window=W, rotary_dim=r, out=out),
+                   reps_swa)
+        emit(cfg, "swa", ts, wl.B * T, "hbm", cnt["swa_bytes"])
+        if reps_glob:
+            ws = torch.empty(zg.global_prefill_workspace_bytes(q, k, rotary_dim=r),
+                             dtype=torch.uint8, device=dev)
+            ts = timed(lambda: zg.global_prefill(q, k, v, wq, wk, rotary_dim=r, workspace=ws,
+                                                 out=out), reps_glob)
+            emit(cfg, "global", ts, wl.B * T, "mfma", cnt["glob_flops"])
+            return q, k, v, g, wq, wk, out, ws
+        return None
+
+    # C1: fp32 gated SWA layer (parity configuration; launch-bound)
+    q, k, v, g, wq, wk = prefill_inputs(C1, device=dev)
+    out = torch.empty_like(q)
+    ts = timed(lambda: zg.swa_prefill(q, k, v, g, wq, wk, window=C1.window,
+                                      rotary_dim=C1.rotary_dim, out=out), 20)
+    emit("C1", "swa", ts, C1.B * C1.T, None, 0)
+    # C2, C4: the layer pair
+    pair("C2", C2, 20, 20)
+    # C3: both layer kinds at T=65536 and the 32-layer hybrid stack over one input set
+    held = pair("C3", C3, 20, 5)
+    q, k, v, g, wq, wk, out, ws = held
+    kinds = stack_kinds(STACKS["hybrid_5to1"])
+
+    def stack():
+        for kd in kinds:
+            if kd == "swa":
+                zg.swa_prefill(q, k, v, g, wq, wk, window=C3.window, rotary_dim=C3.rotary_dim,
+                               out=out)
+            else:
+                zg.global_prefill(q, k, v, wq, wk, rotary_dim=C3.rotary_dim, workspace=ws,
+                                  out=out)
+    emit("C3", "stack", timed(stack, 5), C3.T, None, 0)
+    del q, k, v, g, out, ws, held
+    torch.cuda.empty_cache()
+    pair("C4", C4, 20, 5)
+    torch.cuda.empty_cache()
+    # C5: decode, B=32 at context 262144
+    dec = decode_inputs(C5, device=dev)
+    S, W, r = C5.T, C5.window, C5.rotary_dim
+    pos = torch.full((C5.B,), S - 1, dtype=torch.int32, device=dev)
+    cnt = alg_counts(1, 1, C5.Hq, C5.Hkv, C5.d, W, C5.B, S)
+    dws = torch.empty(zg.global_decode_workspace_bytes(dec["q"], dec["k_new"], S),
+                      dtype=torch.uint8, device=dev)
+    out = torch.empty_like(dec["q"])
+    ts = timed(lambda: zg.global_decode(dec["q"], dec["k_new"], dec["v_new"], dec["wq"],
+                                        dec["wk"], dec["k_cache"], dec["v_cache"], pos,
+                                        rotary_dim=r, workspace=dws, out=out), 20)
+    emit("C5", "global_decode", ts, C5.B, "hbm", cnt["gdec_bytes"])
+    ts = timed(lambda: zg.swa_decode(dec["q"], dec["k_new"], dec["v_new"], dec["g"], dec["wq"],
+                                     dec["wk"], dec["k_ring"], dec["v_ring"], pos,
+                                     rotary_dim=r, out=out), 20)
+    emit("C5", "swa_decode", ts, C5.B, "hbm", cnt["sdec_bytes"])
+    del dec
+    torch.cuda.empty_cache()
+    # the 27 gated SWA layers of a model decode step in one launch (per-layer time)
+    swa_layers = []
+    for i in range(27):
+        x = decode_inputs(C5, device=dev, layer=i, kind="swa")
+        swa_layers.append(dict(kind="swa", q=x["q"], g=x["g"], k_new=x["k_new"],
+                               v_new=x["v_new"], wq=x["wq"], wk=x["wk"], k_cache=x["k_ring"],
+                               v_cache=x["v_ring"]))
+    ts = timed(lambda: zg.model_decode(swa_layers, pos, window=W, rotary_dim=r), 20)
+    emit("C5", "swa_decode_batched_per_layer", [t / 27 for t in ts], C5.B, "hbm",
+         cnt["sdec_bytes"])
 
 
 def run_only(args):
