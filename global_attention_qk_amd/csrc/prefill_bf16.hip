@@ -122,6 +122,11 @@ __device__ __forceinline__ int vt_slot(int key) {
 __device__ __forceinline__ void mfma_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
+// The same product without the wait states, for schedules where P was written at least
+// one MFMA slot earlier (slots are fenced by scheduling barriers).
+__device__ __forceinline__ void mfma_acc_late(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
 
 #ifndef ZG_PREFILL_PIPE
 #define ZG_PREFILL_PIPE 1
@@ -788,7 +793,7 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p, const int lin) {
         const int db = t % DB, jh = t / DB;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
-          mfma_acc(oacc[qb][db], a, __builtin_bit_cast(bf16x8, pw[kb][qb][jh]));
+          mfma_acc_late(oacc[qb][db], a, __builtin_bit_cast(bf16x8, pw[kb][qb][jh]));
         if (kb == 0) {
           // C: softmax of block 1 under the block-0 P.V products
 #pragma unroll
