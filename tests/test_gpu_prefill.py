@@ -204,3 +204,17 @@ def test_bf16_running_max_variant(kind, ws, d):
     bound = qscale * d * float(wq.abs().max()) * float(wk.abs().max()) * 1.02
     assert bound > 96.0, bound
     _check(kind, q, k, v, g, wq, wk, tol=TOL_BF16, workspace=ws)
+
+
+def test_bf16_running_max_variant_loops_over_tiles():
+    # 512 query tiles: more than the CUs of the device, so each workgroup of the looping
+    # running-max grid takes several tiles; rows sampled over the whole sequence.
+    import torch
+    if torch.cuda.get_device_properties(0).multi_processor_count >= 512:
+        pytest.skip("needs more query tiles than CUs")
+    q, k, v, g, wq, wk = _inputs(2, 8192, 8, 2, 128, "bf16", 970)
+    wq[5] = 3.2
+    wk[7] = -3.2
+    rows = np.unique(np.concatenate([np.arange(0, 8192, 131), [63, 64, 8191]]))
+    _check("global", q, k, v, None, wq, wk, tol=TOL_BF16, rows=rows)
+    _check("global", q, k, v, None, wq, wk, tol=TOL_BF16, rows=rows, workspace=None)
