@@ -62,6 +62,10 @@ constexpr int kDmaPhase = ZG_DMA_PHASE;
 constexpr int kBN = 64;           // keys per tile
 constexpr int kXcds = 8;          // accelerator complex dies (one L2 each)
 constexpr int kMaxHalfMfma = 32;  // rotary_dim <= 64 on this path
+constexpr int kQTrigStride = kMaxHalfMfma + 1;  // float2 per Q position: rows 8 banks apart
+// Rotated pairs of the model's partial RoPE, rotary_dim = 2 * floor(0.33 * d / 2).
+template <int D>
+constexpr int kModelHalf = D == 128 ? 21 : 10;
 constexpr float kStaticShiftMax = 96.0f;  // largest score bound (log2 units) without a max
 
 template <int D>
@@ -70,7 +74,7 @@ struct Smem {
   static constexpr int kVtRowB = kBN * 2 + 16;  // padded V^T row (bytes)
   // Phase 1 (Q): raw Q rows, transformed in place; then copied to registers.
   static constexpr int kQ = kRows * kRowB;
-  static constexpr int kQtrig = kRows * kMaxHalfMfma * 8;
+  static constexpr int kQtrig = kRows * kQTrigStride * 8;
   // Main loop: two K~ / V^T buffers, raw K tile and its trig table (fused path).
   static constexpr int kK = kBN * kRowB;
   static constexpr int kVt = D * kVtRowB;
@@ -297,7 +301,7 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p, const int lin) {
       const int pi = e / half, j = e - pi * half;
       float c, s;
       rope_cos_sin(p.pos_offset + i0 + pi, sFr[j], sFr[kMaxHalfMfma + j], c, s);
-      sQtrig[pi * kMaxHalfMfma + j] = make_float2(c, s);
+      sQtrig[pi * kQTrigStride + j] = make_float2(c, s);
     }
 #pragma unroll
     for (int it = 0; it < QIT; ++it) {
@@ -305,59 +309,118 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p, const int lin) {
       if (i0 + qpi[it] >= T) qv[it] = zero;
       *(u32x4*)(sQ + qrow[it] * RW + dc * 8) = qv[it];
     }
-    // Per-dim constants of this thread's chunk: weight, RoPE partner (dim k pairs with
-    // k + r/2), the partner's weight with the sign of its term (minus in the lower half),
-    // and the pair index. Dims past rotary_dim take partner 0 and pair 0 (read, then
-    // discarded): the loop below has no branches, so its LDS reads overlap.
-    float wv[8], wp[8];
-    int part[8], tj[8];
-    bool rot[8];
+    if (p.rdim == 2 * kModelHalf<D>) {
+      // The model's rotary dim: one thread per tile row. The row comes from LDS into
+      // registers whole, so the sum of squares needs no cross-lane reduction and each
+      // rotated pair meets its partner in registers; the transformed row goes back in
+      // place (no other thread reads it before the barrier below).
+      constexpr int H = kModelHalf<D>;
+      __syncthreads();   // raw rows and the trig table are in LDS
+      for (int r = tid; r < kRows; r += kThreads) {
+        bf16* row = sQ + r * RW;
+        const float2* trig = sQtrig + (r % p.bmp) * kQTrigStride;
+        uint32_t xw[D / 2];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int c = dc * 8 + e;
-      const bool lower = c < half;
-      rot[e] = c < p.rdim;
-      part[e] = rot[e] ? (lower ? c + half : c - half) : 0;
-      tj[e] = rot[e] ? (lower ? c : c - half) : 0;
-      wv[e] = sWq[c];
-      wp[e] = lower ? -sWq[part[e]] : sWq[part[e]];
-    }
-    __syncthreads();   // raw rows and the trig table are in LDS
-    u32x4 res[QIT];
+        for (int k = 0; k < DC; ++k) {
+          const u32x4 v = *(const u32x4*)(row + k * 8);
+          xw[4 * k] = v.x;
+          xw[4 * k + 1] = v.y;
+          xw[4 * k + 2] = v.z;
+          xw[4 * k + 3] = v.w;
+        }
+        float2 cs[H];
 #pragma unroll
-    for (int it = 0; it < QIT; ++it) {
-      const uint32_t w4[4] = {qv[it].x, qv[it].y, qv[it].z, qv[it].w};
-      float x[8];
+        for (int j = 0; j < H; ++j) cs[j] = trig[j];
+        float ss = 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[2 * e] = bf16_lo_to_f32(w4[e]);
-        x[2 * e + 1] = bf16_hi_to_f32(w4[e]);
+        for (int i = 0; i < D / 2; ++i) {
+          const bf16x2 t = __builtin_bit_cast(bf16x2, xw[i]);
+          ss = __builtin_amdgcn_fdot2_f32_bf16(t, t, ss, false);
+        }
+        const float rs = __builtin_amdgcn_rsqf(ss * (1.0f / D) + p.eps) * p.qscale;
+        auto xv = [&](int c) -> float {
+          return (c & 1) ? bf16_hi_to_f32(xw[c >> 1]) : bf16_lo_to_f32(xw[c >> 1]);
+        };
+#pragma unroll
+        for (int k = 0; k < DC; ++k) {
+          uint32_t o[4];
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            float y[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const int c = 8 * k + e + u;
+              const float a = xv(c) * sWq[c];
+              float rv = a;
+              if (c < H) {
+                rv = __builtin_fmaf(a, cs[c].x, -(xv(c + H) * sWq[c + H]) * cs[c].y);
+              } else if (c < 2 * H) {
+                rv = __builtin_fmaf(a, cs[c - H].x, (xv(c - H) * sWq[c - H]) * cs[c - H].y);
+              }
+              y[u] = rv * rs;
+            }
+            const bf16x2 pr = {(bf16)y[0], (bf16)y[1]};
+            o[e / 2] = __builtin_bit_cast(uint32_t, pr);
+          }
+          *(u32x4*)(row + k * 8) = (u32x4){o[0], o[1], o[2], o[3]};
+        }
       }
-      float ss = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
-      ss = group_sum<DC>(ss);
-      const float rs = __builtin_amdgcn_rsqf(ss * (1.0f / D) + p.eps) * p.qscale;
-      const bf16* row = sQ + qrow[it] * RW;
-      const float2* trig = sQtrig + qpi[it] * kMaxHalfMfma;
-      float y[8];
+    } else {
+      // Per-dim constants of this thread's chunk: weight, RoPE partner (dim k pairs with
+      // k + r/2), the partner's weight with the sign of its term (minus in the lower half),
+      // and the pair index. Dims past rotary_dim take partner 0 and pair 0 (read, then
+      // discarded): the loop below has no branches, so its LDS reads overlap.
+      float wv[8], wp[8];
+      int part[8], tj[8];
+      bool rot[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float a = x[e] * wv[e];
-        const float b = (float)row[part[e]] * wp[e];
-        const float2 cs = trig[tj[e]];
-        const float r = __builtin_fmaf(a, cs.x, b * cs.y);
-        y[e] = (rot[e] ? r : a) * rs;
+        const int c = dc * 8 + e;
+        const bool lower = c < half;
+        rot[e] = c < p.rdim;
+        part[e] = rot[e] ? (lower ? c + half : c - half) : 0;
+        tj[e] = rot[e] ? (lower ? c : c - half) : 0;
+        wv[e] = sWq[c];
+        wp[e] = lower ? -sWq[part[e]] : sWq[part[e]];
       }
+      __syncthreads();   // raw rows and the trig table are in LDS
+      u32x4 res[QIT];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bf16x2 pr = {(bf16)y[2 * e], (bf16)y[2 * e + 1]};
-        res[it][e] = __builtin_bit_cast(uint32_t, pr);
+      for (int it = 0; it < QIT; ++it) {
+        const uint32_t w4[4] = {qv[it].x, qv[it].y, qv[it].z, qv[it].w};
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[2 * e] = bf16_lo_to_f32(w4[e]);
+          x[2 * e + 1] = bf16_hi_to_f32(w4[e]);
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
+        ss = group_sum<DC>(ss);
+        const float rs = __builtin_amdgcn_rsqf(ss * (1.0f / D) + p.eps) * p.qscale;
+        const bf16* row = sQ + qrow[it] * RW;
+        const float2* trig = sQtrig + qpi[it] * kQTrigStride;
+        float y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float a = x[e] * wv[e];
+          const float b = (float)row[part[e]] * wp[e];
+          const float2 cs = trig[tj[e]];
+          const float r = __builtin_fmaf(a, cs.x, b * cs.y);
+          y[e] = (rot[e] ? r : a) * rs;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bf16x2 pr = {(bf16)y[2 * e], (bf16)y[2 * e + 1]};
+          res[it][e] = __builtin_bit_cast(uint32_t, pr);
+        }
       }
+      __syncthreads();   // every partner read of the raw rows is done
+#pragma unroll
+      for (int it = 0; it < QIT; ++it) *(u32x4*)(sQ + qrow[it] * RW + dc * 8) = res[it];
+
     }
-    __syncthreads();   // every partner read of the raw rows is done
-#pragma unroll
-    for (int it = 0; it < QIT; ++it) *(u32x4*)(sQ + qrow[it] * RW + dc * 8) = res[it];
   }
   __syncthreads();
   // Q~ into registers as the B operand: lane holds query row l32 of its block and the
