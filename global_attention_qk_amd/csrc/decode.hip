@@ -452,6 +452,38 @@ __device__ __forceinline__ void swa_decode_mfma_body(const DecodeArgs& p, const 
   bf16* kr = (bf16*)io.k_cache + ((size_t)b * p.Hkv + kvh) * W * D;
   bf16* vr = (bf16*)io.v_cache + ((size_t)b * p.Hkv + kvh) * W * D;
 
+  // ---- 0. the small inputs first: loads complete in issue order, so the q/k transform
+  // below waits only for these, not for the ring behind them --------------------------------
+  const int half = p.rdim >> 1;
+  const bf16* qg = (const bf16*)io.q + ((size_t)b * p.Hq + kvh * G) * D;
+  const bf16* kn = (const bf16*)io.k_new + ((size_t)b * p.Hkv + kvh) * D;
+  const bf16* vn = (const bf16*)io.v_new + ((size_t)b * p.Hkv + kvh) * D;
+  const bf16* gg = (const bf16*)io.g + ((size_t)b * p.Hq + kvh * G) * D;
+  const int sub = t % DL;   // 8 dims of a row per lane
+  const int r0 = t / DL;    // the row (q head, or k_new when r0 == G) this lane transforms
+  static_assert(kThreads / DL > kMfmaDecodeMaxG, "one pass over the g + 1 rows");
+  u32x4 raw0 = {0u, 0u, 0u, 0u}, vn0 = {0u, 0u, 0u, 0u};
+  float4 w0 = {0.f, 0.f, 0.f, 0.f}, w1 = {0.f, 0.f, 0.f, 0.f};
+  if (r0 <= G) {
+    raw0 = *(const u32x4*)((r0 < G ? qg + r0 * D : kn) + sub * 8);
+    const float* w = (r0 < G ? io.wq : io.wk) + sub * 8;
+    w0 = *(const float4*)w;
+    w1 = *(const float4*)(w + 4);
+  }
+  if (t < DL) vn0 = *(const u32x4*)(vn + t * 8);
+  float fhi = 0.f, flo = 0.f;
+  if (t < half) {
+    fhi = p.fr.hi[t];
+    flo = p.fr.lo[t];
+  }
+  constexpr int GIT = (GM * D / 2 + kThreads - 1) / kThreads;
+  uint32_t gw[GIT];
+#pragma unroll
+  for (int i = 0; i < GIT; ++i) {
+    const int idx = t + i * kThreads;
+    gw[i] = idx < G * D / 2 ? *(const uint32_t*)(gg + 2 * idx) : 0u;
+  }
+
   // ---- 1. the wave's ring slots -> registers (slots past the ring are clamped, masked) ---
   u32x4 ka[2][KS], va[KPL];
 #pragma unroll
@@ -468,21 +500,15 @@ __device__ __forceinline__ void swa_decode_mfma_body(const DecodeArgs& p, const 
   }
 
   // ---- 2. q~ (g rows, scaled by softmax_scale * log2 e) and k~_new into LDS ------------
-  const int half = p.rdim >> 1;
-  for (int j = t; j < half; j += kThreads) {
+  if (t < half) {
     float cs, sn;
-    rope_cos_sin(pos, p.fr.hi[j], p.fr.lo[j], cs, sn);
-    sTrig[j] = make_float2(cs, sn);
+    rope_cos_sin(pos, fhi, flo, cs, sn);
+    sTrig[t] = make_float2(cs, sn);
   }
-  const bf16* qg = (const bf16*)io.q + ((size_t)b * p.Hq + kvh * G) * D;
-  const bf16* kn = (const bf16*)io.k_new + ((size_t)b * p.Hkv + kvh) * D;
-  const bf16* vn = (const bf16*)io.v_new + ((size_t)b * p.Hkv + kvh) * D;
-  const int sub = t % DL;   // 8 dims of a row per lane
-  for (int r = t / DL; r <= G; r += kThreads / DL) {
-    const bf16* src = r < G ? qg + r * D : kn;
-    const float* w = r < G ? io.wq : io.wk;
-    const u32x4 raw = *(const u32x4*)(src + sub * 8);
-    const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+  if (r0 <= G) {
+    const int r = r0;
+    const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    const uint32_t w4[4] = {raw0.x, raw0.y, raw0.z, raw0.w};
     float x[8], ss = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -494,10 +520,10 @@ __device__ __forceinline__ void swa_decode_mfma_body(const DecodeArgs& p, const 
     ss = group_sum<DL>(ss);
     const float rn = 1.0f / sqrtf(ss / D + p.eps);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sRaw[r * D + sub * 8 + e] = x[e] * rn * w[sub * 8 + e];
+    for (int e = 0; e < 8; ++e) sRaw[r * D + sub * 8 + e] = x[e] * rn * w[e];
   }
   for (int c = t; c < (16 - G) * D; c += kThreads) sQ[G * D + c] = (bf16)0.0f;
-  if (t < DL) *(u32x4*)(sVn + t * 8) = *(const u32x4*)(vn + t * 8);
+  if (t < DL) *(u32x4*)(sVn + t * 8) = vn0;
   __syncthreads();
   const float qs = p.scale * 1.4426950408889634f;
   for (int r = t / DL; r <= G; r += kThreads / DL) {
@@ -629,8 +655,10 @@ __device__ __forceinline__ void swa_decode_mfma_body(const DecodeArgs& p, const 
   __syncthreads();
 
   // ---- 6. merge the four waves, gate, store; then the ring slot -------------------------
-  const bf16* gg = (const bf16*)io.g + ((size_t)b * p.Hq + kvh * G) * D;
-  for (int idx = t; idx < G * D / 2; idx += kThreads) {
+#pragma unroll
+  for (int i = 0; i < GIT; ++i) {
+    const int idx = t + i * kThreads;
+    if (idx >= G * D / 2) break;
     const int h = idx / (D / 2), c = 2 * (idx - h * (D / 2));
     float mx = -INFINITY;
 #pragma unroll
@@ -648,9 +676,8 @@ __device__ __forceinline__ void swa_decode_mfma_body(const DecodeArgs& p, const 
       }
     }
     const float inv = 1.0f / lt;
-    const uint32_t gw = *(const uint32_t*)(gg + h * D + c);
-    const bf16x2 ov = {(bf16)(o0 * inv * sigmoidf_(bf16_lo_to_f32(gw))),
-                       (bf16)(o1 * inv * sigmoidf_(bf16_hi_to_f32(gw)))};
+    const bf16x2 ov = {(bf16)(o0 * inv * sigmoidf_(bf16_lo_to_f32(gw[i]))),
+                       (bf16)(o1 * inv * sigmoidf_(bf16_hi_to_f32(gw[i])))};
     *(bf16x2*)(out + h * D + c) = ov;
   }
   // every wave's ring loads were consumed before the last barrier
