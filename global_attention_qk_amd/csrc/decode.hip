@@ -432,14 +432,14 @@ __device__ __forceinline__ void swa_decode_mfma_body(const DecodeArgs& p, const 
   constexpr int KPL = 32 / KG;     // slots per lane in P.V
   const int G = p.Hq / p.Hkv;
   const int W = p.window;
-  const int pos = p.pos[b];
+  // An invalid position is not waited for up front: the step runs at position 0 (its loads
+  // do not depend on the position), then writes NaN outputs and leaves the ring unchanged.
+  const int pos_in = p.pos[b];
+  const bool valid = pos_valid(pos_in, ZGATTN_POS_LIMIT);
+  const int pos = valid ? pos_in : 0;
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   bf16* out = (bf16*)io.out + ((size_t)b * p.Hq + kvh * G) * D;
-  if (!pos_valid(pos, ZGATTN_POS_LIMIT)) {
-    for (int i = t; i < G * D; i += kThreads) out[i] = (bf16)__builtin_nanf("");
-    return;
-  }
   extern __shared__ __attribute__((aligned(16))) char smem[];
   bf16* sQ = (bf16*)(smem + S::kQ);
   bf16* sKn = (bf16*)(smem + S::kKn);
@@ -463,12 +463,16 @@ __device__ __forceinline__ void swa_decode_mfma_body(const DecodeArgs& p, const 
   const int r0 = t / DL;    // the row (q head, or k_new when r0 == G) this lane transforms
   static_assert(kThreads / DL > kMfmaDecodeMaxG, "one pass over the g + 1 rows");
   u32x4 raw0 = {0u, 0u, 0u, 0u}, vn0 = {0u, 0u, 0u, 0u};
-  float4 w0 = {0.f, 0.f, 0.f, 0.f}, w1 = {0.f, 0.f, 0.f, 0.f};
+  float4 wq0 = {0.f, 0.f, 0.f, 0.f}, wq1 = wq0, wk0 = wq0, wk1 = wq0;
   if (r0 <= G) {
     raw0 = *(const u32x4*)((r0 < G ? qg + r0 * D : kn) + sub * 8);
-    const float* w = (r0 < G ? io.wq : io.wk) + sub * 8;
-    w0 = *(const float4*)w;
-    w1 = *(const float4*)(w + 4);
+    // both weight vectors, selected where they are used: a select of the two pointers
+    // becomes a per-lane load of the chosen kernel-argument field, and a select of the
+    // values here would wait for the loads at once
+    wq0 = *(const float4*)(io.wq + sub * 8);
+    wq1 = *(const float4*)(io.wq + sub * 8 + 4);
+    wk0 = *(const float4*)(io.wk + sub * 8);
+    wk1 = *(const float4*)(io.wk + sub * 8 + 4);
   }
   if (t < DL) vn0 = *(const u32x4*)(vn + t * 8);
   float fhi = 0.f, flo = 0.f;
@@ -507,6 +511,7 @@ __device__ __forceinline__ void swa_decode_mfma_body(const DecodeArgs& p, const 
   }
   if (r0 <= G) {
     const int r = r0;
+    const float4 w0 = r < G ? wq0 : wk0, w1 = r < G ? wq1 : wk1;
     const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
     const uint32_t w4[4] = {raw0.x, raw0.y, raw0.z, raw0.w};
     float x[8], ss = 0.f;
@@ -676,12 +681,13 @@ __device__ __forceinline__ void swa_decode_mfma_body(const DecodeArgs& p, const 
       }
     }
     const float inv = 1.0f / lt;
-    const bf16x2 ov = {(bf16)(o0 * inv * sigmoidf_(bf16_lo_to_f32(gw[i]))),
-                       (bf16)(o1 * inv * sigmoidf_(bf16_hi_to_f32(gw[i])))};
+    const float nan = __builtin_nanf("");
+    const bf16x2 ov = {(bf16)(valid ? o0 * inv * sigmoidf_(bf16_lo_to_f32(gw[i])) : nan),
+                       (bf16)(valid ? o1 * inv * sigmoidf_(bf16_hi_to_f32(gw[i])) : nan)};
     *(bf16x2*)(out + h * D + c) = ov;
   }
   // every wave's ring loads were consumed before the last barrier
-  if (t < DL) {
+  if (valid && t < DL) {
     *(u32x4*)(kr + (size_t)sn * D + t * 8) = *(const u32x4*)(sKn + t * 8);
     *(u32x4*)(vr + (size_t)sn * D + t * 8) = *(const u32x4*)(sVn + t * 8);
   }
