@@ -696,61 +696,100 @@ def run_only(args):
           f"{e0.elapsed_time(e1) / max(args.steps, 1):.3f} ms each", flush=True)
 
 
-def cpu_baseline(budget_s: float):
+def _host_facts():
+    """CPU model and the BLAS library numpy calls (name, version, threads)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        import numpy  # noqa: F401  (loads the BLAS library that threadpoolctl inspects)
+        from threadpoolctl import threadpool_info
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            blas = (f"{libs[0].get('internal_api')} {libs[0].get('version')} "
+                    f"({libs[0].get('architecture')})")
+    except Exception:
+        pass
+    return model, blas
+
+
+def cpu_baseline(budget_s: float, n_rows: int = 512):
     """The fp64 oracle on a bounded sample of the same workload, scaled to tokens/s.
 
-    Sample: n stratified query rows of the T=262144 prefill pair (all 32 heads, both
-    layers: the oracle's global rows read all keys up to the row, SWA rows their window)
-    and one decode sequence of each kind at context 262144. CPU seconds per step =
-    T * (global + SWA seconds per row) + 32 * (decode seconds per sequence).
+    Sample: ``n_rows`` stratified query rows of the T=262144 prefill pair (rows 0..15,
+    window edges, tile boundaries, T-1, the rest uniform; all 32 heads; the global rows
+    read every key up to the row, the SWA rows only their window) and one decode sequence
+    of each kind at context 262144. A global row costs in proportion to the keys it sees
+    (i + 1), so its measured time is scaled by T(T+1)/2 / sum(i + 1) over the sample; an
+    SWA row by the layer's visible pairs / sum(min(i + 1, W)); decode by B = 32.
     """
     import numpy as np
-    import torch
+    from threadpoolctl import threadpool_limits
 
     from oracle import attn as O
     from workloads import C4, C5, decode_inputs, prefill_inputs, stratified_rows
 
-    cores = len(os.sched_getaffinity(0))
-    T = C4.T
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    T, W = C4.T, C4.window
     q, k, v, g, wq, wk = prefill_inputs(C4, device="cuda")
     f = lambda t: t.float().cpu().numpy()
-    n_rows = 24
-    rows = np.sort(np.random.default_rng(7).choice(T, size=n_rows, replace=False))
+    rows = stratified_rows(T, n_rows, 7, W)
     kh, vh = f(k), f(v)
     qh, gh = f(q[:, rows]), f(g[:, rows])
     wqh, wkh = f(wq), f(wk)
     del q, k, v, g
     t0 = time.perf_counter()
-    O.prefill_rows(qh, kh, vh, None, wqh, wkh, rows, rotary_dim=C4.rotary_dim,
-                   threads=cores)
-    t_glob = (time.perf_counter() - t0) / n_rows
+    O.prefill_rows(qh, kh, vh, None, wqh, wkh, rows, rotary_dim=C4.rotary_dim, threads=cores)
+    t_glob = time.perf_counter() - t0
     t0 = time.perf_counter()
-    O.prefill_rows(qh, kh, vh, gh, wqh, wkh, rows, window=C4.window,
-                   rotary_dim=C4.rotary_dim, threads=cores)
-    t_swa = (time.perf_counter() - t0) / n_rows
+    O.prefill_rows(qh, kh, vh, gh, wqh, wkh, rows, window=W, rotary_dim=C4.rotary_dim,
+                   threads=cores)
+    t_swa = time.perf_counter() - t0
     del kh, vh
+    glob_scale = (T * (T + 1) / 2) / float(np.sum(rows + 1))
+    swa_pairs = W * (W + 1) // 2 + (T - W) * W
+    swa_scale = swa_pairs / float(np.sum(np.minimum(rows + 1, W)))
     dec = decode_inputs(C5, device="cuda", B=1)
     dh = {n: f(t) for n, t in dec.items()}
     S = C5.T
-    t0 = time.perf_counter()
-    O.decode_global(dh["q"], dh["k_new"], dh["v_new"], dh["wq"], dh["wk"], dh["k_cache"],
-                    dh["v_cache"], np.array([S - 1]), rotary_dim=C5.rotary_dim)
-    t_gd = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    O.decode_swa(dh["q"], dh["k_new"], dh["v_new"], dh["g"], dh["wq"], dh["wk"], dh["k_ring"],
-                 dh["v_ring"], np.array([S - 1]), window=C5.window, rotary_dim=C5.rotary_dim)
-    t_sd = time.perf_counter() - t0
-    step_s = T * (t_glob + t_swa) + C5.B * (t_gd + t_sd)
+    with threadpool_limits(limits=cores):
+        t0 = time.perf_counter()
+        O.decode_global(dh["q"], dh["k_new"], dh["v_new"], dh["wq"], dh["wk"], dh["k_cache"],
+                        dh["v_cache"], np.array([S - 1]), rotary_dim=C5.rotary_dim)
+        t_gd = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        O.decode_swa(dh["q"], dh["k_new"], dh["v_new"], dh["g"], dh["wq"], dh["wk"],
+                     dh["k_ring"], dh["v_ring"], np.array([S - 1]), window=C5.window,
+                     rotary_dim=C5.rotary_dim)
+        t_sd = time.perf_counter() - t0
+    step_s = t_glob * glob_scale + t_swa * swa_scale + C5.B * (t_gd + t_sd)
+    model, blas = _host_facts()
     return {
         "value": (T + C5.B) / step_s,
         "unit": "tokens/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": f"{n_rows} uniformly drawn query rows of the T=262144 prefill pair (all 32 "
-                  f"heads; global {t_glob:.3f} s/row, SWA {t_swa:.3f} s/row) and one decode "
-                  f"sequence per layer kind at context 262144 (global {t_gd:.2f} s, SWA "
-                  f"{t_sd:.4f} s), scaled to one step of 262144 prefill + 32 decode tokens",
+        "sample": f"{len(rows)} stratified query rows of the T=262144 prefill pair (all 32 "
+                  f"heads; global {t_glob:.2f} s for {int(np.sum(rows + 1))} visible keys per "
+                  f"head, scaled by pairs x{glob_scale:.0f}; SWA {t_swa:.2f} s, x{swa_scale:.0f})"
+                  f" and one decode sequence per layer kind at context 262144 (global "
+                  f"{t_gd:.2f} s, SWA {t_sd:.4f} s, x32), summed to one step of 262144 "
+                  f"prefill + 32 decode tokens",
         "seconds_per_step_estimate": step_s,
+        "seconds_by_layer": {"global_prefill": t_glob * glob_scale,
+                             "swa_prefill": t_swa * swa_scale,
+                             "global_decode": C5.B * t_gd, "swa_decode": C5.B * t_sd},
+        "cpu_model": model,
+        "blas": blas,
+        "threads": cores,
+        "parallel_jobs_prefill": min(cores, C4.B * C4.Hkv),
     }
 
 

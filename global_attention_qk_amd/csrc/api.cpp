@@ -5,7 +5,67 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "launch.h"
+
+namespace zg {
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];   // 0 = not queried yet
+struct SmemAttr {
+  const void* kernel;
+  int dev;
+  int bytes;
+};
+constexpr int kMaxSmemAttrs = 512;
+SmemAttr g_smem[kMaxSmemAttrs];
+int g_n_smem = 0;
+std::mutex g_smem_mu;
+}  // namespace
+
+hipError_t device_cu_count(int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int c = g_cus[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *cus = c;
+      return hipSuccess;
+    }
+  }
+  int c = 0;
+  e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (c < 1) c = 1;
+  if (dev >= 0 && dev < kMaxDevices) g_cus[dev].store(c, std::memory_order_relaxed);
+  *cus = c;
+  return hipSuccess;
+}
+
+hipError_t ensure_dynamic_smem(const void* kernel, int bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_smem_mu);
+  for (int i = 0; i < g_n_smem; ++i)
+    if (g_smem[i].kernel == kernel && g_smem[i].dev == dev && g_smem[i].bytes >= bytes)
+      return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return e;
+  for (int i = 0; i < g_n_smem; ++i)
+    if (g_smem[i].kernel == kernel && g_smem[i].dev == dev) {
+      g_smem[i].bytes = bytes;
+      return hipSuccess;
+    }
+  if (g_n_smem < kMaxSmemAttrs) g_smem[g_n_smem++] = SmemAttr{kernel, dev, bytes};
+  return hipSuccess;
+}
+
+}  // namespace zg
 
 using namespace zg;
 

@@ -673,8 +673,7 @@ WsLayout ws_layout(int B, int T, int Hq, int Hkv, int d) {
 template <typename K, typename A>
 hipError_t launch_big(K kern, dim3 grid, dim3 block, int smem, hipStream_t s, const A& a) {
   if (smem > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+    hipError_t e = ensure_dynamic_smem((const void*)kern, smem);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(kern, grid, block, smem, s, a);

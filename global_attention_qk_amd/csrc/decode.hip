@@ -615,6 +615,14 @@ __device__ __forceinline__ void swa_decode_mfma_body(const DecodeArgs& p, const 
   __syncthreads();
 
   // ---- 5. partial P.V of the wave: lane holds dims 8 (lane % DL) .. + 7, slot group lane / DL
+  // Slots the query does not see (past the ring, or not yet written while pos < W - 1)
+  // carry P = 0, but their V rows may hold anything (a fresh ring is uninitialised
+  // memory): they are zeroed so that 0 * NaN or 0 * inf cannot reach the sum.
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    const int slot = 32 * wave + lane / DL + KG * i;
+    if (!(slot < W && (full || slot <= pos))) va[i] = (u32x4){0u, 0u, 0u, 0u};
+  }
   float acc[GM][8];
 #pragma unroll
   for (int h = 0; h < GM; ++h)
@@ -711,8 +719,7 @@ template <typename K>
 hipError_t launch_dyn(K kern, dim3 grid, dim3 block, int smem, hipStream_t s,
                       const DecodeArgs& a) {
   if (smem > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+    hipError_t e = ensure_dynamic_smem((const void*)kern, smem);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(kern, grid, block, smem, s, a);
@@ -764,8 +771,7 @@ template <typename K>
 hipError_t launch_layers(K kern, dim3 grid, dim3 block, int smem, hipStream_t s,
                          const DecodeBatchArgs& pb) {
   if (smem > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+    hipError_t e = ensure_dynamic_smem((const void*)kern, smem);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(kern, grid, block, smem, s, pb);

@@ -9,6 +9,12 @@
 
 namespace zg {
 
+// Per-device facts queried once per device and process (the only global state of the
+// library): the compute-unit count of the current device, and the dynamic-LDS limit of
+// a kernel raised once per (device, kernel). Thread-safe.
+hipError_t device_cu_count(int* cus);
+hipError_t ensure_dynamic_smem(const void* kernel, int bytes);
+
 // One prefill call (either layer kind), already validated on the host.
 struct PrefillArgs {
   const void* q;

@@ -19,11 +19,15 @@
 //     and the next tile's global loads are in flight while the current one is computed.
 //   * Q~ is pre-multiplied by scale * log2(e) so that p = exp2(s - m).
 //   * Static shift: after RMSNorm every score obeys |s| <= B = qscale * d * max|wq| *
-//     max|wk| (RoPE keeps norms). When B is moderate, p = exp2(s) with no max
-//     subtraction is exact (softmax is shift-invariant) and cannot overflow or flush to
-//     zero, so the running max, its reduction and the accumulator rescale disappear. A
-//     second kernel variant keeps an online max for larger bounds; both variants are
-//     launched and each returns at once unless the bound selects it.
+//     max|wk| (RoPE keeps norms). When B is moderate, p = exp2(s - B) with the constant
+//     shift B in place of the running max is exact (softmax is shift-invariant): the
+//     score accumulators start at -B (the MFMA C operand, so the shift costs nothing),
+//     every p lies in [2^-2B, 1], so neither the row sum nor the fp32 P.V accumulator can
+//     overflow (at most T * max|v|), and with B <= 48 the largest p of a row is at least
+//     2^-96, far above the fp32 normal range's end. The running max, its reduction and
+//     the accumulator rescale disappear. A second kernel variant keeps an online max for
+//     larger bounds; both variants are launched and each returns at once unless the bound
+//     selects it.
 //   * The O accumulators stay in AGPRs for the whole kernel (the P.V product is issued
 //     through a constrained MFMA), leaving the VGPRs to the scores and operands.
 //   * K~: for global layers a separate pass writes normalised+rotated K once into a
@@ -66,7 +70,7 @@ constexpr int kQTrigStride = kMaxHalfMfma + 1;  // float2 per Q position: rows 8
 // Rotated pairs of the model's partial RoPE, rotary_dim = 2 * floor(0.33 * d / 2).
 template <int D>
 constexpr int kModelHalf = D == 128 ? 21 : 10;
-constexpr float kStaticShiftMax = 96.0f;  // largest score bound (log2 units) without a max
+constexpr float kStaticShiftMax = 48.0f;  // largest score bound (log2 units) without a max
 
 template <int D>
 struct Smem {
@@ -197,8 +201,9 @@ __device__ __forceinline__ void transform_row(const bf16* raw, bf16* dst, const 
 }
 
 // One query tile (blockIdx-independent: `lin` names the tile).
+// `sinit` starts every score accumulator: -B (the static shift) or 0 (online variant).
 template <int D, bool SWA, bool KPRE, bool STATIC, int NW>
-__device__ __forceinline__ void prefill_tile(const KArgs& p, const int lin) {
+__device__ __forceinline__ void prefill_tile(const KArgs& p, const int lin, const float sinit) {
   using S = Smem<D>;
   constexpr int kThreads = NW * 64;
   constexpr int QB = kRows / 32 / NW;  // 32-row query blocks per wave
@@ -602,7 +607,7 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p, const int lin) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[qb][r] = 0.f;
+      for (int r = 0; r < 16; ++r) sacc[qb][r] = sinit;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const bf16x8 a = *(const bf16x8*)(sK + (kb * 32 + l32) * RW + ks * 16 + hi * 8);
@@ -611,54 +616,65 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p, const int lin) {
         sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[qb][ks], sacc[qb], 0, 0, 0);
     }
   };
-  // Mask (edge tiles), exponentiate, round to bf16 (the P operand) and add the rounded
-  // values to the row sums. The online variant also raises the running max.
-  auto probs = [&](f32x16 (&sacc)[QB], int kb, const int (&rel)[QB], bf16x8 (&pb)[QB][2],
-                   auto masked_tag) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    if (MASKED) {
+  // Mask (edge tiles): scores of keys the row does not see become -inf.
+  auto mask_block = [&](f32x16 (&sacc)[QB], int kb, const int (&rel)[QB]) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int off = kb * 32 + (r >> 2) * 8 + (r & 3);  // key - k0 - 4*hi
-          bool vis = off <= rel[qb];
-          if (SWA) vis = vis && (off > rel[qb] - p.window);
-          if (!vis) sacc[qb][r] = -INFINITY;
-        }
-    }
+      for (int r = 0; r < 16; ++r) {
+        const int off = kb * 32 + (r >> 2) * 8 + (r & 3);  // key - k0 - 4*hi
+        bool vis = off <= rel[qb];
+        if (SWA) vis = vis && (off > rel[qb] - p.window);
+        if (!vis) sacc[qb][r] = -INFINITY;
+      }
+  };
+  // Online variant: this lane's largest (masked) score per query block.
+  auto lane_max = [&](const f32x16 (&sacc)[QB], float (&mt)[QB]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float mu = 0.f;
-      if (!STATIC) {
-        float mt = sacc[qb][0];
+      float m = sacc[qb][0];
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sacc[qb][r]);
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float m_old = m_run[qb];
-        const bool raise = mt > m_old + 8.0f;
-        if (__ballot(raise)) {
-          const float m_new = raise ? mt : m_old;
-          const float alpha = (m_old == -INFINITY) ? 0.f : fast_exp2(m_old - m_new);
-          l_run[qb] *= alpha;
-          acc_fence<QB, DB>(oacc);
+      for (int r = 1; r < 16; ++r) m = fmaxf(m, sacc[qb][r]);
+      mt[qb] = fmaxf(mt[qb], m);
+    }
+  };
+  // Online variant: raise the running max to the row's max over scores not yet
+  // exponentiated (lazily: only when it grows by more than 8, so p <= 2^8), rescaling the
+  // row sum and every P.V product accumulated so far. Every block whose P is formed after
+  // this call must have its scores in `mt`, so that no P is formed against an older max.
+  auto raise_max = [&](const float (&mt_lane)[QB]) {
 #pragma unroll
-          for (int db = 0; db < DB; ++db)
+    for (int qb = 0; qb < QB; ++qb) {
+      const float mt = fmaxf(mt_lane[qb], __shfl_xor(mt_lane[qb], 32));
+      const float m_old = m_run[qb];
+      const bool raise = mt > m_old + 8.0f;
+      if (__ballot(raise)) {
+        const float m_new = raise ? mt : m_old;
+        const float alpha = (m_old == -INFINITY) ? 0.f : fast_exp2(m_old - m_new);
+        l_run[qb] *= alpha;
+        acc_fence<QB, DB>(oacc);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha;
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int db = 0; db < DB; ++db) pin_agpr(oacc[qb][db]);
-          m_run[qb] = m_new;
-        }
-        mu = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
+          for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) pin_agpr(oacc[qb][db]);
+        m_run[qb] = m_new;
       }
+    }
+  };
+  // Exponentiate against the running max (static variant: the accumulators already hold
+  // s - B), round to bf16 (the P operand) and add the rounded values to the row sums.
+  auto expo = [&](const f32x16 (&sacc)[QB], bf16x8 (&pb)[QB][2]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float mu = (STATIC || m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
       float ls = l_run[qb];
 #pragma unroll
       for (int jh = 0; jh < 2; ++jh) {
         bf16x8 v;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          v[e] = (bf16)fast_exp2(STATIC ? sacc[qb][jh * 8 + e] : sacc[qb][jh * 8 + e] - mu);
+        for (int e = 0; e < 8; ++e) v[e] = (bf16)fast_exp2(sacc[qb][jh * 8 + e] - mu);
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           const bf16x2 pr = {v[e], v[e + 1]};
@@ -668,6 +684,21 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p, const int lin) {
       }
       l_run[qb] = ls;
     }
+  };
+  // One 32-key block: mask, (online) raise the max, exponentiate. The block's P.V must be
+  // accumulated before the next block's probs() can raise the max again.
+  auto probs = [&](f32x16 (&sacc)[QB], int kb, const int (&rel)[QB], bf16x8 (&pb)[QB][2],
+                   auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    if (MASKED) mask_block(sacc, kb, rel);
+    if (!STATIC) {
+      float mt[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) mt[qb] = -INFINITY;
+      lane_max(sacc, mt);
+      raise_max(mt);
+    }
+    expo(sacc, pb);
   };
   // O^T += V^T P^T for one 32-key block.
   auto pv = [&](const bf16* sVt, int kb, bf16x8 (&pb)[QB][2]) {
@@ -697,8 +728,8 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p, const int lin) {
       f32x16 s0[1], s1[1];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        s0[0][r] = 0.f;
-        s1[0][r] = 0.f;
+        s0[0][r] = sinit;
+        s1[0][r] = sinit;
       }
       // The two waves sharing a SIMD run the same phases; raising the priority in the
       // MFMA phases lets the MFMA issuer win arbitration while the other wave's
@@ -712,9 +743,21 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p, const int lin) {
         s1[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[0][ks], s1[0], 0, 0, 0);
       }
       set_prio<0>();
+      // Both blocks' P are formed before either P.V: the online max is raised once over
+      // the whole tile, so that P of block 0 and block 1 share one max.
       bf16x8 p0[1][2], p1[1][2];
-      probs(s0, 0, rel, p0, masked_tag);
-      probs(s1, 1, rel, p1, masked_tag);
+      if (decltype(masked_tag)::value) {
+        mask_block(s0, 0, rel);
+        mask_block(s1, 1, rel);
+      }
+      if (!STATIC) {
+        float mt[1] = {-INFINITY};
+        lane_max(s0, mt);
+        lane_max(s1, mt);
+        raise_max(mt);
+      }
+      expo(s0, p0);
+      expo(s1, p1);
       mid();
       set_prio<1>();
       pv(sVt, 0, p0);
@@ -798,7 +841,7 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p, const int lin) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sc[kb][qb][r] = 0.f;
+        for (int r = 0; r < 16; ++r) sc[kb][qb][r] = sinit;
     // softmax piece j (0..7) of block kb: query block j / 4, half j / 2 % 2 of the 16
     // scores, four of them (j % 2)
     auto sm_piece = [&](int kb, int j) {
@@ -1002,12 +1045,11 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p, const int lin) {
   }
 }
 
-// Score bound and variant selection (uniform over the grid): after RMSNorm,
-// ||q^|| <= sqrt(d) max|wq| and ||k^|| <= sqrt(d) max|wk|, so every log2-domain score obeys
+// Score bound (uniform over the grid): after RMSNorm, ||q^|| <= sqrt(d) max|wq| and
+// ||k^|| <= sqrt(d) max|wk|, so every log2-domain score obeys
 // |s| <= qscale * d * max|wq| * max|wk| (2% margin for the bf16 rounding of q~ and k~).
-// False for NaN weights.
 template <int D>
-__device__ __forceinline__ bool static_shift_ok(const KArgs& p) {
+__device__ __forceinline__ float score_bound(const KArgs& p) {
   const int lane = threadIdx.x & 63;
   float wqm = 0.f, wkm = 0.f;
   for (int c = lane; c < D; c += 64) {
@@ -1016,7 +1058,7 @@ __device__ __forceinline__ bool static_shift_ok(const KArgs& p) {
   }
   wqm = wave_max(wqm);
   wkm = wave_max(wkm);
-  return p.qscale * (float)D * wqm * wkm * 1.02f <= kStaticShiftMax;
+  return fabsf(p.qscale) * (float)D * wqm * wkm * 1.02f;
 }
 
 // Both variants are launched and each returns at once unless the bound selects it. The
@@ -1025,12 +1067,13 @@ __device__ __forceinline__ bool static_shift_ok(const KArgs& p) {
 // when it is not selected it costs a single short round of workgroups.
 template <int D, bool SWA, bool KPRE, bool STATIC, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p) {
-  if (static_shift_ok<D>(p) != STATIC) return;
+  const float bound = score_bound<D>(p);
+  if ((bound <= kStaticShiftMax) != STATIC) return;
   if (STATIC) {
-    prefill_tile<D, SWA, KPRE, STATIC, NW>(p, blockIdx.x);
+    prefill_tile<D, SWA, KPRE, STATIC, NW>(p, blockIdx.x, -bound);
   } else {
     for (int lin = blockIdx.x; lin < p.n_blocks; lin += gridDim.x)
-      prefill_tile<D, SWA, KPRE, STATIC, NW>(p, lin);
+      prefill_tile<D, SWA, KPRE, STATIC, NW>(p, lin, 0.f);
   }
 }
 
@@ -1040,16 +1083,12 @@ hipError_t launch_t(const KArgs& ka, int n_blocks, hipStream_t s) {
   constexpr int kThreads = NW * 64;
   auto k_static = prefill_bf16_kernel<D, SWA, KPRE, true, NW>;
   auto k_online = prefill_bf16_kernel<D, SWA, KPRE, false, NW>;
-  hipError_t e = hipFuncSetAttribute((const void*)k_static,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+  hipError_t e = ensure_dynamic_smem((const void*)k_static, smem);
   if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute((const void*)k_online, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          smem);
+  e = ensure_dynamic_smem((const void*)k_online, smem);
   if (e != hipSuccess) return e;
-  int dev = 0, cus = 0;
-  e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  int cus = 0;
+  e = device_cu_count(&cus);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_static, dim3(n_blocks), dim3(kThreads), smem, s, ka);
   hipLaunchKernelGGL(k_online, dim3(std::min(n_blocks, std::max(cus, 1))), dim3(kThreads), smem,

@@ -30,8 +30,9 @@
 //     of its query in Q~ and in O^T, so Q and G are loaded and O stored with 16-byte
 //     accesses, and of the rotated pairs (j, j + 21) only j = 11 .. 20 cross lane groups
 //     (exchanged with one swizzle).
-//   * Static softmax shift as in the other prefill kernel: when the score bound implied
-//     by the norm weights is moderate, p = exp2(s) with no running max; otherwise an
+//   * Static softmax shift as in the other prefill kernel: when the score bound B implied
+//     by the norm weights is moderate (B <= 48 log2 units), the score accumulators start
+//     at -B and p = exp2(s - B) lies in [2^-2B, 1] with no running max; otherwise an
 //     online-max variant runs (both are launched; each returns unless selected).
 #include <type_traits>
 
@@ -52,7 +53,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxWindow = 128;
 constexpr int kMinSegSteps = 8;
 constexpr int kTrigBufs = 3;
-constexpr float kStaticShiftMax = 96.0f;
+constexpr float kStaticShiftMax = 48.0f;   // largest score bound (log2 units) without a max
 
 constexpr int kKRowB = kD * 2 + 16;        // padded K~ / raw K row
 constexpr int kKBlkB = kStep * kKRowB;     // K~ block: 32 rows
@@ -179,8 +180,11 @@ __global__ __launch_bounds__(kThreads, 1) void swa_stream_kernel(const SArgs p) 
     sFr[32 + tid] = p.fr.lo[tid];
   }
   __syncthreads();
+  // |s| <= d * max|wq * qscale| * max|wk| after RMSNorm (2% margin for bf16 operands).
+  // The static variant starts every score accumulator at -bound (so p <= 1); the online
+  // variant at 0.
+  float sinit = 0.f;
   {
-    // |s| <= d * max|wq * qscale| * max|wk| after RMSNorm (2% margin for bf16 operands).
     float wqm = 0.f, wkm = 0.f;
     for (int c = lane; c < kD; c += 64) {
       wqm = fmaxf(wqm, fabsf(sWq[c]));
@@ -188,8 +192,10 @@ __global__ __launch_bounds__(kThreads, 1) void swa_stream_kernel(const SArgs p) 
     }
     wqm = wave_max(wqm);
     wkm = wave_max(wkm);
-    const bool use_static = (float)kD * wqm * wkm * 1.02f <= kStaticShiftMax;
+    const float bound = (float)kD * wqm * wkm * 1.02f;
+    const bool use_static = bound <= kStaticShiftMax;
     if (use_static != STATIC) return;
+    if (STATIC) sinit = -bound;
   }
 
   const int lin = blockIdx.x;
@@ -406,7 +412,7 @@ __global__ __launch_bounds__(kThreads, 1) void swa_stream_kernel(const SArgs p) 
     const char* sK = smem + kOffK + ring_slot(kb) * kKBlkB;
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
-      sacc[kh] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      sacc[kh] = (f32x4){sinit, sinit, sinit, sinit};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const bf16x8 a = *(const bf16x8*)(sK + krow_off(16 * kh + nn, 4 * gg + ks));
@@ -603,8 +609,7 @@ __global__ __launch_bounds__(kThreads, 1) void swa_stream_kernel(const SArgs p) 
 
 template <bool STATIC>
 hipError_t set_smem() {
-  return hipFuncSetAttribute((const void*)swa_stream_kernel<STATIC>,
-                             hipFuncAttributeMaxDynamicSharedMemorySize, kSmem);
+  return ensure_dynamic_smem((const void*)swa_stream_kernel<STATIC>, kSmem);
 }
 
 }  // namespace
@@ -640,10 +645,8 @@ hipError_t launch_swa_stream(const PrefillArgs& a, hipStream_t s) {
   if (ka.n_steps == 0 || ka.n_hb == 0) return hipSuccess;
   // One resident workgroup per CU (the LDS ring takes most of a CU): split every
   // (batch, KV head) stream into segments so that the grid covers the CUs once.
-  int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  int cus = 0;
+  hipError_t e = device_cu_count(&cus);
   if (e != hipSuccess) return e;
   // Segments of at least kMinSegSteps steps keep the three-tile prologue of a segment
   // (and its serial load latency) small against the segment's work.

@@ -226,13 +226,23 @@ size_t zgattn_model_decode_workspace_bytes(const zgattn_desc* desc, int32_t n_la
                                            const int32_t* is_global, int32_t capacity);
 
 /*
- * Standalone QK-RMSNorm + partial RoPE (the q/k-branch transform of both layer kinds).
+ * Standalone QK-RMSNorm + partial RoPE: the transform the q and k branches of both layer
+ * kinds go through before attention ("ZGCM-1-7B 完全解説" explainer, section アーキテクチャ:
+ * QK normalisation by RMSNorm and partial RoPE with rotary ratio 0.33; the jaehun.me
+ * review, section "1) 구조·시스템 공동 설계", states both model-wide). Per row of d values:
+ * y = RoPE(x / sqrt(mean(x^2) + rms_eps) * w, position), rotating the leading rotary_dim
+ * dims as described at the top of this header. Its use here is building decode caches
+ * (which hold post-norm, post-RoPE K) from a prefill's K.
  *   x: [B, T, n_heads, d] contiguous (desc->dtype);  w: fp32 [d];
  *   pos: device int32 [B*T] absolute positions, or NULL for pos_offset + t;
  *   y: same dtype, element (b, t, h, c) stored at
  *      y + b*y_stride_b + t*y_stride_t + h*y_stride_h + c   (strides in elements),
  *   so it can write straight into a [B, Hkv, S, d] cache. y must not overlap x.
  */
+/* Errors: ZGATTN_ENULL for a NULL x, w or y (seq_len > 0); ZGATTN_EINVAL for unaligned
+ * pointers or strides that are not multiples of 16 bytes or are negative; ZGATTN_ERANGE
+ * when pos is NULL and pos_offset + seq_len - 1 exceeds ZGATTN_MAX_POSITION. Positions
+ * given through pos are not checked on the host. */
 int zgattn_qknorm_rope(const zgattn_desc* desc, int32_t n_heads, const void* x,
                        const float* w, const int32_t* pos, void* y, int64_t y_stride_b,
                        int64_t y_stride_t, int64_t y_stride_h, void* stream);

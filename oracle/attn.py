@@ -133,14 +133,30 @@ def prefill(q, k, v, g, wq, wk, *, window=None, rotary_dim=None, rope_base=10000
                         rope_base=rope_base, eps=eps, scale=scale, pos_offset=pos_offset)
 
 
+def _block_keys(ri, window):
+    """Key positions a block of query rows ``ri`` can see: 0 .. max(ri) for a global layer
+    (returned as that contiguous range), the union of the rows' windows
+    ``max(0, i - W + 1) .. i`` for a sliding-window layer (so a windowed block touches, and
+    normalises and rotates, only keys that some row of it sees)."""
+    hi = int(np.max(ri)) + 1
+    if window is None:
+        return np.arange(hi)
+    lo = np.maximum(np.asarray(ri) - window + 1, 0)
+    return np.unique(np.concatenate([np.arange(a, r + 1) for a, r in zip(lo, ri)]))
+
+
 def prefill_rows(q, k, v, g, wq, wk, rows, *, window=None, rotary_dim=None,
                  rope_base=10000.0, eps=1e-6, scale=None, pos_offset=0,
                  row_block=256, threads=1):
     """Layer output for the query rows ``rows`` only: float64 [B, len(rows), Hq, d].
 
-    Same definition as ``prefill``; rows are processed in blocks so that only the keys a
-    block can see are touched. ``q``/``g`` may be given either full [B, T, Hq, d] or already
-    restricted to ``rows`` ([B, len(rows), Hq, d]); k and v are always full length.
+    Same definition as ``prefill``. Rows are taken in blocks (in sorted order) of at most
+    ``row_block``; a block scores only the keys ``_block_keys`` gives (every key visible
+    to one of its rows; the mask removes the rest). A global layer's keys are normalised
+    and rotated once per KV head, a windowed layer's per block, for that block's keys
+    only. ``threads`` > 1 runs the (batch, KV head) pairs on a thread pool. ``q``/``g``
+    may be given either full [B, T, Hq, d] or already restricted to ``rows``
+    ([B, len(rows), Hq, d]); k and v are always full length.
     """
     k = np.asarray(k)
     v = np.asarray(v)
@@ -158,25 +174,37 @@ def prefill_rows(q, k, v, g, wq, wk, rows, *, window=None, rotary_dim=None,
     r = rotary_dim_for(d) if rotary_dim is None else rotary_dim
     sc = 1.0 / math.sqrt(d) if scale is None else scale
     out = np.zeros((B, len(rows), Hq, d), dtype=F64)
+    if len(rows) == 0:
+        return out
     qpos = pos_offset + rows
     qt = qknorm_rope(q_rows, wq, qpos[None, :, None], r, rope_base, eps)  # [B,R,Hq,d]
     order = np.argsort(rows, kind="stable")
 
+    def keys_of(b, kv, keys, kt_all, v_all):
+        if kt_all is not None:      # global: a contiguous range of the transformed keys
+            lo, hi = int(keys[0]), int(keys[-1]) + 1
+            return kt_all[lo:hi], v_all[lo:hi]
+        kt = qknorm_rope(np.asarray(k[b, keys, kv], dtype=F64), wk, pos_offset + keys, r,
+                         rope_base, eps)
+        return kt, np.asarray(v[b, keys, kv], dtype=F64)
+
     def one(b, kv):
-        kmax = int(rows.max()) + 1
-        kt = qknorm_rope(np.asarray(k[b, :kmax, kv], dtype=F64), wk,
-                         pos_offset + np.arange(kmax), r, rope_base, eps)
-        vv = np.asarray(v[b, :kmax, kv], dtype=F64)
+        kt_all = v_all = None
+        if window is None:
+            kmax = int(rows.max()) + 1
+            kt_all = qknorm_rope(np.asarray(k[b, :kmax, kv], dtype=F64), wk,
+                                 pos_offset + np.arange(kmax), r, rope_base, eps)
+            v_all = np.asarray(v[b, :kmax, kv], dtype=F64)
         for start in range(0, len(order), row_block):
             idx = order[start:start + row_block]
             ri = rows[idx]
-            lo = 0 if window is None else max(0, int(ri.min()) - window + 1)
-            hi = int(ri.max()) + 1
-            mask = visible_mask(ri, np.arange(lo, hi), window)
+            keys = _block_keys(ri, window)
+            kt, vv = keys_of(b, kv, keys, kt_all, v_all)
+            mask = visible_mask(ri, keys, window)
             for h in range(kv * grp, (kv + 1) * grp):
-                s = sc * (qt[b, idx, h] @ kt[lo:hi].T)
+                s = sc * (qt[b, idx, h] @ kt.T)
                 p = _softmax_rows(s, mask)
-                out[b, idx, h] = p @ vv[lo:hi]
+                out[b, idx, h] = p @ vv
 
     jobs = [(b, kv) for b in range(B) for kv in range(Hkv)]
     if threads > 1:

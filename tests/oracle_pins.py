@@ -160,6 +160,29 @@ def pin_brute_force():
         assert np.allclose(got, want, rtol=0, atol=1e-12), (n, np.abs(got - want).max())
 
 
+def pin_row_blocks_and_threads():
+    """``prefill_rows`` as the long-context checks run it -- shuffled, sparse rows taken in
+    blocks of 8 (so most blocks' key ranges start past position 0), four (batch, KV head)
+    jobs on a 4-thread pool -- equals the pure-Python brute force, for a global layer and
+    two windows."""
+    B, T, Hq, Hkv, d, r, po = 2, 97, 4, 2, 8, 4, 3
+    q = _rand((B, T, Hq, d), 70)
+    k = _rand((B, T, Hkv, d), 71)
+    v = _rand((B, T, Hkv, d), 72)
+    g = _rand((B, T, Hq, d), 73)
+    wq = 1 + 0.1 * _rand((d,), 74)
+    wk = 1 + 0.1 * _rand((d,), 75)
+    rng = np.random.default_rng(76)
+    rows = rng.permutation(np.concatenate([[0, 1, T - 1],
+                                           rng.choice(np.arange(2, T - 1), 50, replace=False)]))
+    for W in (None, 5, 16):
+        gg = None if W is None else g
+        want = brute_prefill(q, k, v, gg, wq, wk, W, r, pos_offset=po)[:, rows]
+        got = O.prefill_rows(q, k, v, gg, wq, wk, rows, window=W, rotary_dim=r, pos_offset=po,
+                             row_block=8, threads=4)
+        assert np.allclose(got, want, rtol=0, atol=1e-12), (W, np.nanmax(np.abs(got - want)))
+
+
 def pin_sdpa_rotary0():
     """rotary_dim 0: plain GQA attention on normed q/k == torch SDPA (fp64, explicit mask)."""
     import torch

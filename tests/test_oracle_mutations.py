@@ -106,6 +106,11 @@ def _varlen_sees_previous_document(q, k, v, g, wq, wk, cu_seqlens, **kw):
     return out
 
 
+def _block_keys_lo_off_by_one(ri, window):
+    # a row block's key range starts one key late (its first visible key is dropped)
+    return _ORIG["_block_keys"](ri, window)[1:]
+
+
 from oracle import grad as OG
 
 _ORIG_GRADS = OG.prefill_grads
@@ -126,7 +131,8 @@ def _grads_dk_not_summed_over_group(*a, **kw):
 
 
 _ORIG = {n: getattr(O, n) for n in ("partial_rope", "rmsnorm", "visible_mask", "sigmoid",
-                                     "kv_bytes_per_token", "layer_kinds", "prefill_varlen")}
+                                     "kv_bytes_per_token", "layer_kinds", "prefill_varlen",
+                                     "_block_keys")}
 
 MUTANTS = {
     "rope_sign": ("partial_rope", _rope_sign_flipped),
@@ -143,6 +149,7 @@ MUTANTS = {
     "grad_wk_forgotten": (OG, "prefill_grads", _grads_wk_forgotten),
     "grad_dk_one_head": (OG, "prefill_grads", _grads_dk_not_summed_over_group),
     "varlen_crosses_documents": ("prefill_varlen", _varlen_sees_previous_document),
+    "row_block_lo_off_by_one": ("_block_keys", _block_keys_lo_off_by_one),
 }
 
 PINS = [getattr(P, n) for n in dir(P) if n.startswith("pin_")]
@@ -157,6 +164,6 @@ def test_some_pin_catches(mutant, monkeypatch):
     for pin in PINS:
         try:
             pin()
-        except (AssertionError, ValueError, FloatingPointError):
+        except (AssertionError, ValueError, FloatingPointError, IndexError):
             caught.append(pin.__name__)
     assert caught, f"no pin detects the planted mistake {mutant}"
