@@ -7,6 +7,7 @@ library; the first call does, and raises if the library has not been built.
 
 from .api import (  # noqa: F401
     global_decode,
+    global_decode_noalloc,
     global_decode_workspace_bytes,
     global_prefill,
     global_prefill_varlen,

@@ -60,6 +60,7 @@ SIGNATURES = {
     "zgattn_swa_decode": (ctypes.c_int, [DP, P, P, P, P, P, P, P, P, P, P, P]),
     "zgattn_global_decode": (ctypes.c_int, [DP, P, P, P, P, P, P, P, I32, P, P, SZ, P, P]),
     "zgattn_global_decode_workspace_bytes": (SZ, [DP, I32]),
+    "zgattn_global_decode_noalloc": (ctypes.c_int, [DP, P, P, P, P, P, P, P, I32, P, P, P]),
     "zgattn_qknorm_rope": (ctypes.c_int, [DP, I32, P, P, P, P, I64, I64, I64, P]),
     "zgattn_swa_prefill_varlen": (ctypes.c_int, [DP, P, I32, I32, P, P, P, P, P, P, P, P]),
     "zgattn_prefill_backward_workspace_bytes": (SZ, [DP]),

@@ -210,6 +210,26 @@ def global_decode(q, k_new, v_new, wq, wk, k_cache, v_cache, pos, *, rotary_dim=
     return out
 
 
+def global_decode_noalloc(q, k_new, v_new, wq, wk, k_cache, v_cache, pos, *, rotary_dim=None,
+                          rope_base=10000.0, eps=1e-6, scale=0.0, out=None):
+    """global_decode with the library's own per-GPU scratch instead of a workspace: the C
+    call allocates nothing (pass ``out`` to keep this wrapper from allocating either).
+    Calls that overlap on one GPU race on the shared scratch."""
+    _dev(q, k_new, v_new, wq, wk, k_cache, v_cache, pos, out)
+    if pos.dtype != torch.int32:
+        raise TypeError("pos must be int32")
+    if out is None:
+        out = torch.empty_like(q)
+    cap = k_cache.shape[2]
+    d = _decode_desc(q, k_new, 1, rotary_dim, rope_base, eps, scale)
+    check(lib().zgattn_global_decode_noalloc(ctypes.byref(d), _ptr(q), _ptr(k_new),
+                                             _ptr(v_new), _ptr(wq), _ptr(wk), _ptr(k_cache),
+                                             _ptr(v_cache), cap, _ptr(pos), _ptr(out),
+                                             _stream()),
+          "zgattn_global_decode_noalloc")
+    return out
+
+
 def qknorm_rope(x, w, *, pos=None, rotary_dim=None, pos_offset=0, rope_base=10000.0,
                 eps=1e-6, out=None):
     """RMSNorm + partial RoPE of x [B,T,H,d]. ``out`` may be any strided view with the

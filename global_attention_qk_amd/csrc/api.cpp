@@ -320,6 +320,27 @@ int zgattn_global_decode(const zgattn_desc* d, const void* q, const void* k_new,
   return hip_status(launch_global_decode(a, (hipStream_t)stream));
 }
 
+int zgattn_global_decode_noalloc(const zgattn_desc* d, const void* q, const void* k_new,
+                                 const void* v_new, const float* wq, const float* wk,
+                                 void* k_cache, void* v_cache, int32_t capacity,
+                                 const int32_t* pos, void* out, void* stream) {
+  int st = decode_common(d, q, k_new, v_new, wq, wk, k_cache, v_cache, pos, out);
+  if (st) return st;
+  if (capacity < 1 || capacity > ZGATTN_MAX_POSITION + 1) return ZGATTN_ERANGE;
+  DecodeArgs a = make_decode(d, q, k_new, v_new, nullptr, wq, wk, k_cache, v_cache, pos, out);
+  size_t need;
+  if (!global_decode_geometry_capped(a.B, a.Hq, a.Hkv, a.d, capacity,
+                                     ZGATTN_NOALLOC_SCRATCH_BYTES, &a.nsplit, &a.chunk, &need))
+    return ZGATTN_EWORKSPACE;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  if (decode_noalloc_scratch(&ws, &ws_bytes) != hipSuccess) return ZGATTN_EHIP;
+  if (need > ws_bytes) return ZGATTN_EWORKSPACE;
+  a.S = capacity;
+  a.ws = (float*)ws;
+  return hip_status(launch_global_decode(a, (hipStream_t)stream));
+}
+
 size_t zgattn_model_decode_workspace_bytes(const zgattn_desc* d, int32_t n_layers,
                                            const int32_t* is_global, int32_t capacity) {
   if (check_desc(d) || n_layers < 0 || (n_layers > 0 && !is_global)) return 0;

@@ -17,12 +17,25 @@
 // SWA layers: one workgroup per (sequence, kv head) does the whole step over the ring
 // (MFMA scores with the ring in registers when it holds at most 128 slots, the model's
 // window; a per-slot kernel for larger rings).
+#include <mutex>
+
 #include "launch.h"
+#include "zgattn.h"
 
 namespace zg {
+
+// Scratch of zgattn_global_decode_noalloc: the split-K partials of a global decode step
+// for callers that cannot allocate. One copy per GPU, at its own address on each: host
+// code must never pass this name to a kernel, only the address that
+// hipGetSymbolAddress returns for the current device (decode_noalloc_scratch).
+static __device__ __align__(256) unsigned char scratch[ZGATTN_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device, or null
 
 __device__ __forceinline__ bool pos_valid(int pos, int limit) { return pos >= 0 && pos < limit; }
 
@@ -761,6 +774,42 @@ void global_decode_geometry(int B, int Hq, int d, int capacity, int* nsplit, int
   *nsplit = ns;
   *chunk = c;
   *ws_bytes = ((size_t)B * Hq * d * (1 + (size_t)ns) + (size_t)B * Hq * ns * 2) * 4;
+}
+
+bool global_decode_geometry_capped(int B, int Hq, int Hkv, int d, int capacity,
+                                   size_t max_bytes, int* nsplit, int* chunk,
+                                   size_t* ws_bytes) {
+  global_decode_geometry(B, Hq, d, capacity, nsplit, chunk, ws_bytes);
+  const int G = Hq / Hkv;
+  const size_t max_lds = 160 * 1024;   // the split kernel keeps chunk x G scores in LDS
+  while (*ws_bytes > max_bytes) {
+    if (*nsplit == 1) return false;
+    const int c = *chunk * 2;
+    if ((size_t)c * G * 4 > max_lds) return false;
+    *chunk = c;
+    *nsplit = (capacity + c - 1) / c;
+    *ws_bytes = ((size_t)B * Hq * d * (1 + (size_t)*nsplit) + (size_t)B * Hq * *nsplit * 2) * 4;
+  }
+  return true;
+}
+
+hipError_t decode_noalloc_scratch(void** ptr, size_t* bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    // once per device, with that device current
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  *bytes = sizeof(scratch);
+  return hipSuccess;
 }
 
 hipError_t launch_global_decode(const DecodeArgs& a, hipStream_t s) {

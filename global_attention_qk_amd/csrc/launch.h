@@ -142,5 +142,13 @@ hipError_t launch_global_decode(const DecodeArgs& a, hipStream_t s);
 // Split-K geometry and workspace bytes for a global decode call.
 void global_decode_geometry(int B, int Hq, int d, int capacity, int* nsplit, int* chunk,
                             size_t* ws_bytes);
+// The same geometry with chunks lengthened (doubled) until the workspace fits max_bytes
+// and the split kernel's LDS stays within a CU; false when no such geometry exists.
+bool global_decode_geometry_capped(int B, int Hq, int Hkv, int d, int capacity,
+                                   size_t max_bytes, int* nsplit, int* chunk,
+                                   size_t* ws_bytes);
+// Device address of the current device's no-allocation decode scratch (looked up once per
+// device) and its size in bytes.
+hipError_t decode_noalloc_scratch(void** ptr, size_t* bytes);
 
 }  // namespace zg

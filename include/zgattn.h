@@ -190,6 +190,27 @@ int zgattn_global_decode(const zgattn_desc* desc, const void* q, const void* k_n
 size_t zgattn_global_decode_workspace_bytes(const zgattn_desc* desc, int32_t capacity);
 
 /*
+ * zgattn_global_decode without a caller workspace and without any allocation, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. Arguments, outputs and cache update are those of
+ * zgattn_global_decode. The split-K partials go to a scratch array of
+ * ZGATTN_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on, until the
+ * process ends. The same kernels run; when zgattn_global_decode's split geometry would need
+ * more scratch than that, this call takes longer cache chunks (fewer splits), which
+ * changes only the rounding. If the partials cannot fit even so (roughly
+ * B * Hq * head_dim * 8 bytes above the limit) the call returns ZGATTN_EWORKSPACE before
+ * anything is launched. All calls on one GPU share its scratch: calls that overlap on one
+ * GPU (other streams, or threads without ordering between them) race and give undefined
+ * outputs; calls ordered on one stream are safe. Nothing in the scratch needs clearing
+ * between calls: every value a step reads was written earlier in the same step.
+ */
+#define ZGATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int zgattn_global_decode_noalloc(const zgattn_desc* desc, const void* q, const void* k_new,
+                                 const void* v_new, const float* wq, const float* wk,
+                                 void* k_cache, void* v_cache, int32_t capacity,
+                                 const int32_t* pos, void* out, void* stream);
+
+/*
  * One decode step of a whole layer stack (explainer, section アーキテクチャ: 27 gated SWA
  * layers with a fixed 128-token cache and 5 global layers with the full sequence; the
  * jaehun.me review, section "KV 캐시가 6.4배 줄어드는 이유": 20 KiB of KV per token for the

@@ -18,7 +18,7 @@ FAKE = ctypes.c_void_p(4096)  # never dereferenced: every call below fails valid
 def test_exports_every_declared_symbol():
     lib = L.lib()
     declared = L.header_symbols()
-    assert len(declared) == 17
+    assert len(declared) == 18
     for name in declared:
         assert hasattr(lib, name), name
     assert set(declared) == set(L.SIGNATURES)
@@ -107,6 +107,21 @@ def test_decode_checks():
     st = lib.zgattn_swa_decode(ctypes.byref(_d(window=0, n_q_heads=32, n_kv_heads=8)), FAKE,
                                FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
     assert st == -1
+
+
+def test_decode_noalloc_checks():
+    # rejections happen on the host, before the scratch is looked up or anything launches
+    lib = L.lib()
+    call = lambda d, cap=4096, pos=FAKE: lib.zgattn_global_decode_noalloc(
+        ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, cap, pos, FAKE, None)
+    ok = _d(batch=4, seq_len=1, n_q_heads=32, n_kv_heads=8)
+    assert call(ok, cap=0) == -6
+    assert call(ok, pos=None) == -2
+    assert call(_d(dtype=L.F32, n_q_heads=32, n_kv_heads=8)) == -4
+    # partials of B * Hq * d = 2^23 values need 2 * 4 * 2^23 bytes even with one split:
+    # more than the 64 MiB scratch
+    big = _d(batch=1024, seq_len=1, n_q_heads=64, n_kv_heads=8)
+    assert call(big, cap=262144) == -5
 
 
 def test_qknorm_rope_checks():
