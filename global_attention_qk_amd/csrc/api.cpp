@@ -274,9 +274,9 @@ int zgattn_global_prefill(const zgattn_desc* d, const void* q, const void* k, co
     n.fr = a.fr;
     hipError_t e = launch_qknorm_rope(n, s);
     if (e != hipSuccess) return ZGATTN_EHIP;
-    a.kt = (bf16*)workspace;
+    a.kt = workspace;
     const size_t kbytes = (size_t)a.B * a.Hkv * (size_t)a.T * a.d * 2;
-    a.vt = (bf16*)((char*)workspace + ((kbytes + 255) & ~(size_t)255));
+    a.vt = (void*)((char*)workspace + ((kbytes + 255) & ~(size_t)255));
     e = launch_v_tiles(a, s);
     if (e != hipSuccess) return ZGATTN_EHIP;
   }
@@ -434,9 +434,9 @@ int zgattn_global_prefill_varlen(const zgattn_desc* d, const int32_t* cu_seqlens
     n.n_docs = n_docs;
     hipError_t e = launch_qknorm_rope(n, s);
     if (e != hipSuccess) return ZGATTN_EHIP;
-    a.kt = (bf16*)workspace;
+    a.kt = workspace;
     const size_t kbytes = (size_t)a.Hkv * (size_t)a.T * a.d * 2;
-    a.vt = (bf16*)((char*)workspace + ((kbytes + 255) & ~(size_t)255));
+    a.vt = (void*)((char*)workspace + ((kbytes + 255) & ~(size_t)255));
     e = launch_v_tiles(a, s);
     if (e != hipSuccess) return ZGATTN_EHIP;
   }

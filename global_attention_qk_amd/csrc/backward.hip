@@ -18,6 +18,7 @@
 // MFMA, keys on the lanes so that P and dS are B operands as they come out of the
 // accumulators), the norm/RoPE backward for q and k rows with per-block weight partials,
 // and the reduction of those partials.
+#include "common.h"
 #include "launch.h"
 
 namespace zg {

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "types.h"
+
 namespace zg {
 
 typedef __bf16 bf16;
@@ -14,18 +16,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr int kMaxHalfRot = 64;  // rotary_dim / 2 <= 64 (d <= 128)
-// Positions must be exact in fp32 (|p| < 2^24).
-#define ZGATTN_POS_LIMIT (1 << 24)
-
-// Per-pair RoPE phase step in revolutions per position, f_k = base^(-2k/r) / (2 pi),
-// split into an fp32 head and tail (computed in double on the host) so that the phase
-// p * f_k keeps ~44 significant bits for positions up to 2^24.
-struct RopeFreq {
-  float hi[kMaxHalfRot];
-  float lo[kMaxHalfRot];
-};
 
 __device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

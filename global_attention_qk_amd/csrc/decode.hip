@@ -19,6 +19,7 @@
 // window; a per-slot kernel for larger rings).
 #include <mutex>
 
+#include "common.h"
 #include "launch.h"
 #include "zgattn.h"
 

@@ -1,11 +1,13 @@
 // Internal launch interface between the C ABI (api.cpp) and the kernel translation units.
 #pragma once
 
-#include <hip/hip_runtime.h>
+// Host-side only: it includes the HIP runtime API, not the device headers, so the C ABI
+// (api.cpp) builds with an ordinary C++ compiler too (the host-check test does so).
+#include <hip/hip_runtime_api.h>
 #include <stddef.h>
 #include <stdint.h>
 
-#include "common.h"
+#include "types.h"
 
 namespace zg {
 
@@ -24,8 +26,8 @@ struct PrefillArgs {
   void* out;
   const float* wq;
   const float* wk;
-  bf16* kt;           // normalised+rotated K, [B][Hkv][T][d] (global with workspace) or nullptr
-  bf16* vt;           // V as transposed 64-key tiles (with kt), see launch_v_tiles
+  void* kt;           // bf16 normalised+rotated K, [B][Hkv][T][d] (global with workspace) or nullptr
+  void* vt;           // bf16 V as transposed 64-key tiles (with kt), see launch_v_tiles
   int B, T, Hq, Hkv, d, window, rdim, pos_offset;
   int swa;            // 1: gated sliding window; 0: ungated full causal
   float eps;

@@ -35,6 +35,7 @@
 //     about three query tiles) the transform is fused into the tile load.
 #include <type_traits>
 
+#include "common.h"
 #include "launch.h"
 
 namespace zg {
@@ -1158,8 +1159,8 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
   ka.out = (bf16*)a.out;
   ka.wq = a.wq;
   ka.wk = a.wk;
-  ka.kt = a.kt;
-  ka.vt = a.vt;
+  ka.kt = (const bf16*)a.kt;
+  ka.vt = (const bf16*)a.vt;
   ka.T = a.T;
   ka.Hq = a.Hq;
   ka.Hkv = a.Hkv;
@@ -1214,10 +1215,10 @@ hipError_t launch_v_tiles(const PrefillArgs& a, hipStream_t s) {
   const int slots = packed ? varlen_vtile_slots(a.T, a.n_docs) : 0;
   if (n_kt == 0) return hipSuccess;
   if (a.d == 128)
-    hipLaunchKernelGGL(v_tiles_kernel<128>, grid, dim3(256), 0, s, (const bf16*)a.v, a.vt, a.T,
+    hipLaunchKernelGGL(v_tiles_kernel<128>, grid, dim3(256), 0, s, (const bf16*)a.v, (bf16*)a.vt, a.T,
                        a.Hkv, n_kt, a.cu, a.max_len, slots);
   else
-    hipLaunchKernelGGL(v_tiles_kernel<64>, grid, dim3(256), 0, s, (const bf16*)a.v, a.vt, a.T,
+    hipLaunchKernelGGL(v_tiles_kernel<64>, grid, dim3(256), 0, s, (const bf16*)a.v, (bf16*)a.vt, a.T,
                        a.Hkv, n_kt, a.cu, a.max_len, slots);
   return hipGetLastError();
 }

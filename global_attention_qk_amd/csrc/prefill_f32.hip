@@ -6,6 +6,7 @@
 // head; each lane owns one query row and keeps q~ and its output accumulator in
 // registers. K tiles are normalised+rotated once per visit in LDS, V tiles staged in LDS,
 // and every lane reads both with broadcast LDS loads. Any head group, rotary_dim <= d.
+#include "common.h"
 #include "launch.h"
 
 namespace zg {

@@ -36,6 +36,7 @@
 //     online-max variant runs (both are launched; each returns unless selected).
 #include <type_traits>
 
+#include "common.h"
 #include "launch.h"
 
 namespace zg {

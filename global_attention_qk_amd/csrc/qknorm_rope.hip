@@ -9,6 +9,7 @@
 // 32-byte (fp32) access to an arbitrarily strided destination (e.g. straight into a
 // [B, Hkv, S, d] cache). Packed documents restart positions at each document's first
 // token. Row indices are 32-bit (the launcher rejects more than 2^31 - 1 rows).
+#include "common.h"
 #include "launch.h"
 
 namespace zg {
