@@ -60,6 +60,9 @@ def parse():
                          "per-call protocol: 5 warm-ups, median/min/p90 of >= 20 calls "
                          "(>= 5 for the 256K global layer and the stack), caches flushed "
                          "before each call; one JSON line per configuration and layer")
+    ap.add_argument("--fused-k", action="store_true",
+                    help="with --only global_prefill: no workspace, the K transform fused into "
+                         "every K-tile load (the alternative to the K~ pre-pass)")
     ap.add_argument("--sweep-t", default="",
                     help="comma-separated sequence lengths for --sweep (default: all)")
     return ap.parse_args()
@@ -87,6 +90,87 @@ def measured_traffic():
         return float(kv["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None
+
+
+class ClockSampler:
+    """The GPU's current shader clock (amdsmi, MHz), sampled about every 20 ms by a thread
+    while the timed steps run. Reports nothing when amdsmi cannot be used."""
+
+    def __init__(self):
+        import threading
+        self.samples, self.error = [], None
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            try:
+                handles = amdsmi.amdsmi_get_processor_handles()
+                h = handles[0]
+                while not self._stop.is_set():
+                    self.samples.append(
+                        amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.SYS)["clk"])
+                    self._stop.wait(0.02)
+            finally:
+                amdsmi.amdsmi_shut_down()
+        except Exception as e:  # no amdsmi, no permission: no clock in the report
+            self.error = f"{type(e).__name__}: {e}"
+
+    def __enter__(self):
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join(timeout=5)
+
+    def report(self):
+        xs = [x for x in self.samples if isinstance(x, (int, float)) and x > 0]
+        if not xs:
+            return {"source": "amdsmi", "error": self.error or "no samples"}
+        ys = sorted(xs)
+        return {"source": "amdsmi current GFX clock during the timed steps (median: the "
+                          "sustained clock; idle gaps between calls give the low samples)",
+                "median_MHz": ys[len(ys) // 2], "mean_MHz": sum(xs) / len(xs),
+                "min_MHz": ys[0], "max_MHz": ys[-1], "samples": len(xs)}
+
+
+def measured_peaks():
+    """What this GPU sustains on plain library work, next to the spec peaks: a 1 GiB
+    device-to-device copy (read + write bytes / time) and a bf16 8192^3 matrix product
+    (torch / hipBLASLt), each the best of 10 timed runs after warm-up."""
+    import torch
+    out = {}
+
+    def best(fn, reps=10):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / 1e3)
+        return min(ts)
+
+    n = 1 << 30
+    x = torch.empty(n, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    x.fill_(3)
+    out["hbm_copy_GBs"] = 2 * n / best(lambda: y.copy_(x)) / 1e9
+    del x, y
+    m = 8192
+    a = torch.randn(m, m, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(m, m, device="cuda", dtype=torch.bfloat16)
+    c = torch.empty(m, m, device="cuda", dtype=torch.bfloat16)
+    out["bf16_gemm_TFLOPs"] = 2 * m ** 3 / best(lambda: torch.mm(a, b, out=c)) / 1e12
+    del a, b, c
+    torch.cuda.empty_cache()
+    return out
 
 
 def alg_counts(T, B, Hq, Hkv, d, W, Bdec, S):
@@ -173,11 +257,12 @@ def main():
         print(f"[bench] warmup step {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with ClockSampler() as clock:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(events[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     per = {n: [] for n in names}
     for ev in events:
         for j, n in enumerate(names):
@@ -245,8 +330,28 @@ def main():
         },
         "breakdown": breakdown,
     }
+    # Clock and measured peaks (after the timed steps): the spec peak assumes 2.4 GHz;
+    # the fraction at the clock the chip sustained shows what is left for the kernel.
+    sclk = clock.report()
+    rec["sclk"] = sclk
+    del out_s, out_g, ws
+    torch.cuda.empty_cache()
+    try:
+        peaks = measured_peaks()
+    except RuntimeError as e:   # e.g. out of memory next to the resident inputs
+        peaks = {"error": str(e)[:200]}
+    rec["measured_peaks"] = peaks
+    if "median_MHz" in sclk:
+        at_clock = PEAK_BF16_TFLOPS * sclk["median_MHz"] / 2400.0
+        rec["roofline"]["peak_at_sustained_sclk"] = at_clock
+        rec["roofline"]["frac_at_sustained_sclk"] = glob_tflops / at_clock
+    if "bf16_gemm_TFLOPs" in peaks:
+        rec["roofline"]["frac_of_measured_gemm"] = glob_tflops / peaks["bf16_gemm_TFLOPs"]
+    if "hbm_copy_GBs" in peaks:
+        for n in ("swa_prefill", "global_decode", "swa_decode"):
+            breakdown[n]["frac_of_measured_copy"] = breakdown[n]["hbm_GBs"] / peaks["hbm_copy_GBs"]
     if args.cpu_baseline == "on":
-        del q, k, v, g, out_s, out_g, ws
+        del q, k, v, g
         rec["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(rec), flush=True)
 
@@ -663,6 +768,9 @@ def run_only(args):
         out = torch.empty_like(q)
         if args.only == "swa_prefill":
             call = lambda: zg.swa_prefill(q, k, v, g, wq, wk, window=W, rotary_dim=r, out=out)
+        elif args.fused_k:
+            call = lambda: zg.global_prefill(q, k, v, wq, wk, rotary_dim=r, workspace=None,
+                                             out=out)
         else:
             ws = torch.empty(zg.global_prefill_workspace_bytes(q, k, rotary_dim=r),
                              dtype=torch.uint8, device=dev)
