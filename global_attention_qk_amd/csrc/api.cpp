@@ -235,9 +235,8 @@ int zgattn_swa_prefill(const zgattn_desc* d, const void* q, const void* k, const
 size_t zgattn_global_prefill_workspace_bytes(const zgattn_desc* d) {
   if (check_desc(d) || d->seq_len < 0) return 0;
   if (d->dtype != ZGATTN_BF16) return 0;
-  // normalised+rotated K, then V as transposed 64-key tiles (256-byte aligned)
-  const size_t kbytes = (size_t)d->batch * d->n_kv_heads * (size_t)d->seq_len * d->head_dim * 2;
-  return ((kbytes + 255) & ~(size_t)255) +
+  // normalised+rotated K (plus a tile of slack), then V as transposed 64-key tiles
+  return prefill_kt_bytes((size_t)d->batch * d->n_kv_heads * (size_t)d->seq_len, d->head_dim) +
          prefill_vtiles_bytes(d->batch, d->n_kv_heads, d->seq_len, d->head_dim);
 }
 
@@ -275,8 +274,7 @@ int zgattn_global_prefill(const zgattn_desc* d, const void* q, const void* k, co
     hipError_t e = launch_qknorm_rope(n, s);
     if (e != hipSuccess) return ZGATTN_EHIP;
     a.kt = workspace;
-    const size_t kbytes = (size_t)a.B * a.Hkv * (size_t)a.T * a.d * 2;
-    a.vt = (void*)((char*)workspace + ((kbytes + 255) & ~(size_t)255));
+    a.vt = (void*)((char*)workspace + prefill_kt_bytes((size_t)a.B * a.Hkv * a.T, a.d));
     e = launch_v_tiles(a, s);
     if (e != hipSuccess) return ZGATTN_EHIP;
   }
@@ -390,8 +388,7 @@ int zgattn_swa_prefill_varlen(const zgattn_desc* d, const int32_t* cu_seqlens, i
 size_t zgattn_global_prefill_varlen_workspace_bytes(const zgattn_desc* d, int32_t n_docs) {
   if (check_desc(d) || d->seq_len < 0 || d->batch != 1 || n_docs < 1) return 0;
   if (d->dtype != ZGATTN_BF16) return 0;
-  const size_t kbytes = (size_t)d->n_kv_heads * (size_t)d->seq_len * d->head_dim * 2;
-  return ((kbytes + 255) & ~(size_t)255) +
+  return prefill_kt_bytes((size_t)d->n_kv_heads * d->seq_len, d->head_dim) +
          prefill_vtiles_bytes_varlen(d->n_kv_heads, d->seq_len, n_docs, d->head_dim);
 }
 
@@ -435,8 +432,7 @@ int zgattn_global_prefill_varlen(const zgattn_desc* d, const int32_t* cu_seqlens
     hipError_t e = launch_qknorm_rope(n, s);
     if (e != hipSuccess) return ZGATTN_EHIP;
     a.kt = workspace;
-    const size_t kbytes = (size_t)a.Hkv * (size_t)a.T * a.d * 2;
-    a.vt = (void*)((char*)workspace + ((kbytes + 255) & ~(size_t)255));
+    a.vt = (void*)((char*)workspace + prefill_kt_bytes((size_t)a.Hkv * a.T, a.d));
     e = launch_v_tiles(a, s);
     if (e != hipSuccess) return ZGATTN_EHIP;
   }

@@ -39,6 +39,14 @@ struct PrefillArgs {
   int n_docs = 0;
   int max_len = 0;
 };
+// Rows of slack after the last K~ row of the global-prefill workspace: a 64-key tile that
+// starts at the last row stays inside the workspace without clamping its row indices.
+constexpr int kKtSlackRows = 64;
+// Bytes of the K~ part of the global-prefill workspace (rows of all heads + slack), and
+// where the V tiles start (256-byte aligned).
+inline size_t prefill_kt_bytes(size_t rows, int d) {
+  return ((rows + kKtSlackRows) * d * 2 + 255) & ~(size_t)255;
+}
 // V-tile slots per KV head of a packed batch (see doc_tile_base).
 inline int varlen_vtile_slots(int T, int n_docs) { return T / 64 + n_docs; }
 size_t prefill_vtiles_bytes_varlen(int Hkv, int T, int n_docs, int d);

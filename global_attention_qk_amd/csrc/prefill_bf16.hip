@@ -582,16 +582,24 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p, const int lin, cons
   // are clamped to the last row (masked keys).
   constexpr int KPW = D / 32;
   const uint32_t lds_smem = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
+  // Per-lane source offsets of the K~ pieces within a tile (row r of the tile, chunk c),
+  // the same for every tile. A tile past the sequence end reads on into the next head's
+  // rows or the workspace's kKtSlackRows rows of slack: always inside the workspace, and
+  // such keys are always masked (their scores are replaced, not used), so no row is
+  // clamped.
+  constexpr int CPR = D / 8, RPB = 1024 / (2 * D);
+  static_assert(kKtSlackRows >= kBN, "a whole tile of slack past the last K~ row");
+  uint32_t kdma_off[KPW];
+#pragma unroll
+  for (int j = 0; j < KPW; ++j) {
+    const int r = (wave * KPW + j) * RPB + lane / CPR;
+    kdma_off[j] = (uint32_t)(r * (2 * D) + chunk_pos<CPR>(r, lane % CPR) * 16);
+  }
   auto dma_piece = [&](int kt, int buf, int j) {
     const uint32_t dst = lds_smem + buf * S::kDBuf;
     const int k0 = kt * kBN;
     if (j < KPW) {
-      constexpr int CPR = D / 8, RPB = 1024 / (2 * D);
-      const int blk = wave * KPW + j;
-      const int r = blk * RPB + lane / CPR;
-      const int c = chunk_pos<CPR>(r, lane % CPR);
-      dma16(ktsrc + (size_t)k0 * D, (uint32_t)(min(r, T - 1 - k0) * (2 * D) + c * 16),
-            dst + blk * 1024);
+      dma16(ktsrc + (size_t)k0 * D, kdma_off[j], dst + (wave * KPW + j) * 1024);
     } else {
       const int blk = wave * KPW + (j - KPW);
       const int d = blk * 8 + (lane >> 3);
