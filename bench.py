@@ -60,6 +60,11 @@ def parse():
                          "per-call protocol: 5 warm-ups, median/min/p90 of >= 20 calls "
                          "(>= 5 for the 256K global layer and the stack), caches flushed "
                          "before each call; one JSON line per configuration and layer")
+    ap.add_argument("--flush", choices=["read", "write"], default="read",
+                    help="with --configs: evict the caches before each call by reading a 1 GiB "
+                         "buffer (default) or by writing one; a written buffer leaves the "
+                         "memory-side cache full of dirty lines whose write-back then shares "
+                         "HBM with the measured call")
     ap.add_argument("--fused-k", action="store_true",
                     help="with --only global_prefill: no workspace, the K transform fused into "
                          "every K-tile load (the alternative to the K~ pre-pass)")
@@ -632,14 +637,27 @@ def run_configs(args):
     stack), with a 1 GiB buffer written before every call so that neither L2 nor the
     256 MB Infinity Cache still holds the inputs; HIP events around the call only. Prints
     one JSON line per (configuration, layer) with median, min and p90, tokens/s, the
-    roofline fraction and the target."""
+    roofline fraction and the target.
+
+    The default flush reads the 1 GiB buffer (a sum over it), which evicts the inputs just
+    as a write does but leaves clean lines behind. A written buffer leaves up to 256 MB of
+    dirty lines in the memory-side cache, and their write-back (about 32 us at 8 TB/s) is
+    then charged to the next call: a plain read of 453 MB takes about 25 % longer after a
+    write flush than after a read flush, which matters for the microsecond decode calls
+    and not for the millisecond prefill layers. The flush also keeps the GPU busy while
+    the host prepares the measured call, so that the first event does not time the host."""
     import torch
 
     import global_attention_qk_amd as zg
     from workloads import C1, C2, C3, C4, C5, STACKS, decode_inputs, prefill_inputs, stack_kinds
 
     dev = "cuda"
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+    if args.flush == "read":
+        evict = lambda: torch.sum(flush, dim=0, out=sink)
+    else:
+        evict = lambda: flush.fill_(7.0)
 
     def timed(fn, reps):
         for _ in range(5):
@@ -647,7 +665,7 @@ def run_configs(args):
         torch.cuda.synchronize()
         ts = []
         for _ in range(reps):
-            flush.fill_(7)
+            evict()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             fn()
@@ -659,7 +677,8 @@ def run_configs(args):
 
     def emit(cfg, layer, ts, tokens, bound, work):
         med = ts[len(ts) // 2]
-        rec = {"config": cfg, "layer": layer, "reps": len(ts), "median_ms": med,
+        rec = {"config": cfg, "layer": layer, "flush": args.flush, "reps": len(ts),
+               "median_ms": med,
                "min_ms": ts[0], "p90_ms": ts[min(len(ts) - 1, (9 * len(ts)) // 10)],
                "tokens_per_s": tokens / (med / 1e3) if tokens else None}
         if bound == "mfma":
@@ -745,6 +764,14 @@ def run_configs(args):
     ts = timed(lambda: zg.model_decode(swa_layers, pos, window=W, rotary_dim=r), 20)
     emit("C5", "swa_decode_batched_per_layer", [t / 27 for t in ts], C5.B, "hbm",
          cnt["sdec_bytes"])
+    # context for the line above: a library read (torch.sum) of the 27 layers' ring bytes
+    ring_bytes = sum(x["k_cache"].numel() * x["k_cache"].element_size() * 2
+                     for x in swa_layers)
+    del swa_layers
+    buf = torch.ones(ring_bytes // 4, dtype=torch.float32, device=dev)
+    out0 = torch.empty((), dtype=torch.float32, device=dev)
+    ts = timed(lambda: torch.sum(buf, dim=0, out=out0), 20)
+    emit("C5", "plain_read_of_27_rings", ts, 0, "hbm", ring_bytes)
 
 
 def run_only(args):
