@@ -462,14 +462,19 @@ def run_backward(args):
     ws = torch.empty(zg.prefill_backward_workspace_bytes(q, k), dtype=torch.uint8, device=dev)
     cnt = alg_counts(T, C3.B, C3.Hq, C3.Hkv, C3.d, W, 1, 1)
     res = {}
-    for kind in ("swa", "global"):
+    # "global" hands the forward's row log-sum-exp to the backward (the training path);
+    # "global_recompute_lse" lets the backward recompute it
+    for kind in ("swa", "global", "global_recompute_lse"):
         gg = g if kind == "swa" else None
+        lse = None
         if kind == "swa":
             out = zg.swa_prefill(q, k, v, g, wq, wk, window=W, rotary_dim=r)
         else:
-            out = zg.global_prefill(q, k, v, wq, wk, rotary_dim=r)
+            if kind == "global":
+                lse = torch.empty((C3.B, C3.Hq, T), dtype=torch.float32, device=dev)
+            out = zg.global_prefill(q, k, v, wq, wk, rotary_dim=r, lse=lse)
         fn = lambda: zg.prefill_backward(q, k, v, gg, wq, wk, out, dout, window=W,
-                                         rotary_dim=r, workspace=ws)
+                                         rotary_dim=r, workspace=ws, lse=lse)
         fn()
         torch.cuda.synchronize()
         ts = []
@@ -482,6 +487,7 @@ def run_backward(args):
             ts.append(e0.elapsed_time(e1))
         ms = sorted(ts)[len(ts) // 2]
         flops = 2.5 * cnt["swa_flops" if kind == "swa" else "glob_flops"]
+        del out
         res[kind] = {"ms": round(ms, 3), "tokens_per_s": T / (ms / 1e3),
                      "tflops": flops / (ms / 1e3) / 1e12,
                      "mfma_frac": flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS}

@@ -55,7 +55,7 @@ SIGNATURES = {
     "zgattn_abi_version": (ctypes.c_int, []),
     "zgattn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "zgattn_swa_prefill": (ctypes.c_int, [DP, P, P, P, P, P, P, P, P]),
-    "zgattn_global_prefill": (ctypes.c_int, [DP, P, P, P, P, P, P, SZ, P, P]),
+    "zgattn_global_prefill": (ctypes.c_int, [DP, P, P, P, P, P, P, SZ, P, P, P]),
     "zgattn_global_prefill_workspace_bytes": (SZ, [DP]),
     "zgattn_swa_decode": (ctypes.c_int, [DP, P, P, P, P, P, P, P, P, P, P, P]),
     "zgattn_global_decode": (ctypes.c_int, [DP, P, P, P, P, P, P, P, I32, P, P, SZ, P, P]),
@@ -65,7 +65,7 @@ SIGNATURES = {
     "zgattn_swa_prefill_varlen": (ctypes.c_int, [DP, P, I32, I32, P, P, P, P, P, P, P, P]),
     "zgattn_prefill_backward_workspace_bytes": (SZ, [DP]),
     "zgattn_swa_prefill_backward": (ctypes.c_int, [DP] + [P] * 15 + [SZ, P]),
-    "zgattn_global_prefill_backward": (ctypes.c_int, [DP] + [P] * 13 + [SZ, P]),
+    "zgattn_global_prefill_backward": (ctypes.c_int, [DP] + [P] * 14 + [SZ, P]),
     "zgattn_global_prefill_varlen": (ctypes.c_int, [DP, P, I32, I32, P, P, P, P, P, P, SZ, P,
                                                     P]),
     "zgattn_global_prefill_varlen_workspace_bytes": (SZ, [DP, I32]),

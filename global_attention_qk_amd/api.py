@@ -83,10 +83,14 @@ def global_prefill_workspace_bytes(q, k, rotary_dim=None) -> int:
 
 
 def global_prefill(q, k, v, wq, wk, *, rotary_dim=None, pos_offset=0, rope_base=10000.0,
-                   eps=1e-6, scale=0.0, workspace="auto", out=None):
+                   eps=1e-6, scale=0.0, workspace="auto", out=None, lse=None):
     """Ungated full-causal layer. ``workspace``: "auto" allocates the K~ buffer, None runs
-    the fused-K variant, or a caller-owned uint8 CUDA tensor."""
-    _dev(q, k, v, wq, wk, out)
+    the fused-K variant, or a caller-owned uint8 CUDA tensor. ``lse``: an fp32 CUDA tensor
+    [B, Hq, T] that receives each row's log-sum-exp (for ``prefill_backward``), or None."""
+    _dev(q, k, v, wq, wk, out, lse)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != (q.shape[0], q.shape[2], q.shape[1])):
+        raise ValueError("lse must be a contiguous float32 tensor [B, Hq, T]")
     if out is None:
         out = torch.empty_like(q)
     d = _prefill_desc(q, k, 1, rotary_dim, pos_offset, rope_base, eps, scale)
@@ -97,7 +101,8 @@ def global_prefill(q, k, v, wq, wk, *, rotary_dim=None, pos_offset=0, rope_base=
     ws_ptr = _ptr(workspace)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     check(lib().zgattn_global_prefill(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(wq),
-                                      _ptr(wk), ws_ptr, nbytes, _ptr(out), _stream()),
+                                      _ptr(wk), ws_ptr, nbytes, _ptr(out), _ptr(lse),
+                                      _stream()),
           "zgattn_global_prefill")
     return out
 
@@ -311,12 +316,16 @@ def prefill_backward_workspace_bytes(q, k) -> int:
 
 
 def prefill_backward(q, k, v, g, wq, wk, out, dout, *, window=None, rotary_dim=None,
-                     pos_offset=0, rope_base=10000.0, eps=1e-6, scale=0.0, workspace=None):
+                     pos_offset=0, rope_base=10000.0, eps=1e-6, scale=0.0, workspace=None,
+                     lse=None):
     """Gradients of sum(dout * out) for the layer that produced ``out``: a gated SWA layer
-    when ``g`` is given (``window`` its width), else the global layer. Returns dq, dk, dv,
-    dg (None for the global layer), dwq, dwk."""
-    _dev(q, k, v, g, wq, wk, out, dout)
+    when ``g`` is given (``window`` its width), else the global layer. ``lse``: the global
+    forward's row log-sum-exp (``global_prefill(..., lse=...)``), or None to recompute it.
+    Returns dq, dk, dv, dg (None for the global layer), dwq, dwk."""
+    _dev(q, k, v, g, wq, wk, out, dout, lse)
     swa = g is not None
+    if lse is not None and swa:
+        raise ValueError("lse is taken by the global layer's backward only")
     d = _prefill_desc(q, k, window if swa else 1, rotary_dim, pos_offset, rope_base, eps, scale)
     if workspace is None:
         n = int(lib().zgattn_prefill_backward_workspace_bytes(ctypes.byref(d)))
@@ -334,6 +343,6 @@ def prefill_backward(q, k, v, g, wq, wk, out, dout, *, window=None, rotary_dim=N
     else:
         check(lib().zgattn_global_prefill_backward(
             ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(wq), _ptr(wk), _ptr(out),
-            _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dwq), _ptr(dwk), _ptr(workspace), nb,
-            _stream()), "zgattn_global_prefill_backward")
+            _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dwq), _ptr(dwk),
+            _ptr(workspace), nb, _stream()), "zgattn_global_prefill_backward")
     return dq, dk, dv, dg, dwq, dwk

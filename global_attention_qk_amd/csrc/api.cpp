@@ -242,11 +242,14 @@ size_t zgattn_global_prefill_workspace_bytes(const zgattn_desc* d) {
 
 int zgattn_global_prefill(const zgattn_desc* d, const void* q, const void* k, const void* v,
                           const float* wq, const float* wk, void* workspace,
-                          size_t workspace_bytes, void* out, void* stream) {
+                          size_t workspace_bytes, void* out, float* lse, void* stream) {
   int st = prefill_common(d, q, k, v, wq, wk, out);
   if (st) return st;
+  if (lse && ((uintptr_t)lse & 3)) return ZGATTN_EINVAL;
+  if (lse && d->dtype != ZGATTN_BF16) return ZGATTN_EUNSUPPORTED;
   if (d->seq_len == 0) return ZGATTN_OK;
   PrefillArgs a = make_prefill(d, q, k, v, nullptr, wq, wk, out, 0);
+  a.lse = lse;
   hipStream_t s = (hipStream_t)stream;
   if (d->dtype == ZGATTN_F32) return hip_status(launch_prefill_f32(a, s));
   if (!prefill_bf16_supported(a.d, a.Hq / a.Hkv, a.rdim)) return ZGATTN_EUNSUPPORTED;
@@ -447,10 +450,12 @@ size_t zgattn_prefill_backward_workspace_bytes(const zgattn_desc* d) {
 
 int backward_common(const zgattn_desc* d, int swa, const void* q, const void* k, const void* v,
                     const void* g, const float* wq, const float* wk, const void* out,
-                    const void* dout, void* dq, void* dk, void* dv, void* dg, float* dwq,
-                    float* dwk, void* workspace, size_t workspace_bytes, void* stream) {
+                    const float* lse, const void* dout, void* dq, void* dk, void* dv, void* dg,
+                    float* dwq, float* dwk, void* workspace, size_t workspace_bytes,
+                    void* stream) {
   int st = prefill_common(d, q, k, v, wq, wk, const_cast<void*>(out));
   if (st) return st;
+  if (lse && ((uintptr_t)lse & 3)) return ZGATTN_EINVAL;
   if (swa && d->window < 1) return ZGATTN_EINVAL;
   if (d->seq_len == 0) return ZGATTN_OK;
   if (!dout || !dq || !dk || !dv || !dwq || !dwk || (swa && (!g || !dg))) return ZGATTN_ENULL;
@@ -478,6 +483,7 @@ int backward_common(const zgattn_desc* d, int swa, const void* q, const void* k,
   a.dg = swa ? dg : nullptr;
   a.dwq = dwq;
   a.dwk = dwk;
+  a.lse = lse;
   a.ws = workspace;
   a.B = d->batch;
   a.T = d->seq_len;
@@ -500,17 +506,17 @@ int zgattn_swa_prefill_backward(const zgattn_desc* d, const void* q, const void*
                                 void* dv, void* dg, float* dwq, float* dwk, void* workspace,
                                 size_t workspace_bytes, void* stream) {
   if (!g && d && d->seq_len > 0) return check_desc(d) ? check_desc(d) : ZGATTN_ENULL;
-  return backward_common(d, 1, q, k, v, g, wq, wk, out, dout, dq, dk, dv, dg, dwq, dwk,
-                         workspace, workspace_bytes, stream);
+  return backward_common(d, 1, q, k, v, g, wq, wk, out, nullptr, dout, dq, dk, dv, dg, dwq,
+                         dwk, workspace, workspace_bytes, stream);
 }
 
 int zgattn_global_prefill_backward(const zgattn_desc* d, const void* q, const void* k,
                                    const void* v, const float* wq, const float* wk,
-                                   const void* out, const void* dout, void* dq, void* dk,
-                                   void* dv, float* dwq, float* dwk, void* workspace,
-                                   size_t workspace_bytes, void* stream) {
-  return backward_common(d, 0, q, k, v, nullptr, wq, wk, out, dout, dq, dk, dv, nullptr, dwq,
-                         dwk, workspace, workspace_bytes, stream);
+                                   const void* out, const float* lse, const void* dout,
+                                   void* dq, void* dk, void* dv, float* dwq, float* dwk,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  return backward_common(d, 0, q, k, v, nullptr, wq, wk, out, lse, dout, dq, dk, dv, nullptr,
+                         dwq, dwk, workspace, workspace_bytes, stream);
 }
 
 int zgattn_model_decode(const zgattn_desc* d, int32_t n_layers, const int32_t* is_global,

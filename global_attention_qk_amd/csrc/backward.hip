@@ -18,6 +18,8 @@
 // MFMA, keys on the lanes so that P and dS are B operands as they come out of the
 // accumulators), the norm/RoPE backward for q and k rows with per-block weight partials,
 // and the reduction of those partials.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -54,13 +56,14 @@ struct BArgs {
   const bf16* g;      // gate pre-activation (SWA) or nullptr
   const bf16* out;    // forward output O
   const bf16* dout;
-  const bf16* qt;     // Q~ [B][Hq][T][D] (workspace)
+  const bf16* qt;     // Q~ * scale * log2(e), [B][Hq][T][D] (workspace)
   const bf16* kt;     // K~ [B][Hkv][T][D] (workspace)
   bf16* da;           // dA [B][T][Hq][D] (workspace; dout itself for the global layer)
   float* dsum;        // D [B][Hq][T]
   float* lse;         // row log-sum-exp, log2 units [B][Hq][T]
+  const float* lse_in;  // the forward's row log-sum-exp, natural log [B][Hq][T], or nullptr
   const bf16* ktT;    // K~^T tiles [B][Hkv][n64][D][64], keys in slot order (workspace)
-  const bf16* qtT;    // Q~^T tiles [B][Hq][n64][D][64]
+  const bf16* qtT;    // the same as Q~^T tiles [B][Hq][n64][D][64]
   const bf16* daT;    // dA^T tiles [B][Hq][n64][D][64]
   float* dqt;         // dq~ [B][T][Hq][D] fp32
   float* dkt;         // dk~ [B][T][Hkv][D] fp32
@@ -270,9 +273,10 @@ __global__ __launch_bounds__(kTDQ) void bwd_dq_kernel(const BArgs p) {
       acc = mfma32(*(const bf16x8*)(tb + roff[ks] + kb * 32 * RB), qreg[ks], acc);
   };
 
-  // pass 1: row log-sum-exp (log2 units)
+  // pass 1: row log-sum-exp (log2 units), unless the forward's is given (the branch is
+  // uniform over the grid)
   float m = -INFINITY, l = 0.f;
-  run(false, [&](int kt, const char* tb) {
+  if (p.lse_in == nullptr) run(false, [&](int kt, const char* tb) {
     const int k0 = kt * kKB;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -282,7 +286,7 @@ __global__ __launch_bounds__(kTDQ) void bwd_dq_kernel(const BArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        s[r] = visible(key) ? s[r] * p.qscale : -INFINITY;
+        s[r] = visible(key) ? s[r] : -INFINITY;
         tm = fmaxf(tm, s[r]);
       }
       const float mn = fmaxf(m, tm);
@@ -295,12 +299,14 @@ __global__ __launch_bounds__(kTDQ) void bwd_dq_kernel(const BArgs p) {
       }
     }
   });
-  {
+  if (p.lse_in == nullptr) {
     const float mo = __shfl_xor(m, 32), lo = __shfl_xor(l, 32);
     const float ma = fmaxf(m, mo);
     const float la = (m == -INFINITY ? 0.f : l * fast_exp2(m - ma)) +
                      (mo == -INFINITY ? 0.f : lo * fast_exp2(mo - ma));
     m = ma == -INFINITY ? 0.f : ma + __log2f(la);
+  } else {
+    m = p.lse_in[((size_t)b * p.Hq + h) * T + qc] * 1.4426950408889634f;
   }
   const float lse2 = m;
 
@@ -324,7 +330,7 @@ __global__ __launch_bounds__(kTDQ) void bwd_dq_kernel(const BArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        const float pr = visible(key) ? fast_exp2(s[r] * p.qscale - lse2) : 0.f;
+        const float pr = visible(key) ? fast_exp2(s[r] - lse2) : 0.f;
         s[r] = pr * (dp[r] - drow_sum);
       }
 #pragma unroll
@@ -353,31 +359,45 @@ __global__ __launch_bounds__(kTDQ) void bwd_dq_kernel(const BArgs p) {
   }
 }
 
-// ---- dK, dV: one workgroup per (batch, KV head, 128 keys) -------------------------------
-// Eight waves: wave w owns keys 32 (w % 4) .. of the workgroup and half of the head dims
-// (w / 4) of their dK / dV. Every query tile streamed through LDS (Q~ rows, dA rows,
-// Q~^T and dA^T tiles, unpadded and swizzled, fetched by LDS DMA one tile ahead, and the
-// tile's log-sum-exp and D) thus serves 128 keys; the two waves of a key block both form
-// S and dP (over all head dims), which costs a third more MFMA work than splitting the
-// queries but halves the bytes streamed per key, the bound of this kernel.
-constexpr int kKV = 128;           // keys per dK/dV workgroup
-constexpr int kTKV = 512;          // its threads
+// ---- dK, dV: one workgroup per (batch, KV head, 256 keys) -------------------------------
+// Four waves, one per SIMD: wave w owns keys 64 w .. 64 w + 63 of the workgroup (two 32-key
+// blocks) and all head dims of their dK and dV, whose accumulators (4 D / 32 x 16 values
+// per lane and block) stay in AGPRs, the products that feed them being issued as inline
+// assembly. Every query tile streamed through LDS (Q~ rows, dA rows, Q~^T and dA^T tiles,
+// unpadded and swizzled, fetched by LDS DMA one step ahead, and the tile's log-sum-exp and
+// D) serves the 256 keys, and every operand read from it feeds the products of both key
+// blocks of a wave. Per query block of 32 rows: S and dP of both key blocks (keys on the
+// lanes), then P = exp2(S - L), dS = P (dP - D), then dV^T += dA^T P^T and
+// dK~^T += Q~^T dS^T with P and dS as B operands straight from the score registers.
+constexpr int kKV = 256;           // keys per dK/dV workgroup
+constexpr int kTKV = 256;          // its threads
+
+// Accumulate into an AGPR-pinned accumulator. The s_nop covers the wait states an operand
+// written by a vector instruction needs before an MFMA reads it.
+__device__ __forceinline__ void mfma_agpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// The same without wait states, for operands written at least one product earlier.
+__device__ __forceinline__ void mfma_agpr_late(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void pin_agpr(f32x16& v) { asm volatile("" : "+a"(v)); }
 
 template <int D, bool SWA>
-__global__ __launch_bounds__(kTKV) void bwd_dkdv_kernel(const BArgs p) {
+__global__ __launch_bounds__(kTKV, 1) void bwd_dkdv_kernel(const BArgs p) {
   constexpr int KS = D / 16;
-  constexpr int DBH = D / 64;              // 32-row d blocks per wave (half the dims)
+  constexpr int DB = D / 32;               // 32-row d blocks of dK^T / dV^T
   constexpr int RB = D * 2;
   constexpr int TILE = kQB * RB;
   constexpr int BUF = 4 * TILE + 2 * kQB * 4;
-  constexpr int DPW = TILE / 1024 / 8;     // DMA blocks per wave per tile
+  constexpr int DPW = TILE / 1024 / 4;     // 1 KiB DMA blocks per wave per tile
+  static_assert(DPW >= 1, "every wave takes part in each tile's DMA");
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
-  const int kb = wave & 3, dh = wave >> 2;
   const int T = p.T, G = p.group;
   const int n64 = (T + 63) / 64;
   const int nkt = (T + kKV - 1) / kKV;
@@ -385,26 +405,33 @@ __global__ __launch_bounds__(kTKV) void bwd_dkdv_kernel(const BArgs p) {
   const int hb = blockIdx.x / nkt;
   const int b = hb / p.Hkv, kvh = hb % p.Hkv;
   const int k0 = kt * kKV;
-  const int key = k0 + kb * 32 + l32;
-  const int kc = min(key, T - 1);
+  const int wk0 = k0 + 64 * wave;          // the wave's first key
 
-  bf16x8 kreg[KS], vreg[KS];
-  {
+  // the wave's K~ and V rows as B operands: lane l32 holds key wk0 + 32 kb + l32
+  bf16x8 kreg[2][KS], vreg[2][KS];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int kc = min(wk0 + 32 * kb + l32, T - 1);
     const bf16* krow = p.kt + (((size_t)b * p.Hkv + kvh) * T + kc) * D;
     const bf16* vrow = p.v + (((size_t)b * T + kc) * p.Hkv + kvh) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      kreg[ks] = *(const bf16x8*)(krow + ks * 16 + hi * 8);
-      vreg[ks] = *(const bf16x8*)(vrow + ks * 16 + hi * 8);
+      kreg[kb][ks] = *(const bf16x8*)(krow + ks * 16 + hi * 8);
+      vreg[kb][ks] = *(const bf16x8*)(vrow + ks * 16 + hi * 8);
     }
   }
-  f32x16 dvt[DBH], dkt[DBH];
+  f32x16 dvt[2][DB], dkt[2][DB];
 #pragma unroll
-  for (int db = 0; db < DBH; ++db)
+  for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      dvt[db][r] = 0.f;
-      dkt[db][r] = 0.f;
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        dvt[kb][db][r] = 0.f;
+        dkt[kb][db][r] = 0.f;
+      }
+      pin_agpr(dvt[kb][db]);
+      pin_agpr(dkt[kb][db]);
     }
 
   const int k_last = min(k0 + kKV, T) - 1;
@@ -452,8 +479,107 @@ __global__ __launch_bounds__(kTKV) void bwd_dkdv_kernel(const BArgs p) {
   auto put_stats = [&](int buf) {
     if (tid < kQB) {
       float* st = (float*)(smem + buf * BUF + 4 * TILE);
-      st[tid] = lsr;
-      st[kQB + tid] = dsr;
+      st[tid] = -lsr;
+      st[kQB + tid] = -dsr;
+    }
+  };
+
+  // One step over query tile i0 from buffer tb. MASKED: some (query, key) pair of the
+  // step is not visible (diagonal tiles, the window's edges, rows or keys past T).
+  auto step = [&](const char* tb, int i0, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const float* sL = (const float*)(tb + 4 * TILE);
+    const float* sD = sL + kQB;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      // dP and S of both key blocks with accumulators that start at -D and -L (the C
+      // operand of the first product, read straight from the step's statistics, which
+      // hold the negated values): Q~ is stored times scale * log2(e), so P = exp2(S acc)
+      // and dS = P * (dP acc). The lane's rows are qb * 32 + 8 (r / 4) + 4 hi + r % 4,
+      // which is the accumulator layout of four 4-row groups.
+      f32x16 dp[2], s[2];
+      {
+        f32x16 negd;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float4 v = *(const float4*)(sD + qb * 32 + 8 * g4 + 4 * hi);
+          negd[4 * g4] = v.x; negd[4 * g4 + 1] = v.y; negd[4 * g4 + 2] = v.z; negd[4 * g4 + 3] = v.w;
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 ad = *(const bf16x8*)(tb + TILE + roff[ks] + qb * 32 * RB);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            dp[kb] = mfma32(ad, vreg[kb][ks], ks == 0 ? negd : dp[kb]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        f32x16 negl;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float4 v = *(const float4*)(sL + qb * 32 + 8 * g4 + 4 * hi);
+          negl[4 * g4] = v.x; negl[4 * g4 + 1] = v.y; negl[4 * g4 + 2] = v.z; negl[4 * g4 + 3] = v.w;
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 aq = *(const bf16x8*)(tb + roff[ks] + qb * 32 * RB);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            s[kb] = mfma32(aq, kreg[kb][ks], ks == 0 ? negl : s[kb]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // P and dS, rounded to bf16 in pairs: the B operands of the dV and dK products
+      u32x4 pw[2][2], dw[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int key = wk0 + 32 * kb + l32;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          float pr[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            pr[e] = fast_exp2(s[kb][r + e]);
+            if (MASKED) {
+              const int qi = i0 + qb * 32 + 8 * ((r + e) >> 2) + 4 * hi + ((r + e) & 3);
+              const bool vis = key < T && qi < T && key <= qi && (!SWA || key > qi - p.window);
+              pr[e] = vis ? pr[e] : 0.f;
+            }
+          }
+          const bf16x2 pb = {(bf16)pr[0], (bf16)pr[1]};
+          const bf16x2 db2 = {(bf16)(pr[0] * dp[kb][r]), (bf16)(pr[1] * dp[kb][r + 1])};
+          pw[kb][r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, pb);
+          dw[kb][r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, db2);
+        }
+      }
+      bf16x8 pp[2][2], dd[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          pp[kb][j] = __builtin_bit_cast(bf16x8, pw[kb][j]);
+          dd[kb][j] = __builtin_bit_cast(bf16x8, dw[kb][j]);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int off = toff[2 * qb + j] + db * 32 * 128;
+          const bf16x8 av = *(const bf16x8*)(tb + 3 * TILE + off);
+          const bf16x8 ak = *(const bf16x8*)(tb + 2 * TILE + off);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            if (db == 0) {
+              mfma_agpr(dvt[kb][db], av, pp[kb][j]);
+              mfma_agpr(dkt[kb][db], ak, dd[kb][j]);
+            } else {
+              mfma_agpr_late(dvt[kb][db], av, pp[kb][j]);
+              mfma_agpr_late(dkt[kb][db], ak, dd[kb][j]);
+            }
+          }
+        }
     }
   };
 
@@ -462,64 +588,61 @@ __global__ __launch_bounds__(kTKV) void bwd_dkdv_kernel(const BArgs p) {
   vm_wait<0>();
   __syncthreads();
   int cur = 0;
-  for (int it = 0; it < n_it; ++it) {
+  auto advance = [&](int it, auto masked_tag) {
     const int nxt = cur ^ 1;
     fetch(min(it + 1, n_it - 1), nxt);
-    const char* tb = smem + cur * BUF;
-    const float* sL = (const float*)(tb + 4 * TILE);
-    const float* sD = sL + kQB;
-    const int i0 = (qt_lo + it % n_q) * kQB;
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      f32x16 s, dp;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = 0.f;
-        dp[r] = 0.f;
-      }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s = mfma32(*(const bf16x8*)(tb + roff[ks] + qb * 32 * RB), kreg[ks], s);
-        dp = mfma32(*(const bf16x8*)(tb + TILE + roff[ks] + qb * 32 * RB), vreg[ks], dp);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qr = qb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        const int qi = i0 + qr;
-        const bool vis = key < T && qi < T && key <= qi && (!SWA || key > qi - p.window);
-        const float pr = vis ? fast_exp2(s[r] * p.qscale - sL[qr]) : 0.f;
-        s[r] = pr;
-        dp[r] = pr * (dp[r] - sD[qr]);
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const bf16x8 pp = pack8(s, j), dd = pack8(dp, j);
-#pragma unroll
-        for (int db = 0; db < DBH; ++db) {
-          const int off = toff[2 * qb + j] + (dh * DBH + db) * 32 * 128;
-          dvt[db] = mfma32(*(const bf16x8*)(tb + 3 * TILE + off), pp, dvt[db]);
-          dkt[db] = mfma32(*(const bf16x8*)(tb + 2 * TILE + off), dd, dkt[db]);
-        }
-      }
-    }
+    step(smem + cur * BUF, (qt_lo + it % n_q) * kQB, masked_tag);
     put_stats(nxt);
     vm_wait<0>();
     __syncthreads();
     cur = nxt;
+  };
+  if (SWA) {
+    for (int it = 0; it < n_it; ++it) advance(it, std::integral_constant<bool, true>{});
+  } else {
+    // Per head of the group, the query tiles that see every key of the workgroup (all
+    // their queries after its last key, inside the sequence) form one run between the
+    // diagonal tiles before it and a ragged last tile after it: three loops, so that the
+    // masked and unmasked steps never meet at a join (where the compiler would copy the
+    // accumulators between registers).
+    const int full_lo = k0 + kKV <= T ? (k0 + kKV - 1 + kQB - 1) / kQB - qt_lo : n_q;
+    const int full_hi = k0 + kKV <= T ? min(n_q, T / kQB - qt_lo) : n_q;
+    for (int hg = 0; hg < G; ++hg) {
+      int qi = 0;
+      for (; qi < min(full_lo, n_q); ++qi)
+        advance(hg * n_q + qi, std::integral_constant<bool, true>{});
+      for (; qi < full_hi; ++qi) advance(hg * n_q + qi, std::integral_constant<bool, false>{});
+      for (; qi < n_q; ++qi) advance(hg * n_q + qi, std::integral_constant<bool, true>{});
+    }
   }
-  if (key < T) {
+  // 18 wait states at least between the last product and the reads of its accumulators
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      pin_agpr(dvt[kb][db]);
+      pin_agpr(dkt[kb][db]);
+    }
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int key = wk0 + 32 * kb + l32;
+    if (key >= T) continue;
     bf16* vdst = p.dv + (((size_t)b * T + key) * p.Hkv + kvh) * D;
     float* kdst = p.dkt + (((size_t)b * T + key) * p.Hkv + kvh) * D;
 #pragma unroll
-    for (int db = 0; db < DBH; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const int d0 = (dh * DBH + db) * 32 + 8 * r4 + 4 * hi;
+        const int d0 = db * 32 + 8 * r4 + 4 * hi;
         const int r = 4 * r4;
-        *(bf16x4*)(vdst + d0) = (bf16x4){(bf16)dvt[db][r], (bf16)dvt[db][r + 1],
-                                         (bf16)dvt[db][r + 2], (bf16)dvt[db][r + 3]};
-        *(float4*)(kdst + d0) = make_float4(dkt[db][r] * p.scale, dkt[db][r + 1] * p.scale,
-                                            dkt[db][r + 2] * p.scale, dkt[db][r + 3] * p.scale);
+        *(bf16x4*)(vdst + d0) = (bf16x4){(bf16)dvt[kb][db][r], (bf16)dvt[kb][db][r + 1],
+                                         (bf16)dvt[kb][db][r + 2], (bf16)dvt[kb][db][r + 3]};
+        // dk~ = scale * dS^T q~ and the Q~^T tiles hold q~ * scale * log2(e)
+        const float ks = p.scale / p.qscale;
+        *(float4*)(kdst + d0) =
+            make_float4(dkt[kb][db][r] * ks, dkt[kb][db][r + 1] * ks, dkt[kb][db][r + 2] * ks,
+                        dkt[kb][db][r + 3] * ks);
       }
   }
 }
@@ -700,6 +823,7 @@ hipError_t backward_t(const BackwardArgs& a, hipStream_t s) {
   n.x = a.q;
   n.w = a.wq;
   n.y = ws + L.qt;
+  n.out_scale = a.scale * 1.4426950408889634f;   // Q~ carries the log2-domain score scale
   n.H = a.Hq;
   n.ysb = (int64_t)a.Hq * a.T * D;
   n.yst = D;
@@ -709,6 +833,7 @@ hipError_t backward_t(const BackwardArgs& a, hipStream_t s) {
   n.x = a.k;
   n.w = a.wk;
   n.y = ws + L.kt;
+  n.out_scale = 1.0f;
   n.H = a.Hkv;
   n.ysb = (int64_t)a.Hkv * a.T * D;
   n.ysh = (int64_t)a.T * D;
@@ -726,6 +851,7 @@ hipError_t backward_t(const BackwardArgs& a, hipStream_t s) {
   p.da = a.g ? (bf16*)(ws + L.da) : (bf16*)a.dout;
   p.dsum = (float*)(ws + L.dsum);
   p.lse = (float*)(ws + L.lse);
+  p.lse_in = a.swa ? nullptr : a.lse;
   p.dqt = (float*)(ws + L.dqt);
   p.dkt = (float*)(ws + L.dkt);
   p.dv = (bf16*)a.dv;

@@ -38,6 +38,8 @@ struct PrefillArgs {
   const int32_t* cu = nullptr;
   int n_docs = 0;
   int max_len = 0;
+  // Optional row log-sum-exp, natural log, fp32 [B][Hq][T] (dense bf16 global layers).
+  float* lse = nullptr;
 };
 // Rows of slack after the last K~ row of the global-prefill workspace: a 64-key tile that
 // starts at the last row stays inside the workspace without clamping its row indices.
@@ -94,6 +96,7 @@ struct BackwardArgs {
   void* dg;            // SWA only
   float* dwq;
   float* dwk;
+  const float* lse;    // the forward's row log-sum-exp [B][Hq][T] (natural log) or nullptr
   void* ws;            // workspace of backward_workspace_bytes()
   int B, T, Hq, Hkv, d, window, rdim, pos_offset, swa;
   float eps, scale;

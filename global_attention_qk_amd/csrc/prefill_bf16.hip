@@ -118,6 +118,7 @@ struct KArgs {
   const int32_t* cu;
   int max_len, vt_slots;
   int n_blocks;       // query tiles in all: n_qtiles * n_hb
+  float* lse;         // row log-sum-exp [B][Hq][T] (natural log), dense global only; or nullptr
 };
 
 // Swap bits 2 and 3 of a key index within its 16-key group: keys {0-3, 8-11} then
@@ -1015,6 +1016,13 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p, const int lin, cons
     const float inv = 1.0f / lt;
     const int pos = min(qpos[qb], T - 1);   // rows past the end are staged, never stored
     const int hg = (wave * QB + qb) / bpp;
+    if (p.lse != nullptr && hi == 0 && qpos[qb] < T) {
+      // the probabilities were exp2(s - shift) with s in log2 units: the row's log-sum-exp
+      // is log2(l) + shift, returned in natural-log units
+      const float shift = STATIC ? -sinit : m_run[qb];
+      p.lse[((size_t)b * p.Hq + kvh * p.group + hg) * T + qpos[qb]] =
+          (__log2f(lt) + shift) * 0.6931471805599453f;
+    }
     const size_t rowoff = ((seq0 + pos) * p.Hq + kvh * p.group + hg) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -1192,6 +1200,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
   const int n_blocks = ka.n_qtiles * ka.n_hb;
   if (n_blocks == 0) return hipSuccess;
   ka.n_blocks = n_blocks;
+  ka.lse = (a.swa || a.cu) ? nullptr : a.lse;
   if (swa_stream_supported(a)) return launch_swa_stream(a, s);
   const bool kpre = (a.kt != nullptr);
   if (a.d == 128) {

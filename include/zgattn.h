@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define ZGATTN_ABI_VERSION 1
+#define ZGATTN_ABI_VERSION 2
 
 typedef enum {
   ZGATTN_OK = 0,
@@ -99,10 +99,14 @@ int zgattn_swa_prefill(const zgattn_desc* desc, const void* q, const void* k, co
  * aligned) receives normalised+rotated K once before the attention kernel reads it; with
  * workspace == NULL the K transform is instead fused into every K-tile load (slower for
  * long sequences, where each K tile is visited by many query tiles).
+ * `lse` (optional, device fp32 [B, Hq, T], 4-byte aligned; NULL to skip) receives each
+ * row's log-sum-exp of its scaled scores, ln sum_j exp(softmax_scale * q~_i . k~_j) over
+ * the visible keys, for zgattn_global_prefill_backward; bf16 only (ZGATTN_EUNSUPPORTED
+ * for fp32 when lse is not NULL).
  */
 int zgattn_global_prefill(const zgattn_desc* desc, const void* q, const void* k,
                           const void* v, const float* wq, const float* wk, void* workspace,
-                          size_t workspace_bytes, void* out, void* stream);
+                          size_t workspace_bytes, void* out, float* lse, void* stream);
 size_t zgattn_global_prefill_workspace_bytes(const zgattn_desc* desc);
 
 /*
@@ -138,9 +142,11 @@ size_t zgattn_global_prefill_varlen_workspace_bytes(const zgattn_desc* desc, int
  * v, g (SWA), w_q and w_k, where out is the layer of zgattn_swa_prefill /
  * zgattn_global_prefill on the same inputs (the pages train the model end to end, explainer
  * training sections, but print no backward formula: this is the gradient of the forward
- * stated above). out is the forward's output (its log-sum-exp is recomputed, so only out is
- * needed from the forward). dq, dg: [B, T, Hq, d]; dk, dv: [B, T, Hkv, d] (bf16, written,
- * not accumulated); dwq, dwk: fp32 [d] (written). workspace (device, >=
+ * stated above). out is the forward's output. The global form takes the forward's `lse`
+ * (as written by zgattn_global_prefill; device fp32 [B, Hq, T]) or NULL, in which case the
+ * log-sum-exp is recomputed by an extra pass over the keys; the SWA form always recomputes
+ * it (its rows see at most `window` keys). dq, dg: [B, T, Hq, d]; dk, dv: [B, T, Hkv, d]
+ * (bf16, written, not accumulated); dwq, dwk: fp32 [d] (written). workspace (device, >=
  * zgattn_prefill_backward_workspace_bytes(desc) bytes) holds the transformed q~/k~, the
  * row statistics and the fp32 gradients of q~ and k~. bf16 only; head groups 1, 2, 4, 8.
  */
@@ -152,9 +158,9 @@ int zgattn_swa_prefill_backward(const zgattn_desc* desc, const void* q, const vo
                                 size_t workspace_bytes, void* stream);
 int zgattn_global_prefill_backward(const zgattn_desc* desc, const void* q, const void* k,
                                    const void* v, const float* wq, const float* wk,
-                                   const void* out, const void* dout, void* dq, void* dk,
-                                   void* dv, float* dwq, float* dwk, void* workspace,
-                                   size_t workspace_bytes, void* stream);
+                                   const void* out, const float* lse, const void* dout,
+                                   void* dq, void* dk, void* dv, float* dwq, float* dwk,
+                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Gated SWA decode: one new token per sequence against a ring of `window` entries

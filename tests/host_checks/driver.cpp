@@ -69,7 +69,7 @@ static void prefill_checks() {
   CHECK(zgattn_swa_prefill(&x, P(1), P(2), P(3), P(4), W(), W(), P(5), nullptr) == ZGATTN_ERANGE);
   x = d;
   x.rms_eps = NAN;
-  CHECK(zgattn_global_prefill(&x, P(1), P(2), P(3), W(), W(), nullptr, 0, P(5), nullptr) == ZGATTN_EINVAL);
+  CHECK(zgattn_global_prefill(&x, P(1), P(2), P(3), W(), W(), nullptr, 0, P(5), nullptr, nullptr) == ZGATTN_EINVAL);
   CHECK(zgattn_swa_prefill(&d, P(1), P(2), P(3), nullptr, W(), W(), P(5), nullptr) == ZGATTN_ENULL);
   CHECK(zgattn_swa_prefill(&d, (char*)P(1) + 8, P(2), P(3), P(4), W(), W(), P(5), nullptr) == ZGATTN_EINVAL);
   CHECK(zgattn_swa_prefill(nullptr, P(1), P(2), P(3), P(4), W(), W(), P(5), nullptr) == ZGATTN_ENULL);
@@ -82,14 +82,21 @@ static void prefill_checks() {
   const size_t need = zgattn_global_prefill_workspace_bytes(&d);
   CHECK(need >= (size_t)2 * 2 * 300 * 128 * 2);
   stub::reset();
-  CHECK(zgattn_global_prefill(&d, P(1), P(2), P(3), W(), W(), P(6), need - 1, P(5), nullptr) == ZGATTN_EWORKSPACE);
+  CHECK(zgattn_global_prefill(&d, P(1), P(2), P(3), W(), W(), P(6), need - 1, P(5), nullptr, nullptr) == ZGATTN_EWORKSPACE);
   CHECK(stub::launches == 0);
-  CHECK(zgattn_global_prefill(&d, P(1), P(2), P(3), W(), W(), P(6), need, P(5), nullptr) == ZGATTN_OK);
+  CHECK(zgattn_global_prefill(&d, P(1), P(2), P(3), W(), W(), P(6), need, P(5), nullptr, nullptr) == ZGATTN_OK);
   CHECK(stub::aux_launches == 2 && stub::prefill_launches == 1);
   CHECK(stub::last_prefill.kt == P(6) && stub::last_prefill.vt != nullptr && stub::last_prefill.swa == 0);
+  CHECK(stub::last_prefill.lse == nullptr);
   stub::reset();
-  CHECK(zgattn_global_prefill(&d, P(1), P(2), P(3), W(), W(), nullptr, 0, P(5), nullptr) == ZGATTN_OK);
-  CHECK(stub::launches == 1 && stub::last_prefill.kt == nullptr);
+  CHECK(zgattn_global_prefill(&d, P(1), P(2), P(3), W(), W(), nullptr, 0, P(5), (float*)P(14), nullptr) == ZGATTN_OK);
+  CHECK(stub::launches == 1 && stub::last_prefill.kt == nullptr && stub::last_prefill.lse == (float*)P(14));
+  // the row log-sum-exp output: 4-byte aligned, bf16 only
+  stub::reset();
+  CHECK(zgattn_global_prefill(&d, P(1), P(2), P(3), W(), W(), nullptr, 0, P(5), (float*)((char*)P(14) + 2), nullptr) == ZGATTN_EINVAL);
+  zgattn_desc f32d = desc(1, 64, 4, 1, 64, ZGATTN_F32);
+  CHECK(zgattn_global_prefill(&f32d, P(1), P(2), P(3), W(), W(), nullptr, 0, P(5), (float*)P(14), nullptr) == ZGATTN_EUNSUPPORTED);
+  CHECK(stub::launches == 0);
   // fp32 takes its own path; group 16 is unsupported on the bf16 path
   zgattn_desc f = desc(1, 64, 4, 1, 64, ZGATTN_F32);
   CHECK(zgattn_swa_prefill(&f, P(1), P(2), P(3), P(4), W(), W(), P(5), nullptr) == ZGATTN_OK);
@@ -109,7 +116,11 @@ static void prefill_checks() {
   const size_t bneed = zgattn_prefill_backward_workspace_bytes(&d);
   float* dw = (float*)P(20);
   CHECK(zgattn_swa_prefill_backward(&d, P(1), P(2), P(3), P(4), W(), W(), P(5), P(8), P(9), P(10), P(11), P(12), dw, dw, P(13), bneed - 1, nullptr) == ZGATTN_EWORKSPACE);
-  CHECK(zgattn_global_prefill_backward(&d, P(1), P(2), P(3), W(), W(), P(5), P(8), P(9), P(10), P(11), dw, dw, P(13), bneed, nullptr) == ZGATTN_OK);
+  CHECK(zgattn_global_prefill_backward(&d, P(1), P(2), P(3), W(), W(), P(5), nullptr, P(8), P(9), P(10), P(11), dw, dw, P(13), bneed, nullptr) == ZGATTN_OK);
+  CHECK(stub::last_backward.lse == nullptr && stub::last_backward.swa == 0);
+  CHECK(zgattn_global_prefill_backward(&d, P(1), P(2), P(3), W(), W(), P(5), (const float*)P(14), P(8), P(9), P(10), P(11), dw, dw, P(13), bneed, nullptr) == ZGATTN_OK);
+  CHECK(stub::last_backward.lse == (const float*)P(14));
+  CHECK(zgattn_global_prefill_backward(&d, P(1), P(2), P(3), W(), W(), P(5), (const float*)((char*)P(14) + 1), P(8), P(9), P(10), P(11), dw, dw, P(13), bneed, nullptr) == ZGATTN_EINVAL);
   CHECK(zgattn_swa_prefill_backward(&d, P(1), P(2), P(3), nullptr, W(), W(), P(5), P(8), P(9), P(10), P(11), P(12), dw, dw, P(13), bneed, nullptr) == ZGATTN_ENULL);
 }
 

@@ -9,6 +9,7 @@ int launches, prefill_launches, aux_launches, decode_launches, batched_layers,
     scratch_lookups;
 int smem_attr_calls;
 zg::PrefillArgs last_prefill;
+zg::BackwardArgs last_backward;
 zg::DecodeArgs last_decode;
 alignas(256) static unsigned char scratch_buf[256];
 void* const scratch = scratch_buf;
@@ -65,8 +66,9 @@ hipError_t launch_qknorm_rope(const NormRopeArgs&, hipStream_t) {
 size_t backward_workspace_bytes(int B, int T, int Hq, int Hkv, int d) {
   return (size_t)B * T * (Hq + Hkv) * d * 16 + 4096;
 }
-hipError_t launch_prefill_backward(const BackwardArgs&, hipStream_t) {
+hipError_t launch_prefill_backward(const BackwardArgs& a, hipStream_t) {
   ++stub::launches;
+  stub::last_backward = a;
   return hipSuccess;
 }
 static hipError_t rec_decode(const DecodeArgs& a) {

@@ -12,6 +12,7 @@ extern int scratch_lookups;       // decode_noalloc_scratch calls
 extern int smem_attr_calls;       // hipFuncSetAttribute calls
 extern zg::PrefillArgs last_prefill;
 extern zg::DecodeArgs last_decode;
+extern zg::BackwardArgs last_backward;
 extern void* const scratch;       // what decode_noalloc_scratch reports
 void reset();
 }  // namespace stub

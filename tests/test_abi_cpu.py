@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_strerror():
     lib = L.lib()
-    assert lib.zgattn_abi_version() == 1
+    assert lib.zgattn_abi_version() == 2
     for code in L.STATUS:
         assert lib.zgattn_strerror(code)
     assert lib.zgattn_strerror(12345) == b"unknown status"
@@ -84,7 +84,7 @@ def test_global_prefill_workspace():
     vtiles = 2 * 8 * ((1000 + 63) // 64) * 64 * 128 * 2  # V as transposed 64-key tiles
     assert need == ((kbytes + 255) // 256) * 256 + vtiles
     st = lib.zgattn_global_prefill(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                                   need - 1, FAKE, None)
+                                   need - 1, FAKE, None, None)
     assert st == -5
 
 
@@ -212,5 +212,6 @@ def test_backward_checks():
     assert call(d=_d(batch=2, seq_len=300, n_q_heads=48, n_kv_heads=3)) == -4
     assert call(d=_d(batch=2, seq_len=0, n_q_heads=8, n_kv_heads=2)) == 0
     st = lib.zgattn_global_prefill_backward(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                                            FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, need, None)
+                                            None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, need,
+                                            None)
     assert st == -5

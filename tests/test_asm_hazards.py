@@ -1,6 +1,7 @@
-"""Static check of the global prefill kernels' assembly (host only, no GPU).
+"""Static check of the assembly of the kernels with AGPR-pinned accumulators (host only).
 
-The P.V products of `prefill_bf16.hip` are MFMAs written as inline assembly, so the
+The P.V products of `prefill_bf16.hip` and the dV / dK products of `backward.hip` are
+MFMAs written as inline assembly, so the
 compiler does not know that they keep writing their AGPR accumulators for several cycles
 after issue, and it inserts no wait states before a later instruction reads those AGPRs
 (a register copy where control flow joins, the epilogue's reads). An early read returns
@@ -31,11 +32,11 @@ def _agprs(tok):
     return {int(m.group(1))} if m else set()
 
 
-def _kernels(asm):
+def _kernels(asm, name):
     lines = asm.split("\n")
     out = {}
     for i, l in enumerate(lines):
-        m = re.match(r"^(_Z\S*prefill_bf16_kernel\S*):", l)
+        m = re.match(r"^(_Z\S*" + name + r"\S*):", l)
         if m:
             body = []
             for l2 in lines[i + 1:]:
@@ -101,15 +102,17 @@ def _early_reads(body):
 
 @pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
                     reason="hipcc not available")
-def test_no_early_accumulator_reads(tmp_path):
-    src = os.path.join(build_lib.CSRC, "prefill_bf16.hip")
-    out = tmp_path / "prefill_bf16.s"
+@pytest.mark.parametrize("src_name,kernel", [("prefill_bf16.hip", "prefill_bf16_kernel"),
+                                             ("backward.hip", "bwd_dkdv_kernel")])
+def test_no_early_accumulator_reads(tmp_path, src_name, kernel):
+    src = os.path.join(build_lib.CSRC, src_name)
+    out = tmp_path / (src_name + ".s")
     cmd = [build_lib.hipcc()] + build_lib.common_flags() + [
         "-x", "hip", "--cuda-device-only", "-S", src, "-o", str(out)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
-    kernels = _kernels(out.read_text())
-    assert kernels, "no prefill kernels found in the assembly"
+    kernels = _kernels(out.read_text(), kernel)
+    assert kernels, f"no {kernel} kernels found in the assembly"
     n_mfma = sum(1 for b in kernels.values() for s in b if s.startswith("v_mfma") and " a[" in s)
     assert n_mfma > 0, "no assembly MFMAs with AGPR accumulators found"
     problems = {k: _early_reads(b) for k, b in kernels.items()}

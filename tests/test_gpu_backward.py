@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 REL = 2e-2
 
 
-def _check(B, T, Hq, Hkv, d, window, seed, pos_offset=0):
+def _check(B, T, Hq, Hkv, d, window, seed, pos_offset=0, fwd_lse=False):
     need_gpu()
     import torch
     import global_attention_qk_amd as zg
@@ -34,15 +34,27 @@ def _check(B, T, Hq, Hkv, d, window, seed, pos_offset=0):
     if window:
         out = zg.swa_prefill(cq, ck, cv, cg, cwq, cwk, window=window, rotary_dim=r,
                              pos_offset=pos_offset)
+        lse = None
     else:
-        out = zg.global_prefill(cq, ck, cv, cwq, cwk, rotary_dim=r, pos_offset=pos_offset)
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device="cuda") if fwd_lse else None
+        out = zg.global_prefill(cq, ck, cv, cwq, cwk, rotary_dim=r, pos_offset=pos_offset,
+                                lse=lse)
     dq, dk, dv, dg, dwq, dwk = zg.prefill_backward(cq, ck, cv, cg, cwq, cwk, out, cdo,
                                                    window=window, rotary_dim=r,
-                                                   pos_offset=pos_offset)
+                                                   pos_offset=pos_offset, lse=lse)
     torch.cuda.synchronize()
     ref = OG.prefill_grads(host64(q), host64(k), host64(v), None if g is None else host64(g),
                            host64(wq), host64(wk), host64(do), window=window, rotary_dim=r,
                            pos_offset=pos_offset)
+    if lse is not None:
+        # Scores come from bf16 operands (relative error <= 2^-8 each way) and the row sum
+        # from bf16-rounded probabilities (2^-8 relative, 4e-3 in the log): the error is a
+        # small multiple of 2^-8 of the largest |lse|.
+        want = ref["lse"]
+        err = float(np.max(np.abs(host64(lse) - want)))
+        lim = 1e-2 * max(1.0, float(np.max(np.abs(want))))
+        say("forward lse", (B, T, Hq, Hkv, d), f"err={err:.3e} lim={lim:.3e}")
+        assert err <= lim, ("lse", err, lim)
     got = dict(dq=dq, dk=dk, dv=dv, dwq=dwq, dwk=dwk)
     if window:
         got["dg"] = dg
@@ -80,3 +92,13 @@ def test_backward_tiny_and_single_token():
 def test_backward_1024_positions(window):
     # longer rows: 16 key tiles per query row at the end of the sequence
     _check(1, 1024, 8, 2, 128, window, 1600)
+
+
+@pytest.mark.parametrize("T", [300, 1024])
+def test_backward_global_with_forward_lse(T):
+    # the forward's row log-sum-exp handed to the backward (no recomputation pass)
+    _check(2 if T == 300 else 1, T, 8, 2, 128, None, 1700 + T, fwd_lse=True)
+
+
+def test_backward_forward_lse_head_dim_64_offset():
+    _check(1, 150, 4, 1, 64, None, 1800, pos_offset=1000, fwd_lse=True)
