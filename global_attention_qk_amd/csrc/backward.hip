@@ -200,6 +200,8 @@ __global__ __launch_bounds__(kTDQ) void bwd_dq_kernel(const BArgs p) {
     }
   }
   const float drow_sum = p.dsum[((size_t)b * p.Hq + h) * T + qc];
+  const float lse_given = p.lse_in ? p.lse_in[((size_t)b * p.Hq + h) * T + qc] : 0.f;
+  vm_wait_all_known();
 
   const int q_last = min(i0 + bmp, T) - 1;
   const int k_lo = SWA ? max(0, i0 - p.window + 1) : 0;
@@ -246,47 +248,56 @@ __global__ __launch_bounds__(kTDQ) void bwd_dq_kernel(const BArgs p) {
   auto visible = [&](int key) {
     return qvalid && key <= qpos && (!SWA || key > qpos - p.window);
   };
+  // Key tiles below every row of the workgroup (all their keys before its first query,
+  // global layers) need no mask; they come first, then the masked ones (the diagonal, and
+  // every tile of a windowed layer). Two loops, so that the two kinds of step do not meet
+  // at a join.
+  const int n_full = SWA ? 0 : max(0, min(n_tiles, (i0 + 1) / kKB - kt_lo));
   auto run = [&](bool second, auto&& body) {
-    const int nd = second ? 3 * KPW : KPW;   // DMA instructions per wave per tile
 #pragma unroll
     for (int a = 0; a < kDQAhead; ++a) dma(kt_lo + min(a, n_tiles - 1), a, second);
     if (second) vm_wait<(kDQAhead - 1) * 3 * KPW>(); else vm_wait<(kDQAhead - 1) * KPW>();
     __syncthreads();
     int cur = 0;
-    for (int i = 0; i < n_tiles; ++i) {
+    auto one = [&](int i, auto masked_tag) {
       const int ahead = (cur + kDQAhead) % NB;
       dma(kt_lo + min(i + kDQAhead, n_tiles - 1), ahead, second);
-      body(kt_lo + i, smem + cur * BUF);
+      body(kt_lo + i, smem + cur * BUF, masked_tag);
       if (second) vm_wait<(kDQAhead - 1) * 3 * KPW>(); else vm_wait<(kDQAhead - 1) * KPW>();
       __syncthreads();
       cur = cur == NB - 1 ? 0 : cur + 1;
-    }
+    };
+    int i = 0;
+    for (; i < n_full; ++i) one(i, std::integral_constant<bool, false>{});
+    for (; i < n_tiles; ++i) one(i, std::integral_constant<bool, true>{});
     vm_wait<0>();
     __syncthreads();
-    (void)nd;
   };
-  auto scores = [&](const char* tb, int kb, f32x16& acc) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  // S^T of one 32-key block, the accumulator starting at `init`
+  auto scores = [&](const char* tb, int kb, const f32x16& init, f32x16& acc) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      acc = mfma32(*(const bf16x8*)(tb + roff[ks] + kb * 32 * RB), qreg[ks], acc);
+      acc = mfma32(*(const bf16x8*)(tb + roff[ks] + kb * 32 * RB), qreg[ks], ks == 0 ? init : acc);
   };
+  f32x16 zero16;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) zero16[r] = 0.f;
 
   // pass 1: row log-sum-exp (log2 units), unless the forward's is given (the branch is
   // uniform over the grid)
   float m = -INFINITY, l = 0.f;
-  if (p.lse_in == nullptr) run(false, [&](int kt, const char* tb) {
+  if (p.lse_in == nullptr) run(false, [&](int kt, const char* tb, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     const int k0 = kt * kKB;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x16 s;
-      scores(tb, kb, s);
+      scores(tb, kb, zero16, s);
       float tm = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        s[r] = visible(key) ? s[r] : -INFINITY;
+        if (MASKED) s[r] = visible(key) ? s[r] : -INFINITY;
         tm = fmaxf(tm, s[r]);
       }
       const float mn = fmaxf(m, tm);
@@ -306,32 +317,42 @@ __global__ __launch_bounds__(kTDQ) void bwd_dq_kernel(const BArgs p) {
                      (mo == -INFINITY ? 0.f : lo * fast_exp2(mo - ma));
     m = ma == -INFINITY ? 0.f : ma + __log2f(la);
   } else {
-    m = p.lse_in[((size_t)b * p.Hq + h) * T + qc] * 1.4426950408889634f;
+    m = lse_given * 1.4426950408889634f;
   }
   const float lse2 = m;
 
-  // pass 2: P, dP, dS and dQ~^T += K~^T dS^T
+  // pass 2: P, dP, dS and dQ~^T += K~^T dS^T. The S and dP accumulators start at -L and
+  // -D (the lane's row), so that P = exp2(S acc) and dS = P * (dP acc).
+  f32x16 negl, negd;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    negl[r] = -lse2;
+    negd[r] = -drow_sum;
+  }
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
-  run(true, [&](int kt, const char* tb) {
+  run(true, [&](int kt, const char* tb, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     const int k0 = kt * kKB;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x16 s, dp;
-      scores(tb, kb, s);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) dp[r] = 0.f;
+      scores(tb, kb, negl, s);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        dp = mfma32(*(const bf16x8*)(tb + TILE + roff[ks] + kb * 32 * RB), dreg[ks], dp);
+        dp = mfma32(*(const bf16x8*)(tb + TILE + roff[ks] + kb * 32 * RB), dreg[ks],
+                    ks == 0 ? negd : dp);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        const float pr = visible(key) ? fast_exp2(s[r] - lse2) : 0.f;
-        s[r] = pr * (dp[r] - drow_sum);
+        float pr = fast_exp2(s[r]);
+        if (MASKED) {
+          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          pr = visible(key) ? pr : 0.f;
+        }
+        s[r] = pr * dp[r];
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -371,6 +392,13 @@ __global__ __launch_bounds__(kTDQ) void bwd_dq_kernel(const BArgs p) {
 // dK~^T += Q~^T dS^T with P and dS as B operands straight from the score registers.
 constexpr int kKV = 256;           // keys per dK/dV workgroup
 constexpr int kTKV = 256;          // its threads
+// Order of a dK/dV workgroup's (head, query tile) steps: 1 = query tiles from the last one
+// down, the group's heads inside (every workgroup of a KV head starts on the same tile and
+// they advance together, so an XCD's L2 serves a tile to all of them); 0 = per head, query
+// tiles upwards from the diagonal.
+#ifndef ZG_BWD_DESC
+#define ZG_BWD_DESC 1
+#endif
 
 // Accumulate into an AGPR-pinned accumulator. The s_nop covers the wait states an operand
 // written by a vector instruction needs before an MFMA reads it.
@@ -420,6 +448,7 @@ __global__ __launch_bounds__(kTKV, 1) void bwd_dkdv_kernel(const BArgs p) {
       vreg[kb][ks] = *(const bf16x8*)(vrow + ks * 16 + hi * 8);
     }
   }
+  vm_wait_all_known();
   f32x16 dvt[2][DB], dkt[2][DB];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -449,8 +478,18 @@ __global__ __launch_bounds__(kTKV, 1) void bwd_dkdv_kernel(const BArgs p) {
   // step `it` into buffer `buf`: DMA of the four tiles; the row statistics go through
   // registers (lsr, dsr), written into the buffer by put_stats at the end of the step
   float lsr = 0.f, dsr = 0.f;
+  auto coords = [&](int it, int& hg, int& qt) {
+    if (ZG_BWD_DESC) {
+      hg = it % G;
+      qt = qt_hi - it / G;
+    } else {
+      hg = it / n_q;
+      qt = qt_lo + it % n_q;
+    }
+  };
   auto fetch = [&](int it, int buf) {
-    const int hg = it / n_q, qt = qt_lo + it % n_q;
+    int hg, qt;
+    coords(it, hg, qt);
     const int h = kvh * G + hg, i0 = qt * kQB;
     const uint32_t dst = lds0 + buf * BUF;
     const bf16* qbase = p.qt + (((size_t)b * p.Hq + h) * T + i0) * D;
@@ -591,7 +630,9 @@ __global__ __launch_bounds__(kTKV, 1) void bwd_dkdv_kernel(const BArgs p) {
   auto advance = [&](int it, auto masked_tag) {
     const int nxt = cur ^ 1;
     fetch(min(it + 1, n_it - 1), nxt);
-    step(smem + cur * BUF, (qt_lo + it % n_q) * kQB, masked_tag);
+    int hg, qt;
+    coords(it, hg, qt);
+    step(smem + cur * BUF, qt * kQB, masked_tag);
     put_stats(nxt);
     vm_wait<0>();
     __syncthreads();
@@ -600,19 +641,35 @@ __global__ __launch_bounds__(kTKV, 1) void bwd_dkdv_kernel(const BArgs p) {
   if (SWA) {
     for (int it = 0; it < n_it; ++it) advance(it, std::integral_constant<bool, true>{});
   } else {
-    // Per head of the group, the query tiles that see every key of the workgroup (all
-    // their queries after its last key, inside the sequence) form one run between the
-    // diagonal tiles before it and a ragged last tile after it: three loops, so that the
-    // masked and unmasked steps never meet at a join (where the compiler would copy the
-    // accumulators between registers).
-    const int full_lo = k0 + kKV <= T ? (k0 + kKV - 1 + kQB - 1) / kQB - qt_lo : n_q;
-    const int full_hi = k0 + kKV <= T ? min(n_q, T / kQB - qt_lo) : n_q;
-    for (int hg = 0; hg < G; ++hg) {
-      int qi = 0;
-      for (; qi < min(full_lo, n_q); ++qi)
-        advance(hg * n_q + qi, std::integral_constant<bool, true>{});
-      for (; qi < full_hi; ++qi) advance(hg * n_q + qi, std::integral_constant<bool, false>{});
-      for (; qi < n_q; ++qi) advance(hg * n_q + qi, std::integral_constant<bool, true>{});
+    // The query tiles that see every key of the workgroup (all their queries after its
+    // last key, inside the sequence) are one run [f_lo, f_hi] between the diagonal tiles
+    // below it and a ragged last tile above it. The steps over them and over the masked
+    // tiles go in separate loops, so that masked and unmasked steps never meet at a join
+    // (where the compiler would copy the accumulators between registers).
+    const bool any = k0 + kKV <= T;
+    const int f_lo = any ? (k0 + kKV - 1 + kQB - 1) / kQB : qt_hi + 1;
+    const int f_hi = any ? min(qt_hi, T / kQB - 1) : qt_hi;   // empty when f_lo > f_hi
+    auto run = [&](int it0, int it1, auto masked_tag) {
+      for (int it = it0; it < it1; ++it) advance(it, masked_tag);
+    };
+    const std::integral_constant<bool, true> masked{};
+    const std::integral_constant<bool, false> unmasked{};
+    const bool none = f_lo > f_hi;   // then the first masked run takes every step
+    if (ZG_BWD_DESC) {
+      // tiles qt_hi .. f_hi + 1 (ragged top), f_hi .. f_lo, f_lo - 1 .. qt_lo (diagonal)
+      const int a = none ? n_it : (qt_hi - f_hi) * G;
+      const int c = none ? n_it : (qt_hi - f_lo + 1) * G;
+      run(0, a, masked);
+      run(a, c, unmasked);
+      run(c, n_it, masked);
+    } else {
+      const int a = none ? n_q : f_lo - qt_lo;
+      const int c = none ? n_q : f_hi - qt_lo + 1;
+      for (int hg = 0; hg < G; ++hg) {
+        run(hg * n_q, hg * n_q + a, masked);
+        run(hg * n_q + a, hg * n_q + c, unmasked);
+        run(hg * n_q + c, (hg + 1) * n_q, masked);
+      }
     }
   }
   // 18 wait states at least between the last product and the reads of its accumulators

@@ -99,6 +99,16 @@ __device__ __forceinline__ void vm_wait() {
   asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
 
+// Wait for every vector-memory load, as an instruction the compiler sees. After register
+// operands are loaded ahead of a loop that issues LDS DMA (invisible to the compiler's
+// wait counting), this tells the compiler that those loads are complete; otherwise it
+// places vmcnt waits for them inside the loop, which the hardware then applies to the
+// DMA in flight (waiting for the prefetch of the next tile).
+__device__ __forceinline__ void vm_wait_all_known() {
+  // gfx9 encoding: vmcnt 0 (bits 3:0 and 15:14), expcnt 7 (6:4), lgkmcnt 15 (11:8)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
 // Sum over each aligned group of N (2, 4, 8 or 16) lanes, the result in every lane of the
 // group: cross-lane moves within a row of 16 lanes (DPP), no LDS traffic. The pairings
 // (swap neighbours, swap pairs, mirror within 8, mirror within 16) each join two disjoint
