@@ -438,3 +438,28 @@ def pin_grad_finite_differences():
                 fd = (loss(**{name: xp}) - loss(**{name: xm})) / (2 * h)
                 an = gr["d" + name][idx]
                 assert abs(fd - an) <= 1e-6 * max(1.0, abs(fd)), (W, name, idx, fd, an)
+
+
+def pin_grad_rows_match_autograd():
+    """The closed-form gradients at sampled positions (prefill_grads_rows, used where the
+    autograd graph does not fit) equal autograd's at those positions: a gated window layer
+    and a global layer, GQA, row blocks smaller than the sequence, non-default scale and
+    RoPE base."""
+    from oracle import grad as OG
+    B, T, Hq, Hkv, d, r = 2, 23, 4, 2, 8, 4
+    q, k, v = _rand((B, T, Hq, d), 121), _rand((B, T, Hkv, d), 122), _rand((B, T, Hkv, d), 123)
+    g, dout = _rand((B, T, Hq, d), 124), _rand((B, T, Hq, d), 125)
+    wq, wk = 1 + 0.1 * _rand((d,), 126), 1 + 0.1 * _rand((d,), 127)
+    rows, keys = [0, 1, 5, 13, 22], [0, 3, 7, 21, 22]
+    for W, gg, sc, base in ((None, None, None, 10000.0), (5, g, 0.3, 1e7)):
+        kw = dict(window=W, rotary_dim=r, pos_offset=3, scale=sc, rope_base=base)
+        full = OG.prefill_grads(q, k, v, gg, wq, wk, dout, **kw)
+        part = OG.prefill_grads_rows(q, k, v, gg, wq, wk, dout, rows, keys, block=7, **kw)
+        for name, at in (("dq", rows), ("dg", rows), ("dk", keys), ("dv", keys)):
+            if full[name] is None:
+                assert part[name] is None
+                continue
+            err = np.max(np.abs(np.take(full[name], at, axis=1) - part[name]))
+            assert err < 1e-10, (W, name, err)
+        assert np.max(np.abs(full["lse"] - part["lse"])) < 1e-10
+

@@ -102,3 +102,61 @@ def test_backward_global_with_forward_lse(T):
 
 def test_backward_forward_lse_head_dim_64_offset():
     _check(1, 150, 4, 1, 64, None, 1800, pos_offset=1000, fwd_lse=True)
+
+
+def _spread_rows(T, n, seed):
+    """Sorted positions: the first rows, tile and window edges, the middle, the last rows,
+    and uniform draws up to n."""
+    fixed = {0, 1, 2, 63, 64, 127, 128, 129, 255, 256, T // 2 - 1, T // 2, T - 65, T - 64,
+             T - 2, T - 1}
+    fixed = {x for x in fixed if 0 <= x < T}
+    rng = np.random.default_rng(seed)
+    pool = np.setdiff1d(np.arange(T), np.array(sorted(fixed)))
+    extra = rng.choice(pool, size=max(0, n - len(fixed)), replace=False)
+    return np.sort(np.concatenate([np.array(sorted(fixed)), extra])).astype(np.int64)
+
+
+@pytest.mark.parametrize("window", [None, 128])
+def test_backward_sampled_rows_T8192(window):
+    # 8192 positions with the model's head shape (d 128, rotary 42, 4 query heads per KV
+    # head): the gradients at 48 spread query rows (dq, dg) and 48 spread keys (dk, dv, every
+    # query row's contribution) against the oracle's closed-form backward, whose forward
+    # runs over every row in fp64. The global layer takes the forward's log-sum-exp.
+    need_gpu()
+    import torch
+    import global_attention_qk_amd as zg
+    B, T, Hq, Hkv, d, seed = 1, 8192, 8, 2, 128, 1900
+    q = host_tensor((B, T, Hq, d), seed, "bf16")
+    k = host_tensor((B, T, Hkv, d), seed + 1, "bf16")
+    v = host_tensor((B, T, Hkv, d), seed + 2, "bf16")
+    g = host_tensor((B, T, Hq, d), seed + 3, "bf16", 2 ** 0.5) if window else None
+    do = host_tensor((B, T, Hq, d), seed + 4, "bf16")
+    wq = torch.from_numpy(norm_weight(d, seed + 5))
+    wk = torch.from_numpy(norm_weight(d, seed + 6))
+    r = zg.rotary_dim_for(d)
+    cq, ck, cv, cdo, cwq, cwk = (t.cuda() for t in (q, k, v, do, wq, wk))
+    cg = g.cuda() if g is not None else None
+    lse = None
+    if window:
+        out = zg.swa_prefill(cq, ck, cv, cg, cwq, cwk, window=window, rotary_dim=r)
+    else:
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device="cuda")
+        out = zg.global_prefill(cq, ck, cv, cwq, cwk, rotary_dim=r, lse=lse)
+    dq, dk, dv, dg, _, _ = zg.prefill_backward(cq, ck, cv, cg, cwq, cwk, out, cdo,
+                                               window=window, rotary_dim=r, lse=lse)
+    torch.cuda.synchronize()
+    rows, keys = _spread_rows(T, 48, seed + 7), _spread_rows(T, 48, seed + 8)
+    say("backward sampled", (T, window), "oracle over every row (fp64)")
+    ref = OG.prefill_grads_rows(host64(q), host64(k), host64(v),
+                                None if g is None else host64(g), host64(wq), host64(wk),
+                                host64(do), rows, keys, window=window, rotary_dim=r)
+    got = dict(dq=(dq, rows), dk=(dk, keys), dv=(dv, keys))
+    if window:
+        got["dg"] = (dg, rows)
+    for name, (t, at) in got.items():
+        want = ref[name]
+        err = float(np.max(np.abs(host64(t)[:, at] - want)))
+        lim = REL * max(1.0, float(np.max(np.abs(want))))
+        say("backward sampled", (T, window), name, f"err={err:.3e} lim={lim:.3e}")
+        assert err <= lim, (name, err, lim)
+

@@ -130,6 +130,14 @@ def _grads_dk_not_summed_over_group(*a, **kw):
     return r
 
 
+def _softmax_vjp_without_d(p, dp, dsum):
+    return p * dp                               # the row term D of the softmax Jacobian dropped
+
+
+def _group_heads_first_only(kvh, grp):
+    return range(kvh * grp, kvh * grp + 1)      # one query head of the group instead of all
+
+
 _ORIG = {n: getattr(O, n) for n in ("partial_rope", "rmsnorm", "visible_mask", "sigmoid",
                                      "kv_bytes_per_token", "layer_kinds", "prefill_varlen",
                                      "_block_keys")}
@@ -150,6 +158,8 @@ MUTANTS = {
     "grad_dk_one_head": (OG, "prefill_grads", _grads_dk_not_summed_over_group),
     "varlen_crosses_documents": ("prefill_varlen", _varlen_sees_previous_document),
     "row_block_lo_off_by_one": ("_block_keys", _block_keys_lo_off_by_one),
+    "grad_rows_softmax_no_d": (OG, "_softmax_vjp", _softmax_vjp_without_d),
+    "grad_rows_one_head": (OG, "_group_heads", _group_heads_first_only),
 }
 
 PINS = [getattr(P, n) for n in dir(P) if n.startswith("pin_")]
