@@ -25,9 +25,9 @@
 //     every p lies in [2^-2B, 1], so neither the row sum nor the fp32 P.V accumulator can
 //     overflow (at most T * max|v|), and with B <= 48 the largest p of a row is at least
 //     2^-96, far above the fp32 normal range's end. The running max, its reduction and
-//     the accumulator rescale disappear. A second kernel variant keeps an online max for
-//     larger bounds; both variants are launched and each returns at once unless the bound
-//     selects it.
+//     the accumulator rescale disappear. An online-max form of the tile handles larger
+//     bounds; one launch carries both, and the bound (the same for every workgroup) picks
+//     one.
 //   * The O accumulators stay in AGPRs for the whole kernel (the P.V product is issued
 //     through a constrained MFMA), leaving the VGPRs to the scores and operands.
 //   * K~: for global layers a separate pass writes normalised+rotated K once into a
@@ -1078,38 +1078,26 @@ __device__ __forceinline__ float score_bound(const KArgs& p) {
   return fabsf(p.qscale) * (float)D * wqm * wkm * 1.02f;
 }
 
-// Both variants are launched and each returns at once unless the bound selects it. The
-// static-shift variant takes one query tile per workgroup. The online variant, selected
-// only for large norm weights, runs one workgroup per CU looping over the tiles, so that
-// when it is not selected it costs a single short round of workgroups.
-template <int D, bool SWA, bool KPRE, bool STATIC, int NW>
+// One launch, one query tile per workgroup: the bound is the same for every workgroup, so
+// they all take the same variant (static shift when the bound allows it, else the online
+// max).
+template <int D, bool SWA, bool KPRE, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p) {
   const float bound = score_bound<D>(p);
-  if ((bound <= kStaticShiftMax) != STATIC) return;
-  if (STATIC) {
-    prefill_tile<D, SWA, KPRE, STATIC, NW>(p, blockIdx.x, -bound);
-  } else {
-    for (int lin = blockIdx.x; lin < p.n_blocks; lin += gridDim.x)
-      prefill_tile<D, SWA, KPRE, STATIC, NW>(p, lin, 0.f);
-  }
+  if (bound <= kStaticShiftMax)
+    prefill_tile<D, SWA, KPRE, true, NW>(p, blockIdx.x, -bound);
+  else
+    prefill_tile<D, SWA, KPRE, false, NW>(p, blockIdx.x, 0.f);
 }
 
 template <int D, bool SWA, bool KPRE, int NW = kWavesPerBlock>
 hipError_t launch_t(const KArgs& ka, int n_blocks, hipStream_t s) {
   constexpr int smem = Smem<D>::kTotal;
   constexpr int kThreads = NW * 64;
-  auto k_static = prefill_bf16_kernel<D, SWA, KPRE, true, NW>;
-  auto k_online = prefill_bf16_kernel<D, SWA, KPRE, false, NW>;
-  hipError_t e = ensure_dynamic_smem((const void*)k_static, smem);
+  auto kern = prefill_bf16_kernel<D, SWA, KPRE, NW>;
+  hipError_t e = ensure_dynamic_smem((const void*)kern, smem);
   if (e != hipSuccess) return e;
-  e = ensure_dynamic_smem((const void*)k_online, smem);
-  if (e != hipSuccess) return e;
-  int cus = 0;
-  e = device_cu_count(&cus);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_static, dim3(n_blocks), dim3(kThreads), smem, s, ka);
-  hipLaunchKernelGGL(k_online, dim3(std::min(n_blocks, std::max(cus, 1))), dim3(kThreads), smem,
-                     s, ka);
+  hipLaunchKernelGGL(kern, dim3(n_blocks), dim3(kThreads), smem, s, ka);
   return hipGetLastError();
 }
 

@@ -32,8 +32,8 @@
 //     (exchanged with one swizzle).
 //   * Static softmax shift as in the other prefill kernel: when the score bound B implied
 //     by the norm weights is moderate (B <= 48 log2 units), the score accumulators start
-//     at -B and p = exp2(s - B) lies in [2^-2B, 1] with no running max; otherwise an
-//     online-max variant runs (both are launched; each returns unless selected).
+//     at -B and p = exp2(s - B) lies in [2^-2B, 1] with no running max; otherwise the
+//     online-max form runs (one launch carries both; the bound picks one).
 #include <type_traits>
 
 #include "common.h"
@@ -162,8 +162,11 @@ __device__ __forceinline__ float bf16_word(uint32_t w, int half) {
   return half ? bf16_hi_to_f32(w) : bf16_lo_to_f32(w);
 }
 
+// The stream of one workgroup; `sinit` starts every score accumulator: -B for the static
+// shift (so p <= 1), 0 for the online max. The norm weights and RoPE frequencies are in
+// LDS already.
 template <bool STATIC>
-__global__ __launch_bounds__(kThreads, 1) void swa_stream_kernel(const SArgs p) {
+__device__ __forceinline__ void swa_stream_body(const SArgs& p, const float sinit) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   float* sWq = (float*)(smem + kOffW);
   float* sWk = sWq + kD;
@@ -176,33 +179,6 @@ __global__ __launch_bounds__(kThreads, 1) void swa_stream_kernel(const SArgs p) 
   const int ph = wave >> 2;    // which 16 positions of the step
   const int n = lane & 15;     // query column of this lane
   const int grp = lane >> 4;   // lane group: dims [32 grp, 32 grp + 32)
-
-  for (int i = tid; i < kD; i += kThreads) {
-    sWq[i] = p.wq[i] * p.qscale;
-    sWk[i] = p.wk[i];
-  }
-  if (tid < kRH) {
-    sFr[tid] = p.fr.hi[tid];
-    sFr[32 + tid] = p.fr.lo[tid];
-  }
-  __syncthreads();
-  // |s| <= d * max|wq * qscale| * max|wk| after RMSNorm (2% margin for bf16 operands).
-  // The static variant starts every score accumulator at -bound (so p <= 1); the online
-  // variant at 0.
-  float sinit = 0.f;
-  {
-    float wqm = 0.f, wkm = 0.f;
-    for (int c = lane; c < kD; c += 64) {
-      wqm = fmaxf(wqm, fabsf(sWq[c]));
-      wkm = fmaxf(wkm, fabsf(sWk[c]));
-    }
-    wqm = wave_max(wqm);
-    wkm = wave_max(wkm);
-    const float bound = (float)kD * wqm * wkm * 1.02f;
-    const bool use_static = bound <= kStaticShiftMax;
-    if (use_static != STATIC) return;
-    if (STATIC) sinit = -bound;
-  }
 
   const int lin = blockIdx.x;
   const int hb = lin % p.n_hb;
@@ -613,10 +589,39 @@ __global__ __launch_bounds__(kThreads, 1) void swa_stream_kernel(const SArgs p) 
   }
 }
 
-template <bool STATIC>
-hipError_t set_smem() {
-  return ensure_dynamic_smem((const void*)swa_stream_kernel<STATIC>, kSmem);
+// One launch: the score bound is the same for every workgroup, so they all take the same
+// form (static shift when the bound allows it, else the online max).
+__global__ __launch_bounds__(kThreads, 1) void swa_stream_kernel(const SArgs p) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  float* sWq = (float*)(smem + kOffW);
+  float* sWk = sWq + kD;
+  float* sFr = (float*)(smem + kOffFr);
+  const int tid = threadIdx.x, lane = tid & 63;
+  for (int i = tid; i < kD; i += kThreads) {
+    sWq[i] = p.wq[i] * p.qscale;
+    sWk[i] = p.wk[i];
+  }
+  if (tid < kRH) {
+    sFr[tid] = p.fr.hi[tid];
+    sFr[32 + tid] = p.fr.lo[tid];
+  }
+  __syncthreads();
+  // |s| <= d * max|wq * qscale| * max|wk| after RMSNorm (2% margin for bf16 operands).
+  float wqm = 0.f, wkm = 0.f;
+  for (int c = lane; c < kD; c += 64) {
+    wqm = fmaxf(wqm, fabsf(sWq[c]));
+    wkm = fmaxf(wkm, fabsf(sWk[c]));
+  }
+  wqm = wave_max(wqm);
+  wkm = wave_max(wkm);
+  const float bound = (float)kD * wqm * wkm * 1.02f;
+  if (bound <= kStaticShiftMax)
+    swa_stream_body<true>(p, -bound);
+  else
+    swa_stream_body<false>(p, 0.f);
 }
+
+hipError_t set_smem() { return ensure_dynamic_smem((const void*)swa_stream_kernel, kSmem); }
 
 }  // namespace
 
@@ -667,12 +672,9 @@ hipError_t launch_swa_stream(const PrefillArgs& a, hipStream_t s) {
   }
   const int n_seg = (ka.n_steps + ka.seg_steps - 1) / ka.seg_steps;
   const int n_blocks = ka.n_hb * n_seg;
-  e = set_smem<true>();
+  e = set_smem();
   if (e != hipSuccess) return e;
-  e = set_smem<false>();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(swa_stream_kernel<true>, dim3(n_blocks), dim3(kThreads), kSmem, s, ka);
-  hipLaunchKernelGGL(swa_stream_kernel<false>, dim3(n_blocks), dim3(kThreads), kSmem, s, ka);
+  hipLaunchKernelGGL(swa_stream_kernel, dim3(n_blocks), dim3(kThreads), kSmem, s, ka);
   return hipGetLastError();
 }
 
