@@ -256,30 +256,10 @@ int zgattn_global_prefill(const zgattn_desc* d, const void* q, const void* k, co
   if (workspace) {
     if (workspace_bytes < zgattn_global_prefill_workspace_bytes(d) || !aligned16(workspace))
       return ZGATTN_EWORKSPACE;
-    NormRopeArgs n;
-    n.x = k;
-    n.w = wk;
-    n.pos = nullptr;
-    n.y = workspace;
-    n.B = a.B;
-    n.T = a.T;
-    n.H = a.Hkv;
-    n.d = a.d;
-    n.ysb = (int64_t)a.Hkv * a.T * a.d;  // [B][Hkv][T][d]
-    n.yst = a.d;
-    n.ysh = (int64_t)a.T * a.d;
-    n.rdim = a.rdim;
-    n.pos_offset = a.pos_offset;
-    n.is_bf16 = 1;
-    n.eps = a.eps;
-    n.out_scale = 1.0f;
-    n.fr = a.fr;
-    hipError_t e = launch_qknorm_rope(n, s);
-    if (e != hipSuccess) return ZGATTN_EHIP;
+    // K~ rows [B][Hkv][T][d] and V tiles, one pre-pass
     a.kt = workspace;
     a.vt = (void*)((char*)workspace + prefill_kt_bytes((size_t)a.B * a.Hkv * a.T, a.d));
-    e = launch_v_tiles(a, s);
-    if (e != hipSuccess) return ZGATTN_EHIP;
+    if (launch_kv_prepass(a, s) != hipSuccess) return ZGATTN_EHIP;
   }
   return hip_status(launch_prefill_bf16(a, s));
 }
@@ -412,32 +392,10 @@ int zgattn_global_prefill_varlen(const zgattn_desc* d, const int32_t* cu_seqlens
     if (workspace_bytes < zgattn_global_prefill_varlen_workspace_bytes(d, n_docs) ||
         !aligned16(workspace))
       return ZGATTN_EWORKSPACE;
-    NormRopeArgs n;
-    n.x = k;
-    n.w = wk;
-    n.pos = nullptr;
-    n.y = workspace;
-    n.B = 1;
-    n.T = a.T;
-    n.H = a.Hkv;
-    n.d = a.d;
-    n.ysb = 0;
-    n.yst = a.d;                          // [Hkv][T][d]
-    n.ysh = (int64_t)a.T * a.d;
-    n.rdim = a.rdim;
-    n.pos_offset = a.pos_offset;
-    n.is_bf16 = 1;
-    n.eps = a.eps;
-    n.out_scale = 1.0f;
-    n.fr = a.fr;
-    n.cu = cu_seqlens;
-    n.n_docs = n_docs;
-    hipError_t e = launch_qknorm_rope(n, s);
-    if (e != hipSuccess) return ZGATTN_EHIP;
+    // K~ rows [Hkv][T][d] (positions restart at each document) and per-document V tiles
     a.kt = workspace;
     a.vt = (void*)((char*)workspace + prefill_kt_bytes((size_t)a.Hkv * a.T, a.d));
-    e = launch_v_tiles(a, s);
-    if (e != hipSuccess) return ZGATTN_EHIP;
+    if (launch_kv_prepass(a, s) != hipSuccess) return ZGATTN_EHIP;
   }
   return hip_status(launch_prefill_bf16(a, s));
 }

@@ -27,7 +27,7 @@ struct PrefillArgs {
   const float* wq;
   const float* wk;
   void* kt;           // bf16 normalised+rotated K, [B][Hkv][T][d] (global with workspace) or nullptr
-  void* vt;           // bf16 V as transposed 64-key tiles (with kt), see launch_v_tiles
+  void* vt;           // bf16 V as transposed 64-key tiles (with kt), see launch_kv_prepass
   int B, T, Hq, Hkv, d, window, rdim, pos_offset;
   int swa;            // 1: gated sliding window; 0: ungated full causal
   float eps;
@@ -58,7 +58,8 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 bool prefill_bf16_supported(int d, int group, int rdim);
 // Tile-transposed V for the global path: [B][Hkv][ceil(T/64)][d][64] bf16.
 size_t prefill_vtiles_bytes(int B, int Hkv, int T, int d);
-hipError_t launch_v_tiles(const PrefillArgs& a, hipStream_t s);
+// The global path's pre-pass: K~ rows into a.kt and V tiles into a.vt (dense or packed).
+hipError_t launch_kv_prepass(const PrefillArgs& a, hipStream_t s);
 // Streaming sliding-window kernel for the model's layer shape (d 128, 4 query heads per KV
 // head, rotary_dim 42, window <= 128); launch_prefill_bf16 routes such calls to it.
 bool swa_stream_supported(const PrefillArgs& a);

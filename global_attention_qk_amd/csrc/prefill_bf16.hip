@@ -108,7 +108,7 @@ struct KArgs {
   const float* wq;
   const float* wk;
   const bf16* kt;
-  const bf16* vt;     // tile-transposed V (with kt), see v_tiles_kernel
+  const bf16* vt;     // tile-transposed V (with kt), see kv_prepass_kernel
   int T, Hq, Hkv, window, rdim, pos_offset;
   int group, bmp, n_qtiles, n_hb;
   float eps, qscale;
@@ -1102,21 +1102,36 @@ hipError_t launch_t(const KArgs& ka, int n_blocks, hipStream_t s) {
 }
 
 
-// V tile transpose for the global path: V [B, T, Hkv, D] -> vt [B, Hkv, ceil(T/64), D, 64]
-// with the 64 keys of each row in the slot order of the LDS V^T tile (keys past T are 0).
-// The attention kernel then stages V^T tiles with plain 16-byte copies.
-// Packed documents (cu != nullptr, B == 1): blockIdx.z is the document, its tiles start at
-// its own first token and go to slots doc_tile_base(start, doc) .. of each KV head's
-// vt_slots.
+// The global path's pre-pass, one 64-key tile per workgroup:
+//   * K~ rows (RMSNorm * wk, then partial RoPE at the row's position within its sequence)
+//     into the workspace's row layout [B][Hkv][T][D] (packed: [Hkv][T][D]). Rows are written
+//     only for positions inside the sequence (in the dense layout the rows after a head's
+//     last one belong to the next head). D / 8 lanes per row, 8 dims each; rotated partners
+//     go through LDS.
+//   * V transposed into tiles [B][Hkv][ceil(T/64)][D][64] with the 64 keys of each row in
+//     the slot order of the attention kernel's LDS V^T tile (keys past the end are 0), so
+//     that the attention kernel stages V^T tiles with plain 16-byte copies. Packed
+//     documents (cu != nullptr, B == 1): blockIdx.z is the document, its tiles start at its
+//     own first token and go to slots doc_tile_base(start, doc) .. of each KV head's
+//     vt_slots.
+// Every K and V load of a thread is issued before the first is used.
 template <int D>
-__global__ __launch_bounds__(256) void v_tiles_kernel(const bf16* v, bf16* vt, int T, int Hkv,
-                                                      int n_kt, const int32_t* cu, int max_len,
-                                                      int vt_slots) {
-  __shared__ __attribute__((aligned(16))) bf16 s[kBN][D + 8];
+__global__ __launch_bounds__(256) void kv_prepass_kernel(const bf16* k, const bf16* v,
+                                                         const float* wk, bf16* kt, bf16* vt,
+                                                         int T, int Hkv, int n_kt,
+                                                         const int32_t* cu, int max_len,
+                                                         int vt_slots, int rdim, int pos_offset,
+                                                         float eps, RopeFreq fr) {
+  constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  constexpr int RPP = 256 / CPR;              // rows per pass (16 lanes per row at d 128)
+  constexpr int NP = kBN / RPP;               // passes over the tile's 64 rows
+  __shared__ __attribute__((aligned(16))) bf16 sv[kBN][D + 8];
+  __shared__ float sx[RPP][D + 4];
+  __shared__ float2 st[RPP][kMaxHalfRot / 2 + 1];
   const int tile = blockIdx.x, hb = blockIdx.y;
   const int b = hb / Hkv, kvh = hb % Hkv;
-  const int tid = threadIdx.x;
-  size_t seq0 = (size_t)b * T;
+  const int tid = threadIdx.x, sub = tid % CPR, r0 = tid / CPR;
+  size_t seq0 = (size_t)b * T, kt_row0 = ((size_t)b * Hkv + kvh) * T;
   int len = T;
   size_t out_tile = (size_t)hb * n_kt + tile;
   if (cu) {
@@ -1125,22 +1140,77 @@ __global__ __launch_bounds__(256) void v_tiles_kernel(const bf16* v, bf16* vt, i
     doc_range(cu, doc, T, max_len, start, len);
     if (tile * kBN >= len) return;
     seq0 = start;
+    kt_row0 = (size_t)kvh * T + start;
     out_tile = (size_t)kvh * vt_slots + doc_tile_base(start, doc) + tile;
   }
-  for (int c = tid; c < kBN * (D / 8); c += 256) {
-    const int kr = c / (D / 8), dc = c % (D / 8);
-    const int pos = tile * kBN + kr;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (pos < len) val = *(const u32x4*)(v + ((seq0 + pos) * Hkv + kvh) * D + dc * 8);
-    *(u32x4*)&s[kr][dc * 8] = val;
+  // all loads first: pass i covers rows r0 + RPP i
+  u32x4 kv4[NP], vv4[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int pos = tile * kBN + r0 + RPP * i;
+    kv4[i] = vv4[i] = (u32x4){0u, 0u, 0u, 0u};
+    if (pos < len) {
+      const size_t off = ((seq0 + pos) * Hkv + kvh) * D + sub * 8;
+      kv4[i] = *(const u32x4*)(k + off);
+      vv4[i] = *(const u32x4*)(v + off);
+    }
   }
-  __syncthreads();
+  float w[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) w[e] = wk[sub * 8 + e];
+  const int half = rdim >> 1;
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int r = r0 + RPP * i;          // tile row of this lane in pass i
+    const int pos = tile * kBN + r;
+    *(u32x4*)&sv[r][sub * 8] = vv4[i];
+    // RoPE table of the pass's rows (rows past the end are computed and unused)
+    for (int e = tid; e < RPP * half; e += 256) {
+      const int rr = e / half, j = e - rr * half;
+      float c, sn;
+      rope_cos_sin(pos_offset + tile * kBN + rr + RPP * i, fr.hi[j], fr.lo[j], c, sn);
+      st[rr][j] = make_float2(c, sn);
+    }
+    // normalise (sum of squares over the row's lanes) and stage for the partner reads
+    const uint32_t w4[4] = {kv4[i].x, kv4[i].y, kv4[i].z, kv4[i].w};
+    float x[8], ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = bf16_lo_to_f32(w4[e]);
+      x[2 * e + 1] = bf16_hi_to_f32(w4[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
+    ss = group_sum<CPR>(ss);
+    const float rn = 1.0f / sqrtf(ss / D + eps);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x[e] = x[e] * rn * w[e];
+      sx[r0][sub * 8 + e] = x[e];
+    }
+    __syncthreads();
+    // rotate and store the K~ rows inside the sequence
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      // dims past rotary_dim read pair 0 and partner 0 and keep their value
+      const int c = sub * 8 + e;
+      const bool rot = c < rdim, lower = c < half;
+      const float2 cs = st[r0][rot ? (lower ? c : c - half) : 0];
+      const float pr = sx[r0][rot ? (lower ? c + half : c - half) : 0];
+      const float y = lower ? x[e] * cs.x - pr * cs.y : x[e] * cs.x + pr * cs.y;
+      o[e] = (bf16)(rot ? y : x[e]);
+    }
+    if (pos < len) *(bf16x8*)(kt + (kt_row0 + pos) * D + sub * 8) = o;
+    __syncthreads();   // sx / st free for the next pass; sv complete after the last
+  }
+  // V^T tile, keys in slot order (rows past the end were staged as zeros)
   bf16* out = vt + out_tile * (kBN * D);
   for (int c = tid; c < D * (kBN / 8); c += 256) {
     const int d = c / (kBN / 8), sc = c % (kBN / 8);
     bf16x8 o;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = s[vt_slot(sc * 8 + e)][d];  // the slot map is an involution
+    for (int e = 0; e < 8; ++e) o[e] = sv[vt_slot(sc * 8 + e)][d];  // the slot map is an involution
     *(bf16x8*)(out + d * kBN + sc * 8) = o;
   }
 }
@@ -1213,19 +1283,22 @@ size_t prefill_vtiles_bytes_varlen(int Hkv, int T, int n_docs, int d) {
   return (size_t)Hkv * varlen_vtile_slots(T, n_docs) * kBN * d * 2;
 }
 
-hipError_t launch_v_tiles(const PrefillArgs& a, hipStream_t s) {
+hipError_t launch_kv_prepass(const PrefillArgs& a, hipStream_t s) {
   const bool packed = a.cu != nullptr;
   const int n_kt = ((packed ? a.max_len : a.T) + kBN - 1) / kBN;
-  const dim3 grid(n_kt, a.B * a.Hkv, packed ? a.n_docs : 1);
+  const dim3 grid(n_kt, packed ? a.Hkv : a.B * a.Hkv, packed ? a.n_docs : 1);
   const int slots = packed ? varlen_vtile_slots(a.T, a.n_docs) : 0;
   if (n_kt == 0) return hipSuccess;
   if (a.d == 128)
-    hipLaunchKernelGGL(v_tiles_kernel<128>, grid, dim3(256), 0, s, (const bf16*)a.v, (bf16*)a.vt, a.T,
-                       a.Hkv, n_kt, a.cu, a.max_len, slots);
+    hipLaunchKernelGGL(kv_prepass_kernel<128>, grid, dim3(256), 0, s, (const bf16*)a.k,
+                       (const bf16*)a.v, a.wk, (bf16*)a.kt, (bf16*)a.vt, a.T, a.Hkv, n_kt, a.cu,
+                       a.max_len, slots, a.rdim, a.pos_offset, a.eps, a.fr);
   else
-    hipLaunchKernelGGL(v_tiles_kernel<64>, grid, dim3(256), 0, s, (const bf16*)a.v, (bf16*)a.vt, a.T,
-                       a.Hkv, n_kt, a.cu, a.max_len, slots);
+    hipLaunchKernelGGL(kv_prepass_kernel<64>, grid, dim3(256), 0, s, (const bf16*)a.k,
+                       (const bf16*)a.v, a.wk, (bf16*)a.kt, (bf16*)a.vt, a.T, a.Hkv, n_kt, a.cu,
+                       a.max_len, slots, a.rdim, a.pos_offset, a.eps, a.fr);
   return hipGetLastError();
 }
+
 
 }  // namespace zg

@@ -53,7 +53,7 @@ size_t prefill_vtiles_bytes(int B, int Hkv, int T, int d) {
 size_t prefill_vtiles_bytes_varlen(int Hkv, int T, int n_docs, int d) {
   return (size_t)Hkv * (T / 64 + n_docs) * 64 * d * 2;
 }
-hipError_t launch_v_tiles(const PrefillArgs&, hipStream_t) {
+hipError_t launch_kv_prepass(const PrefillArgs&, hipStream_t) {
   ++stub::launches;
   ++stub::aux_launches;
   return hipSuccess;

@@ -5,7 +5,7 @@
 namespace stub {
 extern int launches;              // kernel launches requested (any launcher)
 extern int prefill_launches;      // launch_prefill_bf16 / launch_prefill_f32
-extern int aux_launches;          // qknorm_rope / v_tiles
+extern int aux_launches;          // qknorm_rope / the global pre-pass
 extern int decode_launches;       // single-layer and batched decode launchers
 extern int batched_layers;        // layers passed to the batched decode launchers
 extern int scratch_lookups;       // decode_noalloc_scratch calls

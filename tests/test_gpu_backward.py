@@ -100,6 +100,14 @@ def test_backward_global_with_forward_lse(T):
     _check(2 if T == 300 else 1, T, 8, 2, 128, None, 1700 + T, fwd_lse=True)
 
 
+@pytest.mark.parametrize("window,lse", [(None, True), (None, False), (128, False)])
+def test_backward_ragged_top_tile(window, lse):
+    # T = 1000 (not a multiple of 64): each dK/dV workgroup of 256 keys meets a ragged last
+    # query tile, a run of fully visible tiles and the diagonal tiles; B = 2, 4 query heads
+    # per KV head
+    _check(2, 1000, 8, 2, 128, window, 2000, fwd_lse=lse)
+
+
 def test_backward_forward_lse_head_dim_64_offset():
     _check(1, 150, 4, 1, 64, None, 1800, pos_offset=1000, fwd_lse=True)
 
