@@ -19,6 +19,7 @@
 // accumulators), the norm/RoPE backward for q and k rows with per-block weight partials,
 // and the reduction of those partials.
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 #include "launch.h"
@@ -411,6 +412,17 @@ __device__ __forceinline__ void mfma_agpr_late(f32x16& acc, const bf16x8& a, con
 }
 __device__ __forceinline__ void pin_agpr(f32x16& v) { asm volatile("" : "+a"(v)); }
 
+// f(integral_constant<int, 0>) .. f(integral_constant<int, N - 1>), in order: a loop whose
+// index is a compile-time constant in every iteration.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 template <int D, bool SWA>
 __global__ __launch_bounds__(kTKV, 1) void bwd_dkdv_kernel(const BArgs p) {
   constexpr int KS = D / 16;
@@ -525,101 +537,109 @@ __global__ __launch_bounds__(kTKV, 1) void bwd_dkdv_kernel(const BArgs p) {
 
   // One step over query tile i0 from buffer tb. MASKED: some (query, key) pair of the
   // step is not visible (diagonal tiles, the window's edges, rows or keys past T).
+  // The step is a stream of slots, each one LDS operand read and the two products (key
+  // blocks 0 and 1) that use it: per 32-query block qb, KS dP slots (dA rows), KS S slots
+  // (Q~ rows), then 4 DB dV / dK slots (dA^T, then Q~^T, per (j, db)). Operands are read
+  // kAhead slots before their products, across the phase boundaries, so that the LDS
+  // latency stays hidden behind the products; the P and dS vector work of a block sits
+  // between its S and its dV / dK slots. The dP and S accumulators start at -D and -L
+  // (the C operand of the first product, from the step's statistics, which hold the
+  // negated values): Q~ is stored times scale * log2(e), so P = exp2(S acc) and
+  // dS = P * (dP acc). The lane's rows are qb * 32 + 8 (r / 4) + 4 hi + r % 4, the
+  // accumulator layout of four 4-row groups.
+  constexpr int NSQ = 2 * KS + 4 * DB;   // slots per 32-query block
+  constexpr int NS = 2 * NSQ;            // slots per step
+  constexpr int kAhead = 2;
   auto step = [&](const char* tb, int i0, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     const float* sL = (const float*)(tb + 4 * TILE);
     const float* sD = sL + kQB;
+    auto read_op = [&](int u) -> bf16x8 {
+      const int qb = u / NSQ, w = u % NSQ;
+      if (w < KS) return *(const bf16x8*)(tb + TILE + roff[w] + qb * 32 * RB);
+      if (w < 2 * KS) return *(const bf16x8*)(tb + roff[w - KS] + qb * 32 * RB);
+      const int t = (w - 2 * KS) >> 1, j = t / DB, db = t % DB;
+      const int off = toff[2 * qb + j] + db * 32 * 128;
+      return *(const bf16x8*)(tb + ((w & 1) ? 2 : 3) * TILE + off);
+    };
+    auto read_stats = [&](const float* src, int qb) {
+      f32x16 x;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      // dP and S of both key blocks with accumulators that start at -D and -L (the C
-      // operand of the first product, read straight from the step's statistics, which
-      // hold the negated values): Q~ is stored times scale * log2(e), so P = exp2(S acc)
-      // and dS = P * (dP acc). The lane's rows are qb * 32 + 8 (r / 4) + 4 hi + r % 4,
-      // which is the accumulator layout of four 4-row groups.
-      f32x16 dp[2], s[2];
-      {
-        f32x16 negd;
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const float4 v = *(const float4*)(sD + qb * 32 + 8 * g4 + 4 * hi);
-          negd[4 * g4] = v.x; negd[4 * g4 + 1] = v.y; negd[4 * g4 + 2] = v.z; negd[4 * g4 + 3] = v.w;
-        }
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 ad = *(const bf16x8*)(tb + TILE + roff[ks] + qb * 32 * RB);
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-            dp[kb] = mfma32(ad, vreg[kb][ks], ks == 0 ? negd : dp[kb]);
-        }
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const float4 v = *(const float4*)(src + qb * 32 + 8 * g4 + 4 * hi);
+        x[4 * g4] = v.x; x[4 * g4 + 1] = v.y; x[4 * g4 + 2] = v.z; x[4 * g4 + 3] = v.w;
       }
-      __builtin_amdgcn_sched_barrier(0);
-      {
-        f32x16 negl;
+      return x;
+    };
+    bf16x8 ops[kAhead];
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const float4 v = *(const float4*)(sL + qb * 32 + 8 * g4 + 4 * hi);
-          negl[4 * g4] = v.x; negl[4 * g4 + 1] = v.y; negl[4 * g4 + 2] = v.z; negl[4 * g4 + 3] = v.w;
-        }
+    for (int i = 0; i < kAhead; ++i) ops[i] = read_op(i);
+    f32x16 negc = read_stats(sD, 0);
+    f32x16 dp[2], sc[2];
+    bf16x8 pp[2][2], dd[2][2];
+    static_for<NS>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      constexpr int qb = u / NSQ, w = u % NSQ;
+      const bf16x8 a = ops[0];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 aq = *(const bf16x8*)(tb + roff[ks] + qb * 32 * RB);
+      for (int i = 0; i + 1 < kAhead; ++i) ops[i] = ops[i + 1];
+      if constexpr (u + kAhead < NS) ops[kAhead - 1] = read_op(u + kAhead);
+      if constexpr (w < KS) {
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-            s[kb] = mfma32(aq, kreg[kb][ks], ks == 0 ? negl : s[kb]);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // P and dS, rounded to bf16 in pairs: the B operands of the dV and dK products
-      u32x4 pw[2][2], dw[2][2];
+        for (int kb = 0; kb < 2; ++kb) dp[kb] = mfma32(a, vreg[kb][w], w == 0 ? negc : dp[kb]);
+        if constexpr (w == KS - 2) negc = read_stats(sL, qb);
+      } else if constexpr (w < 2 * KS) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int key = wk0 + 32 * kb + l32;
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          float pr[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            pr[e] = fast_exp2(s[kb][r + e]);
-            if (MASKED) {
-              const int qi = i0 + qb * 32 + 8 * ((r + e) >> 2) + 4 * hi + ((r + e) & 3);
-              const bool vis = key < T && qi < T && key <= qi && (!SWA || key > qi - p.window);
-              pr[e] = vis ? pr[e] : 0.f;
-            }
-          }
-          const bf16x2 pb = {(bf16)pr[0], (bf16)pr[1]};
-          const bf16x2 db2 = {(bf16)(pr[0] * dp[kb][r]), (bf16)(pr[1] * dp[kb][r + 1])};
-          pw[kb][r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, pb);
-          dw[kb][r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, db2);
-        }
-      }
-      bf16x8 pp[2][2], dd[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          pp[kb][j] = __builtin_bit_cast(bf16x8, pw[kb][j]);
-          dd[kb][j] = __builtin_bit_cast(bf16x8, dw[kb][j]);
-        }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int off = toff[2 * qb + j] + db * 32 * 128;
-          const bf16x8 av = *(const bf16x8*)(tb + 3 * TILE + off);
-          const bf16x8 ak = *(const bf16x8*)(tb + 2 * TILE + off);
+        for (int kb = 0; kb < 2; ++kb)
+          sc[kb] = mfma32(a, kreg[kb][w - KS], w == KS ? negc : sc[kb]);
+        if constexpr (w == 2 * KS - 1) {
+          // P and dS, rounded to bf16 in pairs: the B operands of the dV and dK products
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) {
-            if (db == 0) {
-              mfma_agpr(dvt[kb][db], av, pp[kb][j]);
-              mfma_agpr(dkt[kb][db], ak, dd[kb][j]);
-            } else {
-              mfma_agpr_late(dvt[kb][db], av, pp[kb][j]);
-              mfma_agpr_late(dkt[kb][db], ak, dd[kb][j]);
+            const int key = wk0 + 32 * kb + l32;
+            u32x4 pw[2], dw[2];
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+              float pr[2];
+#pragma unroll
+              for (int e = 0; e < 2; ++e) {
+                pr[e] = fast_exp2(sc[kb][r + e]);
+                if (MASKED) {
+                  const int qi = i0 + qb * 32 + 8 * ((r + e) >> 2) + 4 * hi + ((r + e) & 3);
+                  const bool vis =
+                      key < T && qi < T && key <= qi && (!SWA || key > qi - p.window);
+                  pr[e] = vis ? pr[e] : 0.f;
+                }
+              }
+              const bf16x2 pb = {(bf16)pr[0], (bf16)pr[1]};
+              const bf16x2 db2 = {(bf16)(pr[0] * dp[kb][r]), (bf16)(pr[1] * dp[kb][r + 1])};
+              pw[r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, pb);
+              dw[r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, db2);
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              pp[kb][j] = __builtin_bit_cast(bf16x8, pw[j]);
+              dd[kb][j] = __builtin_bit_cast(bf16x8, dw[j]);
             }
           }
         }
-    }
+      } else {
+        constexpr int t = (w - 2 * KS) >> 1, j = t / DB, db = t % DB;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          // the first products after the vector block wait for its last writes
+          if constexpr (w & 1) {
+            if constexpr (db == 0) mfma_agpr(dkt[kb][db], a, dd[kb][j]);
+            else mfma_agpr_late(dkt[kb][db], a, dd[kb][j]);
+          } else {
+            if constexpr (db == 0) mfma_agpr(dvt[kb][db], a, pp[kb][j]);
+            else mfma_agpr_late(dvt[kb][db], a, pp[kb][j]);
+          }
+        }
+        if constexpr (qb == 0 && w == NSQ - 2) negc = read_stats(sD, 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
 
   fetch(0, 0);
