@@ -412,17 +412,6 @@ __device__ __forceinline__ void mfma_agpr_late(f32x16& acc, const bf16x8& a, con
 }
 __device__ __forceinline__ void pin_agpr(f32x16& v) { asm volatile("" : "+a"(v)); }
 
-// f(integral_constant<int, 0>) .. f(integral_constant<int, N - 1>), in order: a loop whose
-// index is a compile-time constant in every iteration.
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
 template <int D, bool SWA>
 __global__ __launch_bounds__(kTKV, 1) void bwd_dkdv_kernel(const BArgs p) {
   constexpr int KS = D / 16;

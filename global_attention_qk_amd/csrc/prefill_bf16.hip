@@ -34,6 +34,7 @@
 //     workspace that the tiles read directly; for SWA layers (each K tile visited by
 //     about three query tiles) the transform is fused into the tile load.
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 #include "launch.h"
@@ -61,7 +62,7 @@ constexpr int kWavesPerBlock = ZG_PREFILL_WAVES;
 constexpr int kDmaBufs = ZG_DMA_BUFS;
 // Phase of the pipelined tile (0 A .. 3 D) whose slots issue the DMA pieces.
 #ifndef ZG_DMA_PHASE
-#define ZG_DMA_PHASE 2
+#define ZG_DMA_PHASE 3
 #endif
 constexpr int kDmaPhase = ZG_DMA_PHASE;
 constexpr int kBN = 64;           // keys per tile
@@ -576,12 +577,13 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p, const int lin, cons
     }
   };
 
-  // LDS DMA of tile kt into buffer buf of the pipelined path. Piece j (0 .. KS-1) is one
+  // LDS DMA of tile kt into buffer buf of the pipelined path. Piece j (0 .. NPW-1) is one
   // 1 KiB block per wave, its 64 lanes landing in consecutive 16-byte slots: the first
-  // D/32 pieces cover K~ (512 / D rows per block), the rest V^T (8 rows per block).
+  // KPW pieces cover K~ (512 / D rows per block), the rest V^T (8 rows per block).
   // Each lane fetches the chunk that the swizzle puts in its slot; K~ rows past the end
   // are clamped to the last row (masked keys).
-  constexpr int KPW = D / 32;
+  constexpr int KPW = D / 8 / NW;   // K~ (and V^T) pieces per wave and tile
+  constexpr int NPW = 2 * KPW;
   const uint32_t lds_smem = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
   // Per-lane source offsets of the K~ pieces within a tile (row r of the tile, chunk c),
   // the same for every tile. A tile past the sequence end reads on into the next head's
@@ -816,12 +818,15 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p, const int lin, cons
       }
     }
   };
-  // Two query blocks per wave, static shift, K~ / V tiles from the workspace: a fenced
-  // software pipeline over the tile's two 32-key blocks, one wave per SIMD,
+  // Static shift, K~ / V tiles from the workspace: a fenced software pipeline over the
+  // tile's two 32-key blocks,
   //   A: QK(0) | B: QK(1) + softmax(0) | C: P.V(0) + softmax(1) + DMA | D: P.V(1)
   // with the vector work cut into pieces placed between the MFMAs so that it issues in
   // their shadow (the P.V products are inline assembly, so the order is pinned with
-  // scheduling barriers rather than left to the scheduler).
+  // scheduling barriers rather than left to the scheduler). Two query blocks per wave and
+  // one wave per SIMD by default (ZG_GLOBAL_WAVES=4); one block per wave and two waves per
+  // SIMD with ZG_GLOBAL_WAVES=8 (twice the LDS operand reads per product: 3 % slower at
+  // T = 262,144, level at B = 4, T = 4096).
   // Per-lane byte offsets of the operand reads within a buffer: the K~ row of a lane is
   // kb*32 + l32 and its chunk 2*ks + hi; the V^T row is db*32 + l32 and its chunk
   // 4*kb + 2*jh + hi. Both swizzles depend on the row only through l32 & 15, so the
@@ -834,11 +839,9 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p, const int lin, cons
   for (int x = 0; x < 4; ++x) voff[x] = S::kDK + l32 * 128 + chunk_pos<8>(l32, 2 * x + hi) * 16;
   auto compute_pipe = [&](int kt, int buf, auto masked_tag, int dma_kt, int dma_buf) {
     constexpr bool MASKED = decltype(masked_tag)::value;
-    static_assert(QB == 2, "pipelined path holds two query blocks per wave");
-    constexpr int QK_SPP = 8 / KS;               // softmax pieces per QK step
     constexpr int PV_STEPS = 2 * DB;
-    constexpr int PV_SPP = 8 / PV_STEPS;         // softmax pieces per P.V step
-    static_assert(KS == 2 * KPW && PV_STEPS == KS, "one DMA piece per slot of a phase");
+    constexpr int NP = 4 * QB;   // softmax pieces per 32-key block
+    static_assert(PV_STEPS == KS && KS % NPW == 0, "DMA pieces spread evenly over a phase");
     const char* tb = smem + buf * S::kDBuf;
     const int k0 = kt * kBN;
     int rel[QB];
@@ -852,7 +855,7 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p, const int lin, cons
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) sc[kb][qb][r] = sinit;
-    // softmax piece j (0..7) of block kb: query block j / 4, half j / 2 % 2 of the 16
+    // softmax piece j (0 .. NP-1) of block kb: query block j / 4, half j / 2 % 2 of the 16
     // scores, four of them (j % 2)
     auto sm_piece = [&](int kb, int j) {
       const int qb = j >> 2, jh = (j >> 1) & 1, eh = j & 1;
@@ -876,7 +879,7 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p, const int lin, cons
     };
     // The tile as one stream of MFMA slots (each: one A operand from LDS, one product
     // per query block): A = K~ block 0 by k-step, B = K~ block 1, C = V^T block 0 by
-    // (d block, key half), D = V^T block 1. Each slot's operand is read two slots ahead.
+    // (d block, key half), D = V^T block 1.
     constexpr int NSLOT = 2 * KS + 2 * PV_STEPS;
     auto read_op = [&](int u) -> bf16x8 {
       if (u < 2 * KS) {
@@ -888,43 +891,52 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p, const int lin, cons
       const int db = t % DB, jh = t / DB;
       return *(const bf16x8*)(tb + voff[2 * kb + jh] + db * 32 * 128);
     };
-    bf16x8 op0 = read_op(0), op1 = read_op(1);
+    // Operand o is read at slot rd_slot(o). With two query blocks per wave (one wave per
+    // SIMD) the operands of phases A, B and C are read during phase A, three per slot, so
+    // that the softmax phases issue no LDS reads (at T = 262,144 0.7 % faster than every
+    // operand two slots ahead, at B = 4, T = 4096 3 %), and phase D's two slots ahead; with
+    // one query block per wave (two waves per SIMD, half the registers) every operand two
+    // slots ahead.
+    auto rd_slot = [](int o) { return (QB == 2 && o < 3 * KS) ? o / 3 : (o < 2 ? 0 : o - 2); };
+    bf16x8 ops[NSLOT];
+    static_for<NSLOT>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
 #pragma unroll
-    for (int u = 0; u < NSLOT; ++u) {
-      const bf16x8 a = op0;
-      op0 = op1;
-      if (u + 2 < NSLOT) op1 = read_op(u + 2);
-      if (u < 2 * KS) {
-        const int kb = u / KS, ks = u % KS;
+      for (int o = 0; o < NSLOT; ++o)
+        if (rd_slot(o) == u) ops[o] = read_op(o);
+      const bf16x8 a = ops[u];
+      if constexpr (u < 2 * KS) {
+        constexpr int kb = u / KS, ks = u % KS;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           sc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[qb][ks], sc[kb][qb], 0, 0, 0);
-        if (kb == 1) {
+        if constexpr (kb == 1) {
           // B: softmax of block 0 under the block-1 score products
 #pragma unroll
-          for (int w = 0; w < QK_SPP; ++w) sm_piece(0, ks * QK_SPP + w);
+          for (int w = ks * NP / KS; w < (ks + 1) * NP / KS; ++w) sm_piece(0, w);
         }
       } else {
-        const int t = (u - 2 * KS) % PV_STEPS, kb = (u - 2 * KS) / PV_STEPS;
-        const int db = t % DB, jh = t / DB;
+        constexpr int t = (u - 2 * KS) % PV_STEPS, kb = (u - 2 * KS) / PV_STEPS;
+        constexpr int db = t % DB, jh = t / DB;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           mfma_acc_late(oacc[qb][db], a, __builtin_bit_cast(bf16x8, pw[kb][qb][jh]));
-        if (kb == 0) {
+        if constexpr (kb == 0) {
           // C: softmax of block 1 under the block-0 P.V products
 #pragma unroll
-          for (int w = 0; w < PV_SPP; ++w) sm_piece(1, t * PV_SPP + w);
+          for (int w = t * NP / PV_STEPS; w < (t + 1) * NP / PV_STEPS; ++w) sm_piece(1, w);
         }
       }
-      // a later tile goes to its buffer, one piece per slot of phase kDmaPhase
-      if (u / KS == kDmaPhase) dma_piece(dma_kt, dma_buf, u % KS);
+      // a later tile goes to its buffer, its NPW pieces spread over phase kDmaPhase
+      if constexpr (u / KS == kDmaPhase && (u % KS) % (KS / NPW) == 0)
+        dma_piece(dma_kt, dma_buf, (u % KS) / (KS / NPW));
       __builtin_amdgcn_sched_barrier(0);
-    }
+    });
   };
   auto nothing = [] {};
 
   int i = 0;
-  if constexpr (KPRE && QB == 2 && STATIC) {
+  if constexpr (KPRE && STATIC) {
     // K~ / V^T tiles go from the workspace straight into LDS (DMA), kDmaBufs - 1 tiles
     // ahead of their use, through kDmaBufs rotating buffers: one barrier per tile. Past
     // the end the last tile is fetched again into an idle buffer (in bounds, never read).
@@ -934,14 +946,14 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p, const int lin, cons
 #pragma unroll
     for (int a = 0; a < AHEAD; ++a)
 #pragma unroll
-      for (int j = 0; j < KS; ++j) dma_piece(tile_of(min(a, last)), a, j);
-    vm_wait<(AHEAD - 1) * KS>();
+      for (int j = 0; j < NPW; ++j) dma_piece(tile_of(min(a, last)), a, j);
+    vm_wait<(AHEAD - 1) * NPW>();
     __syncthreads();
     int cur = 0;
     auto step = [&](int i, auto masked_tag) {
       const int ahead = (cur + AHEAD) % kDmaBufs;
       compute_pipe(tile_of(i), cur, masked_tag, tile_of(min(i + AHEAD, last)), ahead);
-      vm_wait<(AHEAD - 1) * KS>();   // this wave's DMA of tile i + 1 has landed ...
+      vm_wait<(AHEAD - 1) * NPW>();   // this wave's DMA of tile i + 1 has landed ...
       __syncthreads();  // ... and every wave's; tile i's buffer may be overwritten
       cur = cur == kDmaBufs - 1 ? 0 : cur + 1;
     };
