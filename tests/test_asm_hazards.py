@@ -102,12 +102,15 @@ def _early_reads(body):
 
 @pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
                     reason="hipcc not available")
-@pytest.mark.parametrize("src_name,kernel", [("prefill_bf16.hip", "prefill_bf16_kernel"),
-                                             ("backward.hip", "bwd_dkdv_kernel")])
-def test_no_early_accumulator_reads(tmp_path, src_name, kernel):
+@pytest.mark.parametrize("src_name,kernel,extra", [
+    ("prefill_bf16.hip", "prefill_bf16_kernel", []),
+    # the global kernel's other layout (one query block per wave, two waves per SIMD)
+    ("prefill_bf16.hip", "prefill_bf16_kernel", ["-DZG_GLOBAL_WAVES=8"]),
+    ("backward.hip", "bwd_dkdv_kernel", [])])
+def test_no_early_accumulator_reads(tmp_path, src_name, kernel, extra):
     src = os.path.join(build_lib.CSRC, src_name)
     out = tmp_path / (src_name + ".s")
-    cmd = [build_lib.hipcc()] + build_lib.common_flags() + [
+    cmd = [build_lib.hipcc()] + build_lib.common_flags() + extra + [
         "-x", "hip", "--cuda-device-only", "-S", src, "-o", str(out)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
