@@ -6,17 +6,21 @@
 // (the last `window` tokens including the query for SWA, the whole prefix for global),
 // times V, then the elementwise sigmoid gate for SWA.
 //
-// Work decomposition (one workgroup = 4 wave64s = 256 query rows):
+// Work decomposition (one workgroup = 256 query rows):
 //   * The rows are all g = Hq/Hkv query heads of one KV head at 256/g consecutive
 //     positions, so every K/V tile staged in LDS serves the whole head group.
-//   * Each wave owns two 32-row query blocks. Scores are formed transposed,
+//   * Global layers with K~ / V tiles from the workspace: 4 wave64s, one per SIMD, each
+//     owning two 32-row query blocks (each LDS operand read feeds two products); the
+//     other forms: 8 wave64s of one block each. Scores are formed transposed,
 //     S^T = K~ . Q~^T with v_mfma_f32_32x32x16_bf16 (keys on the M side, queries on N),
 //     which leaves one query per lane; the probabilities then already sit in the
 //     B-operand layout of O^T += V^T . P^T, so no cross-lane shuffle is needed between
 //     the two products and the softmax row statistics are per-lane scalars.
-//   * V is transposed into LDS with the keys of each 16-key group permuted so that a
-//     lane's eight keys are one 16-byte LDS read. K/V tiles are double-buffered in LDS
-//     and the next tile's global loads are in flight while the current one is computed.
+//   * V is transposed with the keys of each 16-key group permuted so that a lane's eight
+//     keys are one 16-byte LDS read. Global layers: a pre-pass writes V as such tiles and
+//     the kernel moves K~ / V^T tiles from the workspace straight into three rotating LDS
+//     buffers by LDS DMA, two tiles ahead. The other forms stage the next tile through
+//     registers into two LDS buffers while the current one is computed.
 //   * Q~ is pre-multiplied by scale * log2(e) so that p = exp2(s - m).
 //   * Static shift: after RMSNorm every score obeys |s| <= B = qscale * d * max|wq| *
 //     max|wk| (RoPE keeps norms). When B is moderate, p = exp2(s - B) with the constant
