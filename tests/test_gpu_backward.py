@@ -168,3 +168,27 @@ def test_backward_sampled_rows_T8192(window):
         say("backward sampled", (T, window), name, f"err={err:.3e} lim={lim:.3e}")
         assert err <= lim, (name, err, lim)
 
+
+
+def _random_cases(n=8, seed=880011):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        d = int(rng.choice([64, 128]))
+        Hkv = int(rng.choice([1, 2]))
+        Hq = Hkv * int(rng.choice([1, 2, 4, 8]))
+        B = int(rng.choice([1, 2]))
+        T = int(rng.integers(1, 701))
+        window = None if i % 2 == 0 else int(rng.integers(1, 201))
+        pos = int(rng.integers(0, 50_001))
+        lse = bool(window is None and rng.integers(0, 2))
+        cases.append((i, B, T, Hq, Hkv, d, window, pos, lse))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(), ids=lambda c: f"case{c[0]}")
+def test_backward_random_shapes(case):
+    # seeded random batches, lengths (1 .. 700, ragged), head groups, head dims, windows,
+    # position offsets and, for the global layer, with or without the forward's lse
+    i, B, T, Hq, Hkv, d, window, pos, lse = case
+    _check(B, T, Hq, Hkv, d, window, 2100 + 10 * i, pos_offset=pos, fwd_lse=lse)
