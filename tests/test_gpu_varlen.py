@@ -106,3 +106,30 @@ def test_global_varlen_long_documents_sampled_rows():
     rows = np.unique(np.concatenate([edges[(edges >= 0) & (edges < T)],
                                      rng.integers(0, T, 256)]))
     _run("global", lens, 8, 2, 128, 570, rows=rows)
+
+
+def _random_packings(n=6, seed=990077):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        n_docs = int(rng.integers(1, 13))
+        lens = [int(x) for x in rng.integers(0, 400, size=n_docs)]
+        if sum(lens) == 0:
+            lens[0] = 1
+        model = i % 2 == 0   # the streaming SWA kernel's shape
+        d = 128 if model else int(rng.choice([64, 128]))
+        Hkv = int(rng.choice([1, 2]))
+        Hq = Hkv * (4 if model else int(rng.choice([1, 2, 4, 8])))
+        window = int(rng.integers(1, 129 if model else 300))
+        pos = int(rng.integers(0, 20_000))
+        cases.append((i, lens, Hq, Hkv, d, window, pos))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_packings(), ids=lambda c: f"case{c[0]}")
+def test_varlen_random_packings(case):
+    # seeded random document counts and lengths (empty documents included), head shapes,
+    # windows and position offsets through both packed layers
+    i, lens, Hq, Hkv, d, window, pos = case
+    _run("swa", lens, Hq, Hkv, d, 600 + 10 * i, window=window, pos_offset=pos)
+    _run("global", lens, Hq, Hkv, d, 600 + 10 * i, pos_offset=pos)
