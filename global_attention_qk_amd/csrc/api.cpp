@@ -153,11 +153,12 @@ int hip_status(hipError_t e) { return e == hipSuccess ? ZGATTN_OK : ZGATTN_EHIP;
 
 int decode_common(const zgattn_desc* d, const void* q, const void* k_new, const void* v_new,
                   const float* wq, const float* wk, void* kc, void* vc, const int32_t* pos,
-                  void* out) {
+                  void* out, bool allow_f32 = true) {
   int st = check_desc(d);
   if (st) return st;
   if (!q || !k_new || !v_new || !wq || !wk || !kc || !vc || !pos || !out) return ZGATTN_ENULL;
-  if (d->dtype != ZGATTN_BF16) return ZGATTN_EUNSUPPORTED;
+  if (d->dtype != ZGATTN_BF16 && !(allow_f32 && d->dtype == ZGATTN_F32))
+    return ZGATTN_EUNSUPPORTED;
   const int G = d->n_q_heads / d->n_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return ZGATTN_EUNSUPPORTED;
   if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(kc) ||
@@ -190,6 +191,7 @@ DecodeArgs make_decode(const zgattn_desc* d, const void* q, const void* k_new,
   a.window = d->window;
   a.nsplit = 0;
   a.chunk = 0;
+  a.f32 = d->dtype == ZGATTN_F32;
   a.eps = d->rms_eps;
   a.scale = scale_of(d);
   a.fr = rope_freq(d->rotary_dim, d->rope_base);
@@ -490,7 +492,8 @@ int zgattn_model_decode(const zgattn_desc* d, int32_t n_layers, const int32_t* i
   int n_glob = 0, n_swa = 0;
   for (int i = 0; i < n_layers; ++i) {
     const zgattn_decode_layer& L = layers[i];
-    st = decode_common(d, L.q, L.k_new, L.v_new, L.wq, L.wk, L.k_cache, L.v_cache, pos, L.out);
+    st = decode_common(d, L.q, L.k_new, L.v_new, L.wq, L.wk, L.k_cache, L.v_cache, pos, L.out,
+                       /*allow_f32=*/false);
     if (st) return st;
     if (is_global[i]) {
       ++n_glob;

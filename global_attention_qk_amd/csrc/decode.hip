@@ -1,4 +1,4 @@
-// Single-token decode for both layer kinds (bf16 caches).
+// Single-token decode for both layer kinds (bf16 caches; fp32 for single-layer calls).
 //
 // "ZGCM-1-7B 完全解説" explainer, section アーキテクチャ: the 27 gated SWA layers keep a
 // fixed 128-token KV cache while the 5 global layers keep the whole sequence, and decode
@@ -17,7 +17,10 @@
 // SWA layers: one workgroup per (sequence, kv head) does the whole step over the ring
 // (MFMA scores with the ring in registers when it holds at most 128 slots, the model's
 // window; a per-slot kernel for larger rings).
+// fp32 tensors and caches take the same kernels instantiated for float, with the scores on
+// the vector ALUs (the per-slot SWA kernel; the global split kernel's fp32 form).
 #include <mutex>
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -92,7 +95,7 @@ __device__ void norm_rope_rows_lds(float* buf, const float* wrow[], int nrows, i
 // ---------------------------------------------------------------------------------------
 // Global decode, step 1: prep.
 // ---------------------------------------------------------------------------------------
-template <int D>
+template <int D, typename T = bf16>
 __device__ __forceinline__ void gdec_prep_kernel_body(const DecodeArgs& p, const LayerIO& io, int kvh, int b) {
   const int G = p.Hq / p.Hkv;
   const int pos = p.pos[b];
@@ -101,8 +104,8 @@ __device__ __forceinline__ void gdec_prep_kernel_body(const DecodeArgs& p, const
   float* buf = (float*)smem;                 // (G + 1) rows
   float* tmp = buf + (G + 1) * D;
   const int t = threadIdx.x;
-  const bf16* q = (const bf16*)io.q + ((size_t)b * p.Hq + kvh * G) * D;
-  const bf16* kn = (const bf16*)io.k_new + ((size_t)b * p.Hkv + kvh) * D;
+  const T* q = (const T*)io.q + ((size_t)b * p.Hq + kvh * G) * D;
+  const T* kn = (const T*)io.k_new + ((size_t)b * p.Hkv + kvh) * D;
   for (int i = t; i < (G + 1) * D; i += kThreads)
     buf[i] = i < G * D ? (float)q[i] : (float)kn[i - G * D];
   const float* wrow[9];
@@ -113,15 +116,15 @@ __device__ __forceinline__ void gdec_prep_kernel_body(const DecodeArgs& p, const
   float* wsq = io.ws + ((size_t)b * p.Hq + kvh * G) * D;
   for (int i = t; i < G * D; i += kThreads) wsq[i] = buf[i] * qs;
   const size_t crow = (((size_t)b * p.Hkv + kvh) * p.S + pos) * D;
-  const bf16* vn = (const bf16*)io.v_new + ((size_t)b * p.Hkv + kvh) * D;
+  const T* vn = (const T*)io.v_new + ((size_t)b * p.Hkv + kvh) * D;
   for (int c = t; c < D; c += kThreads) {
-    ((bf16*)io.k_cache)[crow + c] = (bf16)buf[G * D + c];
-    ((bf16*)io.v_cache)[crow + c] = vn[c];
+    ((T*)io.k_cache)[crow + c] = (T)buf[G * D + c];
+    ((T*)io.v_cache)[crow + c] = vn[c];
   }
 }
-template <int D>
+template <int D, typename T = bf16>
 __global__ __launch_bounds__(kThreads) void gdec_prep_kernel(const DecodeArgs p) {
-  gdec_prep_kernel_body<D>(p, layer_io(p), (int)blockIdx.x, (int)blockIdx.y);
+  gdec_prep_kernel_body<D, T>(p, layer_io(p), (int)blockIdx.x, (int)blockIdx.y);
 }
 template <int D>
 __global__ __launch_bounds__(kThreads) void gdec_prep_kernel_layers(const DecodeBatchArgs pb) {
@@ -132,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void gdec_prep_kernel_layers(const Decode
 // ---------------------------------------------------------------------------------------
 // Global decode, step 2: one split of the cache.
 // ---------------------------------------------------------------------------------------
-template <int D, int G>
+template <int D, int G, typename T = bf16>
 __device__ __forceinline__ void gdec_split_kernel_body(const DecodeArgs& p, const LayerIO& io, int split, int kvh, int b) {
   constexpr int KS = D / 32;            // k-steps of the 16x16x32 product
   constexpr int DC = D / 8;             // 8-wide d chunks
@@ -151,9 +154,36 @@ __device__ __forceinline__ void gdec_split_kernel_body(const DecodeArgs& p, cons
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int l16 = lane & 15, q4 = lane >> 4;
   const size_t cbase = (((size_t)b * p.Hkv + kvh) * p.S + c0) * D;
-  const bf16* kc = (const bf16*)io.k_cache + cbase;
-  const bf16* vc = (const bf16*)io.v_cache + cbase;
+  const T* kc = (const T*)io.k_cache + cbase;
+  const T* vc = (const T*)io.v_cache + cbase;
 
+  if constexpr (std::is_same<T, float>::value) {
+    // fp32 caches: one key per thread at a time, the G dot products on the vector ALUs,
+    // q~ from LDS (every lane reads the same word: a broadcast)
+    __shared__ float sQ[G * D];
+    const float* wsq = io.ws + ((size_t)b * p.Hq + kvh * G) * D;
+    for (int i = t; i < G * D; i += kThreads) sQ[i] = wsq[i];
+    __syncthreads();
+    for (int kl = t; kl < n; kl += kThreads) {
+      float sc[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) sc[h] = 0.f;
+      const float* krow = kc + (size_t)kl * D;
+#pragma unroll 4
+      for (int c = 0; c < D; c += 4) {
+        const float4 kv = *(const float4*)(krow + c);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          sc[h] = __builtin_fmaf(sQ[h * D + c], kv.x, sc[h]);
+          sc[h] = __builtin_fmaf(sQ[h * D + c + 1], kv.y, sc[h]);
+          sc[h] = __builtin_fmaf(sQ[h * D + c + 2], kv.z, sc[h]);
+          sc[h] = __builtin_fmaf(sQ[h * D + c + 3], kv.w, sc[h]);
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) sP[kl * G + h] = sc[h];
+    }
+  } else {
   // q~ as the B operand: column = head l16 (zero beyond G), k = d.
   bf16x8 qb[KS];
   {
@@ -202,6 +232,7 @@ __device__ __forceinline__ void gdec_split_kernel_body(const DecodeArgs& p, cons
       }
     }
   }
+  }
   __syncthreads();
   // Phase B: exact max / sum per head over the chunk, P in place.
   for (int h = wave; h < G; h += 4) {
@@ -230,12 +261,19 @@ __device__ __forceinline__ void gdec_split_kernel_body(const DecodeArgs& p, cons
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
 #pragma unroll 4
   for (int kl = kl0; kl < n; kl += NKL) {
-    const u32x4 raw = *(const u32x4*)(vc + (size_t)kl * D + dc * 8);
     float v[8];
-    v[0] = bf16_lo_to_f32(raw.x); v[1] = bf16_hi_to_f32(raw.x);
-    v[2] = bf16_lo_to_f32(raw.y); v[3] = bf16_hi_to_f32(raw.y);
-    v[4] = bf16_lo_to_f32(raw.z); v[5] = bf16_hi_to_f32(raw.z);
-    v[6] = bf16_lo_to_f32(raw.w); v[7] = bf16_hi_to_f32(raw.w);
+    if constexpr (std::is_same<T, float>::value) {
+      const float4 v0 = *(const float4*)(vc + (size_t)kl * D + dc * 8);
+      const float4 v1 = *(const float4*)(vc + (size_t)kl * D + dc * 8 + 4);
+      v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
+      v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+    } else {
+      const u32x4 raw = *(const u32x4*)(vc + (size_t)kl * D + dc * 8);
+      v[0] = bf16_lo_to_f32(raw.x); v[1] = bf16_hi_to_f32(raw.x);
+      v[2] = bf16_lo_to_f32(raw.y); v[3] = bf16_hi_to_f32(raw.y);
+      v[4] = bf16_lo_to_f32(raw.z); v[5] = bf16_hi_to_f32(raw.z);
+      v[6] = bf16_lo_to_f32(raw.w); v[7] = bf16_hi_to_f32(raw.w);
+    }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float pw = sP[kl * G + h];
@@ -263,9 +301,9 @@ __device__ __forceinline__ void gdec_split_kernel_body(const DecodeArgs& p, cons
     ml[(hq * p.nsplit + split) * 2 + 1] = sL[t];
   }
 }
-template <int D, int G>
+template <int D, int G, typename T = bf16>
 __global__ __launch_bounds__(kThreads) void gdec_split_kernel(const DecodeArgs p) {
-  gdec_split_kernel_body<D, G>(p, layer_io(p), (int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z);
+  gdec_split_kernel_body<D, G, T>(p, layer_io(p), (int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z);
 }
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void gdec_split_kernel_layers(const DecodeBatchArgs pb) {
@@ -276,13 +314,13 @@ __global__ __launch_bounds__(kThreads) void gdec_split_kernel_layers(const Decod
 // ---------------------------------------------------------------------------------------
 // Global decode, step 3: log-sum-exp merge of the splits.
 // ---------------------------------------------------------------------------------------
-template <int D>
+template <int D, typename T = bf16>
 __device__ __forceinline__ void gdec_combine_kernel_body(const DecodeArgs& p, const LayerIO& io, int h, int b) {
   const int d = threadIdx.x;
   const int pos = p.pos[b];
-  bf16* out = (bf16*)io.out + ((size_t)b * p.Hq + h) * D;
+  T* out = (T*)io.out + ((size_t)b * p.Hq + h) * D;
   if (!pos_valid(pos, p.S)) {
-    out[d] = (bf16)__builtin_nanf("");
+    out[d] = (T)__builtin_nanf("");
     return;
   }
   const int ns = min(p.nsplit, pos / p.chunk + 1);
@@ -297,11 +335,11 @@ __device__ __forceinline__ void gdec_combine_kernel_body(const DecodeArgs& p, co
     L = __builtin_fmaf(ml[2 * s + 1], w, L);
     o = __builtin_fmaf(acc[(size_t)s * D + d], w, o);
   }
-  out[d] = (bf16)(o / L);
+  out[d] = (T)(o / L);
 }
-template <int D>
+template <int D, typename T = bf16>
 __global__ __launch_bounds__(D) void gdec_combine_kernel(const DecodeArgs p) {
-  gdec_combine_kernel_body<D>(p, layer_io(p), (int)blockIdx.x, (int)blockIdx.y);
+  gdec_combine_kernel_body<D, T>(p, layer_io(p), (int)blockIdx.x, (int)blockIdx.y);
 }
 template <int D>
 __global__ __launch_bounds__(D) void gdec_combine_kernel_layers(const DecodeBatchArgs pb) {
@@ -312,16 +350,16 @@ __global__ __launch_bounds__(D) void gdec_combine_kernel_layers(const DecodeBatc
 // ---------------------------------------------------------------------------------------
 // SWA decode over the ring: one workgroup per (kv head, sequence).
 // ---------------------------------------------------------------------------------------
-template <int D>
+template <int D, typename T = bf16>
 __global__ __launch_bounds__(kThreads) void swa_decode_kernel(const DecodeArgs p) {
   const int kvh = blockIdx.x, b = blockIdx.y;
   const int G = p.Hq / p.Hkv;
   const int W = p.window;
   const int pos = p.pos[b];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  bf16* out = (bf16*)p.out + ((size_t)b * p.Hq + kvh * G) * D;
+  T* out = (T*)p.out + ((size_t)b * p.Hq + kvh * G) * D;
   if (!pos_valid(pos, ZGATTN_POS_LIMIT)) {
-    for (int i = t; i < G * D; i += kThreads) out[i] = (bf16)__builtin_nanf("");
+    for (int i = t; i < G * D; i += kThreads) out[i] = (T)__builtin_nanf("");
     return;
   }
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -329,9 +367,9 @@ __global__ __launch_bounds__(kThreads) void swa_decode_kernel(const DecodeArgs p
   float* tmp = buf + (G + 1) * D;
   float* sv = tmp + (G + 1) * D;    // v_new
   float* sS = sv + D;               // [G][W]
-  const bf16* q = (const bf16*)p.q + ((size_t)b * p.Hq + kvh * G) * D;
-  const bf16* kn = (const bf16*)p.k_new + ((size_t)b * p.Hkv + kvh) * D;
-  const bf16* vn = (const bf16*)p.v_new + ((size_t)b * p.Hkv + kvh) * D;
+  const T* q = (const T*)p.q + ((size_t)b * p.Hq + kvh * G) * D;
+  const T* kn = (const T*)p.k_new + ((size_t)b * p.Hkv + kvh) * D;
+  const T* vn = (const T*)p.v_new + ((size_t)b * p.Hkv + kvh) * D;
   for (int i = t; i < (G + 1) * D; i += kThreads)
     buf[i] = i < G * D ? (float)q[i] : (float)kn[i - G * D];
   for (int c = t; c < D; c += kThreads) sv[c] = (float)vn[c];
@@ -341,10 +379,10 @@ __global__ __launch_bounds__(kThreads) void swa_decode_kernel(const DecodeArgs p
   norm_rope_rows_lds<D>(buf, wrow, G + 1, pos, p.rdim, p.eps, p.fr, tmp);
   const float qs = p.scale * 1.4426950408889634f;
   const int slot = pos % W;
-  bf16* kr = (bf16*)p.k_cache + ((size_t)b * p.Hkv + kvh) * W * D;
-  bf16* vr = (bf16*)p.v_cache + ((size_t)b * p.Hkv + kvh) * W * D;
-  // the new key as the cache will hold it (bf16); the ring slot itself is written last
-  for (int c = t; c < D; c += kThreads) buf[G * D + c] = (float)(bf16)buf[G * D + c];
+  T* kr = (T*)p.k_cache + ((size_t)b * p.Hkv + kvh) * W * D;
+  T* vr = (T*)p.v_cache + ((size_t)b * p.Hkv + kvh) * W * D;
+  // the new key as the cache will hold it; the ring slot itself is written last
+  for (int c = t; c < D; c += kThreads) buf[G * D + c] = (float)(T)buf[G * D + c];
   __syncthreads();
   // scores
   for (int idx = t; idx < G * W; idx += kThreads) {
@@ -355,6 +393,15 @@ __global__ __launch_bounds__(kThreads) void swa_decode_kernel(const DecodeArgs p
       d = 0.f;
       if (s == slot) {
         for (int c = 0; c < D; ++c) d = __builtin_fmaf(buf[h * D + c], buf[G * D + c], d);
+      } else if constexpr (std::is_same<T, float>::value) {
+        const float* kro = kr + (size_t)s * D;
+        for (int c = 0; c < D; c += 4) {
+          const float4 kv = *(const float4*)(kro + c);
+          d = __builtin_fmaf(buf[h * D + c], kv.x, d);
+          d = __builtin_fmaf(buf[h * D + c + 1], kv.y, d);
+          d = __builtin_fmaf(buf[h * D + c + 2], kv.z, d);
+          d = __builtin_fmaf(buf[h * D + c + 3], kv.w, d);
+        }
       } else {
         const bf16* kro = kr + (size_t)s * D;
         for (int c = 0; c < D; c += 8) {
@@ -387,7 +434,7 @@ __global__ __launch_bounds__(kThreads) void swa_decode_kernel(const DecodeArgs p
     for (int s = lane; s < W; s += 64) sS[h * W + s] *= inv;
   }
   __syncthreads();
-  const bf16* g = (const bf16*)p.g + ((size_t)b * p.Hq + kvh * G) * D;
+  const T* g = (const T*)p.g + ((size_t)b * p.Hq + kvh * G) * D;
   for (int idx = t; idx < G * D; idx += kThreads) {
     const int h = idx / D, c = idx % D;
     const int ns = pos >= W - 1 ? W : pos + 1;
@@ -397,12 +444,12 @@ __global__ __launch_bounds__(kThreads) void swa_decode_kernel(const DecodeArgs p
       o = __builtin_fmaf(sS[h * W + s], vv, o);
     }
     o *= sigmoidf_((float)g[idx]);
-    out[idx] = (bf16)o;
+    out[idx] = (T)o;
   }
   __syncthreads();
   for (int c = t; c < D; c += kThreads) {
-    kr[(size_t)slot * D + c] = (bf16)buf[G * D + c];
-    vr[(size_t)slot * D + c] = (bf16)sv[c];
+    kr[(size_t)slot * D + c] = (T)buf[G * D + c];
+    vr[(size_t)slot * D + c] = (T)sv[c];
   }
 }
 
@@ -740,24 +787,24 @@ hipError_t launch_dyn(K kern, dim3 grid, dim3 block, int smem, hipStream_t s,
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, typename T = bf16>
 hipError_t global_decode_t(const DecodeArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
-  hipError_t e = launch_dyn(gdec_prep_kernel<D>, dim3(a.Hkv, a.B), dim3(kThreads),
+  hipError_t e = launch_dyn(gdec_prep_kernel<D, T>, dim3(a.Hkv, a.B), dim3(kThreads),
                             2 * (G + 1) * D * 4, s, a);
   if (e != hipSuccess) return e;
   constexpr int NKL = kThreads / (D / 8);
   const int smem_split = max(a.chunk * G * 4, NKL * G * D * 4);
   const dim3 g3(a.nsplit, a.Hkv, a.B);
   switch (G) {
-    case 1: e = launch_dyn(gdec_split_kernel<D, 1>, g3, dim3(kThreads), smem_split, s, a); break;
-    case 2: e = launch_dyn(gdec_split_kernel<D, 2>, g3, dim3(kThreads), smem_split, s, a); break;
-    case 4: e = launch_dyn(gdec_split_kernel<D, 4>, g3, dim3(kThreads), smem_split, s, a); break;
-    case 8: e = launch_dyn(gdec_split_kernel<D, 8>, g3, dim3(kThreads), smem_split, s, a); break;
+    case 1: e = launch_dyn(gdec_split_kernel<D, 1, T>, g3, dim3(kThreads), smem_split, s, a); break;
+    case 2: e = launch_dyn(gdec_split_kernel<D, 2, T>, g3, dim3(kThreads), smem_split, s, a); break;
+    case 4: e = launch_dyn(gdec_split_kernel<D, 4, T>, g3, dim3(kThreads), smem_split, s, a); break;
+    case 8: e = launch_dyn(gdec_split_kernel<D, 8, T>, g3, dim3(kThreads), smem_split, s, a); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(gdec_combine_kernel<D>, dim3(a.Hq, a.B), dim3(D), 0, s, a);
+  hipLaunchKernelGGL((gdec_combine_kernel<D, T>), dim3(a.Hq, a.B), dim3(D), 0, s, a);
   return hipGetLastError();
 }
 
@@ -814,6 +861,7 @@ hipError_t decode_noalloc_scratch(void** ptr, size_t* bytes) {
 }
 
 hipError_t launch_global_decode(const DecodeArgs& a, hipStream_t s) {
+  if (a.f32) return a.d == 128 ? global_decode_t<128, float>(a, s) : global_decode_t<64, float>(a, s);
   return a.d == 128 ? global_decode_t<128>(a, s) : global_decode_t<64>(a, s);
 }
 
@@ -900,10 +948,15 @@ hipError_t launch_global_decode_layers(const DecodeArgs& a, const LayerIO* io, i
 }
 
 hipError_t launch_swa_decode(const DecodeArgs& a, hipStream_t s) {
-  if (swa_decode_mfma_ok(a)) return launch_swa_mfma<false>(dim3(a.Hkv, a.B), s, a, a);
-  // rings of more than 128 slots: the per-slot kernel
   const int G = a.Hq / a.Hkv;
   const int smem = (2 * (G + 1) * a.d + a.d + G * a.window) * 4;
+  if (a.f32) {   // fp32: the per-slot kernel for every ring size
+    if (a.d == 128)
+      return launch_dyn(swa_decode_kernel<128, float>, dim3(a.Hkv, a.B), dim3(kThreads), smem, s, a);
+    return launch_dyn(swa_decode_kernel<64, float>, dim3(a.Hkv, a.B), dim3(kThreads), smem, s, a);
+  }
+  if (swa_decode_mfma_ok(a)) return launch_swa_mfma<false>(dim3(a.Hkv, a.B), s, a, a);
+  // rings of more than 128 slots: the per-slot kernel
   if (a.d == 128) return launch_dyn(swa_decode_kernel<128>, dim3(a.Hkv, a.B), dim3(kThreads), smem, s, a);
   return launch_dyn(swa_decode_kernel<64>, dim3(a.Hkv, a.B), dim3(kThreads), smem, s, a);
 }

@@ -122,6 +122,7 @@ struct DecodeArgs {
   int B, Hq, Hkv, d, S, rdim, window, nsplit, chunk;
   float eps, scale;
   RopeFreq fr;
+  int f32;             // tensors and caches fp32 (single-layer calls), else bf16
 };
 hipError_t launch_swa_decode(const DecodeArgs& a, hipStream_t s);
 

@@ -171,7 +171,8 @@ int zgattn_global_prefill_backward(const zgattn_desc* desc, const void* q, const
  * Position p lives in ring slot p % window. The call writes k~_new and v_new into slot
  * pos % window, then attends over positions max(0, pos-window+1) .. pos. A sequence
  * whose pos is negative or above ZGATTN_MAX_POSITION gets NaN outputs and an untouched
- * ring (checked on the device, since pos lives there).
+ * ring (checked on the device, since pos lives there). Tensors and ring are bf16 or fp32
+ * (desc->dtype).
  */
 int zgattn_swa_decode(const zgattn_desc* desc, const void* q, const void* k_new,
                       const void* v_new, const void* g, const float* wq, const float* wk,
@@ -186,7 +187,7 @@ int zgattn_swa_decode(const zgattn_desc* desc, const void* q, const void* k_new,
  * The call writes k~_new, v_new at cache index pos[b], then attends over 0 .. pos[b].
  * `workspace` (device, >= zgattn_global_decode_workspace_bytes(desc, capacity) bytes)
  * holds per-split partial results. A sequence with pos outside [0, capacity) gets NaN
- * outputs and an untouched cache.
+ * outputs and an untouched cache. Tensors and caches are bf16 or fp32 (desc->dtype).
  */
 int zgattn_global_decode(const zgattn_desc* desc, const void* q, const void* k_new,
                          const void* v_new, const float* wq, const float* wk,
@@ -232,6 +233,7 @@ int zgattn_global_decode_noalloc(const zgattn_desc* desc, const void* q, const v
  *   zgattn_model_decode_workspace_bytes(...) bytes) holds the global layers' partials.
  * Shapes and parameters come from desc (one desc for the stack). Errors as for the
  * single-layer calls; any invalid layer fails the whole call before anything launches.
+ * bf16 only (ZGATTN_EUNSUPPORTED for fp32, which the single-layer calls take).
  */
 typedef struct {
   const void* q;

@@ -141,8 +141,13 @@ static void decode_checks() {
   CHECK(stub::launches == 0);
   CHECK(zgattn_global_decode(&d, P(1), P(2), P(3), W(), W(), P(5), P(6), cap, pos, P(8), need, P(7), nullptr) == ZGATTN_OK);
   CHECK(stub::last_decode.S == cap && stub::last_decode.ws == (float*)P(8) && stub::last_decode.nsplit > 0);
+  CHECK(stub::last_decode.f32 == 0);
+  // fp32 tensors and caches: the same calls, flagged for the fp32 kernels
   zgattn_desc f = desc(4, 1, 32, 8, 128, ZGATTN_F32);
-  CHECK(zgattn_global_decode(&f, P(1), P(2), P(3), W(), W(), P(5), P(6), cap, pos, P(8), need, P(7), nullptr) == ZGATTN_EUNSUPPORTED);
+  CHECK(zgattn_global_decode(&f, P(1), P(2), P(3), W(), W(), P(5), P(6), cap, pos, P(8), need, P(7), nullptr) == ZGATTN_OK);
+  CHECK(stub::last_decode.f32 == 1);
+  CHECK(zgattn_swa_decode(&f, P(1), P(2), P(3), P(4), W(), W(), P(5), P(6), pos, P(7), nullptr) == ZGATTN_OK);
+  CHECK(stub::last_decode.f32 == 1 && stub::last_decode.window == 128);
   // the no-allocation variant: scratch looked up only for calls that launch
   stub::reset();
   CHECK(zgattn_global_decode_noalloc(&d, P(1), P(2), P(3), W(), W(), P(5), P(6), cap, pos, P(7), nullptr) == ZGATTN_OK);
@@ -173,6 +178,12 @@ static void decode_checks() {
   CHECK(zgattn_model_decode(&d, n, kinds.data(), L.data(), 4096, pos, P(900), mneed, nullptr) == ZGATTN_ENULL);
   CHECK(stub::launches == 0);
   CHECK(zgattn_model_decode(&d, 2000, kinds.data(), L.data(), 4096, pos, P(900), mneed, nullptr) == ZGATTN_EINVAL);
+  // the batched stack step is bf16 only
+  L[17].out = P(107 + 9 * 17);
+  zgattn_desc f32 = desc(4, 1, 32, 8, 128, ZGATTN_F32);
+  stub::reset();
+  CHECK(zgattn_model_decode(&f32, n, kinds.data(), L.data(), 4096, pos, P(900), mneed, nullptr) == ZGATTN_EUNSUPPORTED);
+  CHECK(stub::launches == 0);
 }
 
 static void norm_rope_checks() {

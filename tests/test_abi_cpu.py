@@ -102,7 +102,9 @@ def test_decode_checks():
     assert call(nb=need - 1) == -5
     assert call(cap=0) == -6
     assert call(pos=None) == -2
-    assert call(d=_d(dtype=L.F32, n_q_heads=32, n_kv_heads=8)) == -4
+    # fp32 passes the dtype check (its workspace check comes after it); nothing launches
+    assert call(d=_d(batch=4, seq_len=1, n_q_heads=32, n_kv_heads=8, dtype=L.F32),
+                nb=need - 1) == -5
     assert call(d=_d(n_q_heads=48, n_kv_heads=3)) == -4   # head group 16
     st = lib.zgattn_swa_decode(ctypes.byref(_d(window=0, n_q_heads=32, n_kv_heads=8)), FAKE,
                                FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
@@ -117,7 +119,7 @@ def test_decode_noalloc_checks():
     ok = _d(batch=4, seq_len=1, n_q_heads=32, n_kv_heads=8)
     assert call(ok, cap=0) == -6
     assert call(ok, pos=None) == -2
-    assert call(_d(dtype=L.F32, n_q_heads=32, n_kv_heads=8)) == -4
+    assert call(_d(dtype=L.F32, n_q_heads=32, n_kv_heads=8), cap=0) == -6   # fp32 accepted
     # partials of B * Hq * d = 2^23 values need 2 * 4 * 2^23 bytes even with one split:
     # more than the 64 MiB scratch
     big = _d(batch=1024, seq_len=1, n_q_heads=64, n_kv_heads=8)

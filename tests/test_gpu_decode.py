@@ -57,13 +57,13 @@ def test_qknorm_rope_position_array():
     assert maxabs(host64(out), want) <= TOL_BF16
 
 
-def _decode_case(B, Hq, Hkv, d, S, seed):
-    q = host_tensor((B, Hq, d), seed, "bf16")
-    g = host_tensor((B, Hq, d), seed + 1, "bf16")
-    kn = host_tensor((B, Hkv, d), seed + 2, "bf16")
-    vn = host_tensor((B, Hkv, d), seed + 3, "bf16")
-    kc = host_tensor((B, Hkv, S, d), seed + 4, "bf16")
-    vc = host_tensor((B, Hkv, S, d), seed + 5, "bf16")
+def _decode_case(B, Hq, Hkv, d, S, seed, dtype="bf16"):
+    q = host_tensor((B, Hq, d), seed, dtype)
+    g = host_tensor((B, Hq, d), seed + 1, dtype)
+    kn = host_tensor((B, Hkv, d), seed + 2, dtype)
+    vn = host_tensor((B, Hkv, d), seed + 3, dtype)
+    kc = host_tensor((B, Hkv, S, d), seed + 4, dtype)
+    vc = host_tensor((B, Hkv, S, d), seed + 5, dtype)
     return q, g, kn, vn, kc, vc, _w(d, seed + 6), _w(d, seed + 7)
 
 
@@ -122,6 +122,66 @@ def test_swa_decode_vs_oracle(W, d, Hq, Hkv):
     kr2, vr2 = host64(krd), host64(vrd)
     for b, p in enumerate(pos):
         assert maxabs(kr2[b, :, p % W], ktn[b]) <= 2e-2
+        assert np.array_equal(vr2[b, :, p % W], host64(vn)[b])
+        others = np.ones(W, bool)
+        others[p % W] = False
+        assert np.array_equal(kr2[b, :, others], host64(kr)[b, :, others])
+
+
+# fp32 tensors and caches (the per-slot SWA kernel and the global split kernel's fp32 form):
+# parity at the fp32 tolerance, the new token's k~ within 1e-5 and its v copied exactly
+@pytest.mark.parametrize("B,Hq,Hkv,d,S,pos", [(3, 8, 2, 128, 5000, [0, 1234, 4999]),
+                                              (2, 4, 4, 64, 300, [17, 299]),
+                                              (1, 16, 2, 128, 70000, [69999]),
+                                              (2, 2, 1, 64, 1, [0, 0])])
+def test_global_decode_fp32(B, Hq, Hkv, d, S, pos):
+    zg = _zg()
+    import torch
+    q, g, kn, vn, kc, vc, wq, wk = _decode_case(B, Hq, Hkv, d, S, 4000 + S, "f32")
+    kcd, vcd = kc.cuda(), vc.cuda()
+    posd = torch.tensor(pos, dtype=torch.int32, device="cuda")
+    out = zg.global_decode(q.cuda(), kn.cuda(), vn.cuda(), wq.cuda(), wk.cuda(), kcd, vcd, posd)
+    torch.cuda.synchronize()
+    assert out.dtype == torch.float32
+    want, ktn = O.decode_global(host64(q), host64(kn), host64(vn), host64(wq), host64(wk),
+                                host64(kc), host64(vc), np.array(pos),
+                                rotary_dim=zg.rotary_dim_for(d))
+    err = maxabs(host64(out), want)
+    say("global_decode fp32", (B, Hq, Hkv, d, S), pos, err)
+    assert err <= TOL_F32
+    kc2, vc2 = host64(kcd), host64(vcd)
+    for b, p in enumerate(pos):
+        assert maxabs(kc2[b, :, p], ktn[b]) <= 1e-5
+        assert np.array_equal(vc2[b, :, p], host64(vn)[b])
+        mask = np.ones(S, bool)
+        mask[p] = False
+        assert np.array_equal(kc2[b, :, mask], host64(kc)[b, :, mask])
+
+
+@pytest.mark.parametrize("W,d,Hq,Hkv", [(128, 128, 8, 2), (50, 64, 4, 1), (300, 128, 2, 2),
+                                        (1, 64, 8, 1)])
+def test_swa_decode_fp32(W, d, Hq, Hkv):
+    zg = _zg()
+    import torch
+    pos = sorted({0, 5, max(W - 2, 0), W - 1, W, 300, 100000})
+    B = len(pos)
+    r = zg.rotary_dim_for(d)
+    q, g, kn, vn, kr, vr, wq, wk = _decode_case(B, Hq, Hkv, d, W, 5000 + W, "f32")
+    krd, vrd = kr.cuda(), vr.cuda()
+    posd = torch.tensor(pos, dtype=torch.int32, device="cuda")
+    out = zg.swa_decode(q.cuda(), kn.cuda(), vn.cuda(), g.cuda(), wq.cuda(), wk.cuda(), krd,
+                        vrd, posd, rotary_dim=r)
+    torch.cuda.synchronize()
+    assert out.dtype == torch.float32
+    want, ktn = O.decode_swa(host64(q), host64(kn), host64(vn), host64(g), host64(wq),
+                             host64(wk), host64(kr), host64(vr), np.array(pos), window=W,
+                             rotary_dim=r)
+    err = maxabs(host64(out), want)
+    say("swa_decode fp32", W, d, Hq, Hkv, pos, err)
+    assert err <= TOL_F32
+    kr2, vr2 = host64(krd), host64(vrd)
+    for b, p in enumerate(pos):
+        assert maxabs(kr2[b, :, p % W], ktn[b]) <= 1e-5
         assert np.array_equal(vr2[b, :, p % W], host64(vn)[b])
         others = np.ones(W, bool)
         others[p % W] = False
