@@ -492,8 +492,7 @@ int zgattn_model_decode(const zgattn_desc* d, int32_t n_layers, const int32_t* i
   int n_glob = 0, n_swa = 0;
   for (int i = 0; i < n_layers; ++i) {
     const zgattn_decode_layer& L = layers[i];
-    st = decode_common(d, L.q, L.k_new, L.v_new, L.wq, L.wk, L.k_cache, L.v_cache, pos, L.out,
-                       /*allow_f32=*/false);
+    st = decode_common(d, L.q, L.k_new, L.v_new, L.wq, L.wk, L.k_cache, L.v_cache, pos, L.out);
     if (st) return st;
     if (is_global[i]) {
       ++n_glob;
@@ -503,8 +502,9 @@ int zgattn_model_decode(const zgattn_desc* d, int32_t n_layers, const int32_t* i
       ++n_swa;
     }
   }
-  if (n_swa && (d->window < 1 || d->window > kSwaDecodeLayersMaxWindow))
-    return ZGATTN_EUNSUPPORTED;
+  const bool f32 = d->dtype == ZGATTN_F32;
+  if (n_swa && d->window < 1) return ZGATTN_EINVAL;
+  if (n_swa && !f32 && d->window > kSwaDecodeLayersMaxWindow) return ZGATTN_EUNSUPPORTED;
   DecodeArgs a = make_decode(d, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                              nullptr, pos, nullptr);
   size_t stride = 0;
@@ -517,8 +517,35 @@ int zgattn_model_decode(const zgattn_desc* d, int32_t n_layers, const int32_t* i
     if (workspace_bytes < n_glob * stride) return ZGATTN_EWORKSPACE;
     a.S = capacity;
   }
-  // launches per kind, kMaxDecodeLayers layers at a time (all SWA layers first)
   const hipStream_t s = (hipStream_t)stream;
+  if (f32) {
+    // fp32: the single-layer kernels, one layer after another
+    int gi = 0;
+    for (int i = 0; i < n_layers; ++i) {
+      const zgattn_decode_layer& L = layers[i];
+      DecodeArgs la = a;
+      la.q = L.q;
+      la.k_new = L.k_new;
+      la.v_new = L.v_new;
+      la.wq = L.wq;
+      la.wk = L.wk;
+      la.k_cache = L.k_cache;
+      la.v_cache = L.v_cache;
+      la.out = L.out;
+      if (is_global[i]) {
+        la.g = nullptr;
+        la.ws = (float*)((char*)workspace + (gi++) * stride);
+        st = hip_status(launch_global_decode(la, s));
+      } else {
+        la.g = L.g;
+        la.ws = nullptr;
+        st = hip_status(launch_swa_decode(la, s));
+      }
+      if (st) return st;
+    }
+    return ZGATTN_OK;
+  }
+  // launches per kind, kMaxDecodeLayers layers at a time (all SWA layers first)
   LayerIO io[kMaxDecodeLayers];
   for (int kind = 0; kind < 2; ++kind) {
     int m = 0, gi = 0;

@@ -233,7 +233,8 @@ int zgattn_global_decode_noalloc(const zgattn_desc* desc, const void* q, const v
  *   zgattn_model_decode_workspace_bytes(...) bytes) holds the global layers' partials.
  * Shapes and parameters come from desc (one desc for the stack). Errors as for the
  * single-layer calls; any invalid layer fails the whole call before anything launches.
- * bf16 only (ZGATTN_EUNSUPPORTED for fp32, which the single-layer calls take).
+ * bf16: SWA rings of at most 128 slots (ZGATTN_EUNSUPPORTED above). fp32 tensors and
+ * caches run the layers one after another through the single-layer kernels.
  */
 typedef struct {
   const void* q;

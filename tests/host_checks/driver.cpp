@@ -178,12 +178,14 @@ static void decode_checks() {
   CHECK(zgattn_model_decode(&d, n, kinds.data(), L.data(), 4096, pos, P(900), mneed, nullptr) == ZGATTN_ENULL);
   CHECK(stub::launches == 0);
   CHECK(zgattn_model_decode(&d, 2000, kinds.data(), L.data(), 4096, pos, P(900), mneed, nullptr) == ZGATTN_EINVAL);
-  // the batched stack step is bf16 only
+  // fp32: one single-layer launch sequence per layer, in layer order
   L[17].out = P(107 + 9 * 17);
   zgattn_desc f32 = desc(4, 1, 32, 8, 128, ZGATTN_F32);
   stub::reset();
-  CHECK(zgattn_model_decode(&f32, n, kinds.data(), L.data(), 4096, pos, P(900), mneed, nullptr) == ZGATTN_EUNSUPPORTED);
-  CHECK(stub::launches == 0);
+  CHECK(zgattn_model_decode(&f32, n, kinds.data(), L.data(), 4096, pos, P(900), mneed, nullptr) == ZGATTN_OK);
+  CHECK(stub::decode_launches == n && stub::batched_layers == 0);
+  CHECK(stub::last_decode.f32 == 1 && stub::last_decode.out == P(107 + 9 * (n - 1)));
+  CHECK(stub::last_decode.ws == (kinds[n - 1] ? (float*)((char*)P(900) + (n_glob - 1) * (mneed / n_glob)) : nullptr));
 }
 
 static void norm_rope_checks() {

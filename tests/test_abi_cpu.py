@@ -166,7 +166,11 @@ def test_model_decode_checks():
     bad = (L.DecodeLayer * 3)(lay(), lay(out=4100), lay())     # misaligned output
     assert call(tab=bad) == -1
     assert call(d=_d(batch=4, seq_len=1, n_q_heads=32, n_kv_heads=8, window=129)) == -4
-    assert call(d=_d(batch=4, seq_len=1, n_q_heads=32, n_kv_heads=8, dtype=L.F32)) == -4
+    # fp32 passes the dtype check (single-layer kernels per layer); its workspace check
+    # still comes first, so nothing launches here
+    f32 = _d(batch=4, seq_len=1, n_q_heads=32, n_kv_heads=8, dtype=L.F32)
+    assert call(d=f32, nb=need - 1) == -5
+    assert call(d=_d(batch=4, seq_len=1, n_q_heads=32, n_kv_heads=8, window=0)) == -1
 
 
 def test_varlen_prefill_checks():
