@@ -347,6 +347,7 @@ int varlen_common(const zgattn_desc* d, const int32_t* cu, int32_t n_docs, int32
   if (d->seq_len == 0 || max_len == 0) return ZGATTN_OK;
   if (!cu || !q || !k || !v || !wq || !wk || !out) return ZGATTN_ENULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ZGATTN_EINVAL;
+  if (d->dtype == ZGATTN_F32) return ZGATTN_OK;   // the fp32 kernel: any head group and rotary dim
   if (d->dtype != ZGATTN_BF16) return ZGATTN_EUNSUPPORTED;
   if (!prefill_bf16_supported(d->head_dim, d->n_q_heads / d->n_kv_heads, d->rotary_dim))
     return ZGATTN_EUNSUPPORTED;
@@ -367,6 +368,7 @@ int zgattn_swa_prefill_varlen(const zgattn_desc* d, const int32_t* cu_seqlens, i
   a.cu = cu_seqlens;
   a.n_docs = n_docs;
   a.max_len = max_seqlen;
+  if (d->dtype == ZGATTN_F32) return hip_status(launch_prefill_f32(a, (hipStream_t)stream));
   return hip_status(launch_prefill_bf16(a, (hipStream_t)stream));
 }
 
@@ -390,6 +392,8 @@ int zgattn_global_prefill_varlen(const zgattn_desc* d, const int32_t* cu_seqlens
   a.n_docs = n_docs;
   a.max_len = max_seqlen;
   hipStream_t s = (hipStream_t)stream;
+  // fp32: the vector-ALU kernel, which takes no workspace (a given one is not used)
+  if (d->dtype == ZGATTN_F32) return hip_status(launch_prefill_f32(a, s));
   if (workspace) {
     if (workspace_bytes < zgattn_global_prefill_varlen_workspace_bytes(d, n_docs) ||
         !aligned16(workspace))

@@ -6,6 +6,8 @@
 // head; each lane owns one query row and keeps q~ and its output accumulator in
 // registers. K tiles are normalised+rotated once per visit in LDS, V tiles staged in LDS,
 // and every lane reads both with broadcast LDS loads. Any head group, rotary_dim <= d.
+// Dense batches, or packed documents (one grid slice per document, grid sized by the
+// longest).
 #include "common.h"
 #include "launch.h"
 
@@ -25,6 +27,8 @@ struct FArgs {
   int T, Hq, Hkv, window, rdim, pos_offset, swa, group;
   float eps, scale;
   RopeFreq fr;
+  const int32_t* cu;   // packed documents (B == 1, T = total tokens), or nullptr
+  int max_len;
 };
 
 // RMSNorm + partial RoPE of one LDS row (length D, fp32), written to `dst` (LDS).
@@ -60,7 +64,17 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(const FArgs p) {
   const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int kvh = h / p.group;
   const int i0 = tile * kT;
-  const int T = p.T;
+  // sequence of this workgroup: tokens [seq0, seq0 + T) of the token order; with packed
+  // documents, document b, whose positions restart at pos_offset
+  int T = p.T;
+  size_t seq0 = (size_t)b * p.T;
+  if (p.cu) {
+    int start, len;
+    doc_range(p.cu, b, p.T, p.max_len, start, len);
+    if (i0 >= len) return;   // the whole workgroup, before any barrier
+    T = len;
+    seq0 = start;
+  }
   const int qi = i0 + t;
   for (int c = t; c < D; c += 64) {
     sW[c] = p.wq[c];
@@ -69,7 +83,7 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(const FArgs p) {
   __syncthreads();
   // q row -> LDS (thread-per-row), transform into sK (scratch), then to registers.
   {
-    const float* src = p.q + (((size_t)b * T + qi) * p.Hq + h) * D;
+    const float* src = p.q + ((seq0 + qi) * p.Hq + h) * D;
     for (int c = 0; c < D; c += 4) {
       float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
       if (qi < T) x = *(const float4*)(src + c);
@@ -97,7 +111,7 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(const FArgs p) {
     const int k0 = kt * kT;
     const int kj = k0 + t;
     {
-      const size_t off = (((size_t)b * T + kj) * p.Hkv + kvh) * D;
+      const size_t off = ((seq0 + kj) * p.Hkv + kvh) * D;
       for (int c = 0; c < D; c += 4) {
         float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
         float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -144,7 +158,7 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(const FArgs p) {
     __syncthreads();
   }
   if (qi < T) {
-    const size_t off = (((size_t)b * T + qi) * p.Hq + h) * D;
+    const size_t off = ((seq0 + qi) * p.Hq + h) * D;
     const float inv = 1.0f / l;
 #pragma unroll
     for (int c = 0; c < D; ++c) {
@@ -177,7 +191,10 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s) {
   f.eps = a.eps;
   f.scale = a.scale;
   f.fr = a.fr;
-  const dim3 grid((a.T + kT - 1) / kT, a.Hq, a.B);
+  f.cu = a.cu;
+  f.max_len = a.max_len;
+  const dim3 grid = a.cu ? dim3((a.max_len + kT - 1) / kT, a.Hq, a.n_docs)
+                         : dim3((a.T + kT - 1) / kT, a.Hq, a.B);
   if (grid.x == 0) return hipSuccess;
   if (a.d == 128)
     hipLaunchKernelGGL(prefill_f32_kernel<128>, grid, dim3(64), 0, s, f);

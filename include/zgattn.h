@@ -122,9 +122,10 @@ size_t zgattn_global_prefill_workspace_bytes(const zgattn_desc* desc);
  * document's first token (RoPE). max_seqlen (host) bounds every document's length and sizes
  * the grid. The table lives on the device and is not validated on the host: out-of-range
  * entries are clamped (no access leaves the tensors) and give unspecified outputs.
- * bf16 only, on the MFMA paths (ZGATTN_EUNSUPPORTED otherwise). The global form takes the
- * same optional workspace as zgattn_global_prefill, sized by
- * zgattn_global_prefill_varlen_workspace_bytes(desc, n_docs).
+ * bf16 on the MFMA paths (their head-group and rotary limits; ZGATTN_EUNSUPPORTED
+ * otherwise), or fp32 on the vector-ALU kernel (any head group and rotary dim). The bf16
+ * global form takes the same optional workspace as zgattn_global_prefill, sized by
+ * zgattn_global_prefill_varlen_workspace_bytes(desc, n_docs) (0 for fp32, which uses none).
  */
 int zgattn_swa_prefill_varlen(const zgattn_desc* desc, const int32_t* cu_seqlens,
                               int32_t n_docs, int32_t max_seqlen, const void* q,

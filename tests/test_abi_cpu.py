@@ -184,7 +184,9 @@ def test_varlen_prefill_checks():
     assert call(mx=1001) == -1
     assert call(cu=None) == -2
     assert call(g=None) == -2
-    assert call(d=_d(batch=1, seq_len=1000, n_q_heads=8, n_kv_heads=2, dtype=L.F32)) == -4
+    # fp32 passes the dtype check (the vector-ALU kernel); the gate check still comes first
+    assert call(d=_d(batch=1, seq_len=1000, n_q_heads=8, n_kv_heads=2, dtype=L.F32),
+                g=None) == -2
     assert call(mx=0, cu=None, g=None) == 0                     # every document empty
     ws = lib.zgattn_global_prefill_varlen_workspace_bytes(ctypes.byref(d), 3)
     kbytes = (2 * 1000 + 64) * 128 * 2

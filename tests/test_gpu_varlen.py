@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 from oracle import attn as O
-from tests.gpu_util import TOL_BF16, host64, maxabs, need_gpu, say, threads
+from tests.gpu_util import TOL_BF16, TOL_F32, host64, maxabs, need_gpu, say, threads
 from workloads import host_tensor, norm_weight
 
 pytestmark = pytest.mark.gpu
@@ -21,13 +21,13 @@ def _zg():
     return zg
 
 
-def _packed(lens, Hq, Hkv, d, seed):
+def _packed(lens, Hq, Hkv, d, seed, dtype="bf16"):
     import torch
     T = int(sum(lens))
-    q = host_tensor((T, Hq, d), seed, "bf16")
-    k = host_tensor((T, Hkv, d), seed + 1, "bf16")
-    v = host_tensor((T, Hkv, d), seed + 2, "bf16")
-    g = host_tensor((T, Hq, d), seed + 3, "bf16", 2 ** 0.5)
+    q = host_tensor((T, Hq, d), seed, dtype)
+    k = host_tensor((T, Hkv, d), seed + 1, dtype)
+    v = host_tensor((T, Hkv, d), seed + 2, dtype)
+    g = host_tensor((T, Hq, d), seed + 3, dtype, 2 ** 0.5)
     wq = torch.from_numpy(norm_weight(d, seed + 4))
     wk = torch.from_numpy(norm_weight(d, seed + 5))
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
@@ -35,11 +35,11 @@ def _packed(lens, Hq, Hkv, d, seed):
 
 
 def _run(kind, lens, Hq, Hkv, d, seed, *, window=128, workspace="auto", rope_base=10000.0,
-         pos_offset=0, rows=None):
+         pos_offset=0, rows=None, dtype="bf16", rdim=None):
     zg = _zg()
     import torch
-    q, k, v, g, wq, wk, cu = _packed(lens, Hq, Hkv, d, seed)
-    r = zg.rotary_dim_for(d)
+    q, k, v, g, wq, wk, cu = _packed(lens, Hq, Hkv, d, seed, dtype)
+    r = zg.rotary_dim_for(d) if rdim is None else rdim
     dv = [t.cuda() for t in (q, k, v, g, wq, wk)]
     cud = torch.from_numpy(cu).cuda()
     mx = int(max(lens))
@@ -58,8 +58,8 @@ def _run(kind, lens, Hq, Hkv, d, seed, *, window=128, workspace="auto", rope_bas
                             rope_base=rope_base, pos_offset=pos_offset, threads=threads())
     got = host64(out) if rows is None else host64(out)[rows]
     err = maxabs(got, want)
-    say("varlen", kind, d, Hq, Hkv, lens[:8], f"W={window} base={rope_base} err={err:.3e}")
-    assert err <= TOL_BF16, err
+    say("varlen", kind, dtype, d, Hq, Hkv, lens[:8], f"W={window} base={rope_base} err={err:.3e}")
+    assert err <= (TOL_F32 if dtype == "f32" else TOL_BF16), err
 
 
 LENS = [1, 63, 64, 65, 300, 7, 129, 200, 128]
@@ -133,3 +133,12 @@ def test_varlen_random_packings(case):
     i, lens, Hq, Hkv, d, window, pos = case
     _run("swa", lens, Hq, Hkv, d, 600 + 10 * i, window=window, pos_offset=pos)
     _run("global", lens, Hq, Hkv, d, 600 + 10 * i, pos_offset=pos)
+
+
+@pytest.mark.parametrize("kind", ["swa", "global"])
+def test_varlen_fp32(kind):
+    # fp32 packed documents on the vector-ALU kernel: empty and one-token documents, tile
+    # boundaries, three query heads per KV head and a rotary dim the MFMA paths do not take
+    lens = [0, 1, 63, 64, 65, 130, 0, 200]
+    _run(kind, lens, 6, 2, 128, 580, window=50, dtype="f32", pos_offset=123, rdim=80)
+    _run(kind, [70, 1, 190], 4, 1, 64, 590, window=128, dtype="f32")
