@@ -229,8 +229,8 @@ int zgattn_swa_prefill(const zgattn_desc* d, const void* q, const void* k, const
   if (!aligned16(g)) return ZGATTN_EINVAL;
   PrefillArgs a = make_prefill(d, q, k, v, g, wq, wk, out, 1);
   hipStream_t s = (hipStream_t)stream;
-  if (d->dtype == ZGATTN_F32) return hip_status(launch_prefill_f32(a, s));
-  if (!prefill_bf16_supported(a.d, a.Hq / a.Hkv, a.rdim)) return ZGATTN_EUNSUPPORTED;
+  if (d->dtype == ZGATTN_F32 || !prefill_bf16_supported(a.d, a.Hq / a.Hkv, a.rdim))
+    return hip_status(launch_prefill_valu(a, d->dtype == ZGATTN_F32, s));
   return hip_status(launch_prefill_bf16(a, s));
 }
 
@@ -248,13 +248,17 @@ int zgattn_global_prefill(const zgattn_desc* d, const void* q, const void* k, co
   int st = prefill_common(d, q, k, v, wq, wk, out);
   if (st) return st;
   if (lse && ((uintptr_t)lse & 3)) return ZGATTN_EINVAL;
-  if (lse && d->dtype != ZGATTN_BF16) return ZGATTN_EUNSUPPORTED;
+  // fp32, or a bf16 shape the MFMA kernels do not take: the vector-ALU kernel (no
+  // workspace used, no log-sum-exp output)
+  const bool valu = d->dtype == ZGATTN_F32 ||
+                    !prefill_bf16_supported(d->head_dim, d->n_q_heads / d->n_kv_heads,
+                                            d->rotary_dim);
+  if (lse && valu) return ZGATTN_EUNSUPPORTED;
   if (d->seq_len == 0) return ZGATTN_OK;
   PrefillArgs a = make_prefill(d, q, k, v, nullptr, wq, wk, out, 0);
   a.lse = lse;
   hipStream_t s = (hipStream_t)stream;
-  if (d->dtype == ZGATTN_F32) return hip_status(launch_prefill_f32(a, s));
-  if (!prefill_bf16_supported(a.d, a.Hq / a.Hkv, a.rdim)) return ZGATTN_EUNSUPPORTED;
+  if (valu) return hip_status(launch_prefill_valu(a, d->dtype == ZGATTN_F32, s));
   if (workspace) {
     if (workspace_bytes < zgattn_global_prefill_workspace_bytes(d) || !aligned16(workspace))
       return ZGATTN_EWORKSPACE;
@@ -347,11 +351,13 @@ int varlen_common(const zgattn_desc* d, const int32_t* cu, int32_t n_docs, int32
   if (d->seq_len == 0 || max_len == 0) return ZGATTN_OK;
   if (!cu || !q || !k || !v || !wq || !wk || !out) return ZGATTN_ENULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ZGATTN_EINVAL;
-  if (d->dtype == ZGATTN_F32) return ZGATTN_OK;   // the fp32 kernel: any head group and rotary dim
-  if (d->dtype != ZGATTN_BF16) return ZGATTN_EUNSUPPORTED;
-  if (!prefill_bf16_supported(d->head_dim, d->n_q_heads / d->n_kv_heads, d->rotary_dim))
-    return ZGATTN_EUNSUPPORTED;
   return ZGATTN_OK;
+}
+
+// fp32 tensors, or bf16 shapes the MFMA kernels do not take: the vector-ALU kernel.
+bool prefill_takes_valu(const zgattn_desc* d) {
+  return d->dtype == ZGATTN_F32 ||
+         !prefill_bf16_supported(d->head_dim, d->n_q_heads / d->n_kv_heads, d->rotary_dim);
 }
 
 int zgattn_swa_prefill_varlen(const zgattn_desc* d, const int32_t* cu_seqlens, int32_t n_docs,
@@ -368,7 +374,8 @@ int zgattn_swa_prefill_varlen(const zgattn_desc* d, const int32_t* cu_seqlens, i
   a.cu = cu_seqlens;
   a.n_docs = n_docs;
   a.max_len = max_seqlen;
-  if (d->dtype == ZGATTN_F32) return hip_status(launch_prefill_f32(a, (hipStream_t)stream));
+  if (prefill_takes_valu(d))
+    return hip_status(launch_prefill_valu(a, d->dtype == ZGATTN_F32, (hipStream_t)stream));
   return hip_status(launch_prefill_bf16(a, (hipStream_t)stream));
 }
 
@@ -392,8 +399,8 @@ int zgattn_global_prefill_varlen(const zgattn_desc* d, const int32_t* cu_seqlens
   a.n_docs = n_docs;
   a.max_len = max_seqlen;
   hipStream_t s = (hipStream_t)stream;
-  // fp32: the vector-ALU kernel, which takes no workspace (a given one is not used)
-  if (d->dtype == ZGATTN_F32) return hip_status(launch_prefill_f32(a, s));
+  // the vector-ALU kernel takes no workspace (a given one is not used)
+  if (prefill_takes_valu(d)) return hip_status(launch_prefill_valu(a, d->dtype == ZGATTN_F32, s));
   if (workspace) {
     if (workspace_bytes < zgattn_global_prefill_varlen_workspace_bytes(d, n_docs) ||
         !aligned16(workspace))

@@ -54,7 +54,9 @@ inline int varlen_vtile_slots(int T, int n_docs) { return T / 64 + n_docs; }
 size_t prefill_vtiles_bytes_varlen(int Hkv, int T, int n_docs, int d);
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
-hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
+// The vector-ALU prefill (fp32 arithmetic): fp32 tensors (f32), or bf16 tensors of shapes
+// the MFMA kernels do not take (prefill_bf16_supported false). Dense or packed documents.
+hipError_t launch_prefill_valu(const PrefillArgs& a, bool f32, hipStream_t s);
 bool prefill_bf16_supported(int d, int group, int rdim);
 // Tile-transposed V for the global path: [B][Hkv][ceil(T/64)][d][64] bf16.
 size_t prefill_vtiles_bytes(int B, int Hkv, int T, int d);

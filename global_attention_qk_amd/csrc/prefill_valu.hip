@@ -1,13 +1,17 @@
-// fp32 prefill attention (both layer kinds) on the vector ALUs.
+// Prefill attention (both layer kinds) on the vector ALUs, fp32 arithmetic throughout.
 //
 // Same definition as the bf16 MFMA path (hyper.ai summary of arXiv 2609.13356, section
-// 方法; "ZGCM-1-7B 完全解説" explainer, section アーキテクチャ) kept in fp32 end to end,
-// for fp32 tensors. One wave64 workgroup owns 64 consecutive positions of one query
+// 方法; "ZGCM-1-7B 完全解説" explainer, section アーキテクチャ) kept in fp32 end to end:
+// the kernel for fp32 tensors, and for bf16 tensors whose shape the MFMA kernels do not
+// take (other head groups, rotary dims above 64). One wave64 workgroup owns 64 consecutive
+// positions of one query
 // head; each lane owns one query row and keeps q~ and its output accumulator in
 // registers. K tiles are normalised+rotated once per visit in LDS, V tiles staged in LDS,
 // and every lane reads both with broadcast LDS loads. Any head group, rotary_dim <= d.
 // Dense batches, or packed documents (one grid slice per document, grid sized by the
 // longest).
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -17,11 +21,11 @@ namespace {
 constexpr int kT = 64;  // positions per workgroup and keys per tile
 
 struct FArgs {
-  const float* q;
-  const float* k;
-  const float* v;
-  const float* g;
-  float* out;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* g;
+  void* out;
   const float* wq;
   const float* wk;
   int T, Hq, Hkv, window, rdim, pos_offset, swa, group;
@@ -51,8 +55,26 @@ __device__ void norm_rope_row_f32(const float* raw, float* dst, const float* w, 
   for (int c = rdim; c < D; ++c) dst[c] = raw[c] * rn * w[c];
 }
 
-template <int D>
-__global__ __launch_bounds__(64) void prefill_f32_kernel(const FArgs p) {
+// Four consecutive elements of a row as fp32 (rows start 16-byte aligned).
+template <typename T>
+__device__ __forceinline__ float4 load4(const T* x) {
+  if constexpr (std::is_same<T, float>::value) {
+    return *(const float4*)x;
+  } else {
+    const u32x2 w = *(const u32x2*)x;
+    return make_float4(bf16_lo_to_f32(w.x), bf16_hi_to_f32(w.x), bf16_lo_to_f32(w.y),
+                       bf16_hi_to_f32(w.y));
+  }
+}
+
+// E: element type of the tensors (float or bf16)
+template <int D, typename E>
+__global__ __launch_bounds__(64) void prefill_valu_kernel(const FArgs p) {
+  const E* pq = (const E*)p.q;
+  const E* pk = (const E*)p.k;
+  const E* pv = (const E*)p.v;
+  const E* pg = (const E*)p.g;
+  E* pout = (E*)p.out;
   constexpr int RS = D + 1;  // padded LDS row
   __shared__ float sRaw[kT * RS];
   __shared__ float sK[kT * RS];
@@ -83,10 +105,10 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(const FArgs p) {
   __syncthreads();
   // q row -> LDS (thread-per-row), transform into sK (scratch), then to registers.
   {
-    const float* src = p.q + ((seq0 + qi) * p.Hq + h) * D;
+    const E* src = pq + ((seq0 + qi) * p.Hq + h) * D;
     for (int c = 0; c < D; c += 4) {
       float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (qi < T) x = *(const float4*)(src + c);
+      if (qi < T) x = load4(src + c);
       sRaw[t * RS + c] = x.x;
       sRaw[t * RS + c + 1] = x.y;
       sRaw[t * RS + c + 2] = x.z;
@@ -116,8 +138,8 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(const FArgs p) {
         float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
         float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
         if (kj < T) {
-          x = *(const float4*)(p.k + off + c);
-          y = *(const float4*)(p.v + off + c);
+          x = load4(pk + off + c);
+          y = load4(pv + off + c);
         }
         sRaw[t * RS + c] = x.x; sRaw[t * RS + c + 1] = x.y;
         sRaw[t * RS + c + 2] = x.z; sRaw[t * RS + c + 3] = x.w;
@@ -163,21 +185,21 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(const FArgs p) {
 #pragma unroll
     for (int c = 0; c < D; ++c) {
       float o = acc[c] * inv;
-      if (p.swa) o *= 1.0f / (1.0f + expf(-p.g[off + c]));
-      p.out[off + c] = o;
+      if (p.swa) o *= 1.0f / (1.0f + expf(-(float)pg[off + c]));
+      pout[off + c] = (E)o;
     }
   }
 }
 
 }  // namespace
 
-hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s) {
+hipError_t launch_prefill_valu(const PrefillArgs& a, bool f32, hipStream_t s) {
   FArgs f;
-  f.q = (const float*)a.q;
-  f.k = (const float*)a.k;
-  f.v = (const float*)a.v;
-  f.g = (const float*)a.g;
-  f.out = (float*)a.out;
+  f.q = a.q;
+  f.k = a.k;
+  f.v = a.v;
+  f.g = a.g;
+  f.out = a.out;
   f.wq = a.wq;
   f.wk = a.wk;
   f.T = a.T;
@@ -196,10 +218,13 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s) {
   const dim3 grid = a.cu ? dim3((a.max_len + kT - 1) / kT, a.Hq, a.n_docs)
                          : dim3((a.T + kT - 1) / kT, a.Hq, a.B);
   if (grid.x == 0) return hipSuccess;
-  if (a.d == 128)
-    hipLaunchKernelGGL(prefill_f32_kernel<128>, grid, dim3(64), 0, s, f);
-  else
-    hipLaunchKernelGGL(prefill_f32_kernel<64>, grid, dim3(64), 0, s, f);
+  if (f32) {
+    if (a.d == 128) hipLaunchKernelGGL((prefill_valu_kernel<128, float>), grid, dim3(64), 0, s, f);
+    else hipLaunchKernelGGL((prefill_valu_kernel<64, float>), grid, dim3(64), 0, s, f);
+  } else {
+    if (a.d == 128) hipLaunchKernelGGL((prefill_valu_kernel<128, bf16>), grid, dim3(64), 0, s, f);
+    else hipLaunchKernelGGL((prefill_valu_kernel<64, bf16>), grid, dim3(64), 0, s, f);
+  }
   return hipGetLastError();
 }
 

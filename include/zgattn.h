@@ -85,6 +85,8 @@ const char* zgattn_strerror(int status);
  *   q, g, out: [B, T, Hq, d];  k, v: [B, T, Hkv, d];  wq, wk: fp32 [d].
  *   out = softmax over the window of (q~ . k~) applied to v, times sigmoid(g).
  * QK-RMSNorm and partial RoPE are applied on the fly as Q and K tiles are loaded.
+ * bf16 on the MFMA kernels for head groups 1, 2, 4, 8 and rotary_dim <= 64, any other
+ * bf16 shape and fp32 on a vector-ALU kernel (fp32 arithmetic).
  * T == 0 is a no-op. out must not alias any input.
  */
 int zgattn_swa_prefill(const zgattn_desc* desc, const void* q, const void* k, const void* v,
@@ -102,7 +104,8 @@ int zgattn_swa_prefill(const zgattn_desc* desc, const void* q, const void* k, co
  * `lse` (optional, device fp32 [B, Hq, T], 4-byte aligned; NULL to skip) receives each
  * row's log-sum-exp of its scaled scores, ln sum_j exp(softmax_scale * q~_i . k~_j) over
  * the visible keys, for zgattn_global_prefill_backward; bf16 only (ZGATTN_EUNSUPPORTED
- * for fp32 when lse is not NULL).
+ * for fp32 and for the bf16 shapes that run on the vector-ALU kernel, as for
+ * zgattn_swa_prefill, when lse is not NULL).
  */
 int zgattn_global_prefill(const zgattn_desc* desc, const void* q, const void* k,
                           const void* v, const float* wq, const float* wk, void* workspace,

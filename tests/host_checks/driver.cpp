@@ -97,11 +97,23 @@ static void prefill_checks() {
   zgattn_desc f32d = desc(1, 64, 4, 1, 64, ZGATTN_F32);
   CHECK(zgattn_global_prefill(&f32d, P(1), P(2), P(3), W(), W(), nullptr, 0, P(5), (float*)P(14), nullptr) == ZGATTN_EUNSUPPORTED);
   CHECK(stub::launches == 0);
-  // fp32 takes its own path; group 16 is unsupported on the bf16 path
+  // fp32, and bf16 shapes the MFMA kernels do not take (head group 16), go to the
+  // vector-ALU kernel; the latter cannot give the log-sum-exp
   zgattn_desc f = desc(1, 64, 4, 1, 64, ZGATTN_F32);
+  stub::reset();
   CHECK(zgattn_swa_prefill(&f, P(1), P(2), P(3), P(4), W(), W(), P(5), nullptr) == ZGATTN_OK);
+  CHECK(stub::valu_launches == 1 && stub::last_valu_f32);
   zgattn_desc g16 = desc(1, 64, 32, 2, 128);
-  CHECK(zgattn_swa_prefill(&g16, P(1), P(2), P(3), P(4), W(), W(), P(5), nullptr) == ZGATTN_EUNSUPPORTED);
+  stub::reset();
+  CHECK(zgattn_swa_prefill(&g16, P(1), P(2), P(3), P(4), W(), W(), P(5), nullptr) == ZGATTN_OK);
+  CHECK(stub::valu_launches == 1 && !stub::last_valu_f32);
+  CHECK(zgattn_global_prefill(&g16, P(1), P(2), P(3), W(), W(), P(6), 1 << 30, P(5), nullptr, nullptr) == ZGATTN_OK);
+  CHECK(stub::valu_launches == 2 && stub::aux_launches == 0);   // no pre-pass
+  CHECK(zgattn_global_prefill(&g16, P(1), P(2), P(3), W(), W(), nullptr, 0, P(5), (float*)P(14), nullptr) == ZGATTN_EUNSUPPORTED);
+  zgattn_desc model = desc(1, 64, 4, 1, 128);
+  stub::reset();
+  CHECK(zgattn_swa_prefill(&model, P(1), P(2), P(3), P(4), W(), W(), P(5), nullptr) == ZGATTN_OK);
+  CHECK(stub::valu_launches == 0 && stub::prefill_launches == 1);
   // varlen
   zgattn_desc v = desc(1, 1000, 8, 2, 128);
   stub::reset();

@@ -5,6 +5,8 @@
 #include "stubs.h"
 
 namespace stub {
+int valu_launches;
+bool last_valu_f32;
 int launches, prefill_launches, aux_launches, decode_launches, batched_layers,
     scratch_lookups;
 int smem_attr_calls;
@@ -15,6 +17,7 @@ alignas(256) static unsigned char scratch_buf[256];
 void* const scratch = scratch_buf;
 void reset() {
   launches = prefill_launches = aux_launches = decode_launches = batched_layers = 0;
+  valu_launches = 0;
   scratch_lookups = 0;
 }
 }  // namespace stub
@@ -42,7 +45,11 @@ static hipError_t rec_prefill(const PrefillArgs& a) {
   return hipSuccess;
 }
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t) { return rec_prefill(a); }
-hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t) { return rec_prefill(a); }
+hipError_t launch_prefill_valu(const PrefillArgs& a, bool f32, hipStream_t) {
+  ++stub::valu_launches;
+  stub::last_valu_f32 = f32;
+  return rec_prefill(a);
+}
 bool prefill_bf16_supported(int d, int group, int rdim) {
   return (d == 64 || d == 128) && group >= 1 && 256 % group == 0 && (256 / group) % 32 == 0 &&
          rdim <= 64;

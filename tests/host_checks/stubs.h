@@ -4,7 +4,9 @@
 
 namespace stub {
 extern int launches;              // kernel launches requested (any launcher)
-extern int prefill_launches;      // launch_prefill_bf16 / launch_prefill_f32
+extern int prefill_launches;      // launch_prefill_bf16 / launch_prefill_valu
+extern int valu_launches;         // launch_prefill_valu alone
+extern bool last_valu_f32;
 extern int aux_launches;          // qknorm_rope / the global pre-pass
 extern int decode_launches;       // single-layer and batched decode launchers
 extern int batched_layers;        // layers passed to the batched decode launchers

@@ -70,10 +70,15 @@ def test_nulls_and_alignment():
     assert _swa(_d(seq_len=0), q=None, g=None, out=None) == 0
 
 
-def test_bf16_mfma_path_limits():
-    # rotary_dim above 64 and head groups the 256-row tile cannot split are refused
-    assert _swa(_d(rotary_dim=80)) == -4
-    assert _swa(_d(n_q_heads=3, n_kv_heads=1)) == -4
+def test_bf16_other_shapes_refuse_only_the_lse():
+    # rotary_dim above 64 and head groups the 256-row tile cannot split run on the
+    # vector-ALU kernel, which gives no log-sum-exp: asking for it is refused before launch
+    lib = L.lib()
+    for kw in (dict(rotary_dim=80), dict(n_q_heads=3, n_kv_heads=1)):
+        d = _d(**kw)
+        st = lib.zgattn_global_prefill(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, 0,
+                                       FAKE, FAKE, None)
+        assert st == -4
 
 
 def test_global_prefill_workspace():

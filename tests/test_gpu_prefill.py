@@ -218,3 +218,11 @@ def test_bf16_running_max_variant_loops_over_tiles():
     rows = np.unique(np.concatenate([np.arange(0, 8192, 131), [63, 64, 8191]]))
     _check("global", q, k, v, None, wq, wk, tol=TOL_BF16, rows=rows)
     _check("global", q, k, v, None, wq, wk, tol=TOL_BF16, rows=rows, workspace=None)
+
+
+@pytest.mark.parametrize("kind", ["swa", "global"])
+@pytest.mark.parametrize("Hq,Hkv,rdim", [(6, 2, 42), (4, 1, 128), (8, 8, 80)])
+def test_bf16_shapes_off_the_mfma_paths(kind, Hq, Hkv, rdim):
+    # head group 3, full rotary and rotary 80: bf16 tensors on the vector-ALU kernel
+    q, k, v, g, wq, wk = _inputs(2, 230, Hq, Hkv, 128, "bf16", 3100 + Hq + rdim)
+    _check(kind, q, k, v, g, wq, wk, window=70, rdim=rdim, pos_offset=9, tol=TOL_BF16)

@@ -142,3 +142,9 @@ def test_varlen_fp32(kind):
     lens = [0, 1, 63, 64, 65, 130, 0, 200]
     _run(kind, lens, 6, 2, 128, 580, window=50, dtype="f32", pos_offset=123, rdim=80)
     _run(kind, [70, 1, 190], 4, 1, 64, 590, window=128, dtype="f32")
+
+
+@pytest.mark.parametrize("kind", ["swa", "global"])
+def test_varlen_bf16_shape_off_the_mfma_paths(kind):
+    # three query heads per KV head and rotary 80 (bf16): the vector-ALU kernel per document
+    _run(kind, [0, 90, 1, 150], 6, 2, 128, 595, window=40, rdim=80)
