@@ -414,7 +414,7 @@ int zgattn_global_prefill_varlen(const zgattn_desc* d, const int32_t* cu_seqlens
 }
 
 size_t zgattn_prefill_backward_workspace_bytes(const zgattn_desc* d) {
-  if (check_desc(d) || d->seq_len < 0 || d->dtype != ZGATTN_BF16) return 0;
+  if (check_desc(d) || d->seq_len < 0) return 0;
   return backward_workspace_bytes(d->batch, d->seq_len, d->n_q_heads, d->n_kv_heads,
                                   d->head_dim);
 }
@@ -433,9 +433,6 @@ int backward_common(const zgattn_desc* d, int swa, const void* q, const void* k,
   if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
       (swa && (!aligned16(g) || !aligned16(dg))))
     return ZGATTN_EINVAL;
-  if (d->dtype != ZGATTN_BF16) return ZGATTN_EUNSUPPORTED;
-  const int G = d->n_q_heads / d->n_kv_heads;
-  if (G != 1 && G != 2 && G != 4 && G != 8) return ZGATTN_EUNSUPPORTED;
   if (!workspace || !aligned16(workspace) ||
       workspace_bytes < zgattn_prefill_backward_workspace_bytes(d))
     return ZGATTN_EWORKSPACE;
@@ -468,6 +465,7 @@ int backward_common(const zgattn_desc* d, int swa, const void* q, const void* k,
   a.eps = d->rms_eps;
   a.scale = scale_of(d);
   a.fr = rope_freq(d->rotary_dim, d->rope_base);
+  a.f32 = d->dtype == ZGATTN_F32;
   return hip_status(launch_prefill_backward(a, (hipStream_t)stream));
 }
 

@@ -718,10 +718,10 @@ __global__ __launch_bounds__(kTKV, 1) void bwd_dkdv_kernel(const BArgs p) {
 // pair partners are exchanged through LDS. Each workgroup leaves one partial of the
 // weight gradient (sum over its rows of u * x^, u = R^T dx~).
 struct NArgs {
-  const bf16* x;       // raw q or k [B][T][H][D]
+  const void* x;       // raw q or k [B][T][H][D] (element type E of the kernel)
   const float* w;
   const float* dxt;    // dx~ [B][T][H][D] fp32
-  bf16* dx;            // [B][T][H][D]
+  void* dx;            // [B][T][H][D] (E)
   float* part;         // [gridDim.x][D]
   int B, T, H, rdim, pos_offset;
   float eps;
@@ -729,7 +729,7 @@ struct NArgs {
 };
 constexpr int kNormBlocks = 1024;
 
-template <int D>
+template <int D, typename E = bf16>
 __global__ __launch_bounds__(kT) void bwd_norm_rope_kernel(const NArgs p) {
   constexpr int LPR = D / 8;                 // lanes per row
   constexpr int RPP = kT / LPR;              // rows per pass
@@ -751,12 +751,19 @@ __global__ __launch_bounds__(kT) void bwd_norm_rope_kernel(const NArgs p) {
     const int64_t rc = ok ? row : n_rows - 1;
     float x[8], g[8];
     {
-      const u32x4 xw = *(const u32x4*)(p.x + rc * D + sub * 8);
-      const uint32_t x4[4] = {xw.x, xw.y, xw.z, xw.w};
+      if constexpr (std::is_same<E, float>::value) {
+        const float4 x0 = *(const float4*)((const float*)p.x + rc * D + sub * 8);
+        const float4 x1 = *(const float4*)((const float*)p.x + rc * D + sub * 8 + 4);
+        x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
+        x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+      } else {
+        const u32x4 xw = *(const u32x4*)((const bf16*)p.x + rc * D + sub * 8);
+        const uint32_t x4[4] = {xw.x, xw.y, xw.z, xw.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[2 * e] = bf16_lo_to_f32(x4[e]);
-        x[2 * e + 1] = bf16_hi_to_f32(x4[e]);
+        for (int e = 0; e < 4; ++e) {
+          x[2 * e] = bf16_lo_to_f32(x4[e]);
+          x[2 * e + 1] = bf16_hi_to_f32(x4[e]);
+        }
       }
       const float4 g0 = *(const float4*)(p.dxt + rc * D + sub * 8);
       const float4 g1 = *(const float4*)(p.dxt + rc * D + sub * 8 + 4);
@@ -798,10 +805,18 @@ __global__ __launch_bounds__(kT) void bwd_norm_rope_kernel(const NArgs p) {
     for (int o = 1; o < LPR; o <<= 1) dot += __shfl_xor(dot, o);
     dot *= 1.0f / D;
     if (ok) {
-      bf16x8 o8;
+      if constexpr (std::is_same<E, float>::value) {
+        float* o = (float*)p.dx + row * D + sub * 8;
+        *(float4*)o = make_float4(rn * (dxh[0] - xh[0] * dot), rn * (dxh[1] - xh[1] * dot),
+                                  rn * (dxh[2] - xh[2] * dot), rn * (dxh[3] - xh[3] * dot));
+        *(float4*)(o + 4) = make_float4(rn * (dxh[4] - xh[4] * dot), rn * (dxh[5] - xh[5] * dot),
+                                        rn * (dxh[6] - xh[6] * dot), rn * (dxh[7] - xh[7] * dot));
+      } else {
+        bf16x8 o8;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o8[e] = (bf16)(rn * (dxh[e] - xh[e] * dot));
-      *(bf16x8*)(p.dx + row * D + sub * 8) = o8;
+        for (int e = 0; e < 8; ++e) o8[e] = (bf16)(rn * (dxh[e] - xh[e] * dot));
+        *(bf16x8*)((bf16*)p.dx + row * D + sub * 8) = o8;
+      }
     }
   }
 #pragma unroll
@@ -867,6 +882,350 @@ hipError_t launch_big(K kern, dim3 grid, dim3 block, int smem, hipStream_t s, co
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(kern, grid, block, smem, s, a);
+  return hipGetLastError();
+}
+
+// ---- vector-ALU backward: fp32 tensors, or head groups the MFMA kernels do not take ------
+// The same gradient in fp32 arithmetic throughout (element type E of the tensors): Q~ (times
+// the softmax scale) and K~ from the forward's transform, then
+//   prep:  dA = dO sigmoid(G) (SWA; dO itself for the global layer), D = sum dO O, dG,
+//   dq:    per query (one lane, 64 per workgroup): the row log-sum-exp unless the forward
+//          gave it, then dq~ = scale sum_j P (dP - D) k~_j over the visible keys,
+//   dk/dv: per key (one lane): dv = sum_i P dA_i, dk~ = sum_i dS q~_i (scale included in
+//          Q~) over the visible queries of every head of the group,
+// and the norm/RoPE backward and weight reductions of the MFMA path.
+constexpr int kVT = 64;   // rows (queries or keys) per workgroup of the vector-ALU kernels
+
+struct VArgs {
+  const void* out;     // forward output O [B][T][Hq][D]
+  const void* dout;
+  const void* g;       // gate pre-activation (SWA) or nullptr
+  const void* v;       // [B][T][Hkv][D]
+  const void* qt;      // Q~ * scale [B][Hq][T][D]
+  const void* kt;      // K~ [B][Hkv][T][D]
+  void* da;            // dA [B][T][Hq][D] (dout itself for the global layer)
+  float* dsum;         // D [B][Hq][T]
+  float* lse;          // row log-sum-exp, natural log [B][Hq][T]
+  const float* lse_in; // the forward's, or nullptr
+  float* dqt;          // dq~ [B][T][Hq][D] fp32
+  float* dkt;          // dk~ [B][T][Hkv][D] fp32
+  void* dv;            // [B][T][Hkv][D]
+  void* dg;            // [B][T][Hq][D] or nullptr
+  int B, T, Hq, Hkv, window, swa, group;
+  float scale;
+};
+
+template <typename E>
+__device__ __forceinline__ float ld(const E* x, size_t i) { return (float)x[i]; }
+
+// one thread per (b, t, head) row
+template <int D, typename E>
+__global__ __launch_bounds__(kT) void valu_bwd_prep_kernel(const VArgs p) {
+  const int64_t row = (int64_t)blockIdx.x * kT + threadIdx.x;
+  if (row >= (int64_t)p.B * p.T * p.Hq) return;
+  const int h = (int)(row % p.Hq);
+  const int64_t bt = row / p.Hq;
+  const int b = (int)(bt / p.T), t = (int)(bt % p.T);
+  const E* dO = (const E*)p.dout + row * D;
+  const E* O = (const E*)p.out + row * D;
+  float dsum = 0.f;
+#pragma unroll 8
+  for (int c = 0; c < D; ++c) dsum = __builtin_fmaf(ld(dO, c), ld(O, c), dsum);
+  if (p.g) {
+    const E* G = (const E*)p.g + row * D;
+    E* dA = (E*)p.da + row * D;
+    E* dG = (E*)p.dg + row * D;
+#pragma unroll 8
+    for (int c = 0; c < D; ++c) {
+      const float sg = sigmoidf_(ld(G, c));
+      dA[c] = (E)(ld(dO, c) * sg);
+      dG[c] = (E)(ld(dO, c) * ld(O, c) * (1.0f - sg));
+    }
+  }
+  p.dsum[((size_t)b * p.Hq + h) * p.T + t] = dsum;
+}
+
+__device__ __forceinline__ bool valu_visible(int key, int q, int T, int swa, int window) {
+  return key < T && q < T && key <= q && (!swa || key > q - window);
+}
+
+// grid (query tiles, Hq, B), kVT threads; dynamic LDS: K~, V and dA rows (padded)
+template <int D, typename E>
+__global__ __launch_bounds__(kVT) void valu_bwd_dq_kernel(const VArgs p) {
+  constexpr int RS = D + 1;
+  extern __shared__ float vsm[];
+  float* sK = vsm;
+  float* sV = sK + kVT * RS;
+  float* sA = sV + kVT * RS;
+  const int t = threadIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int kvh = h / p.group;
+  const int i0 = blockIdx.x * kVT, i = i0 + t;
+  const bool valid = i < p.T;
+  const int ic = valid ? i : p.T - 1;
+  const E* qrow = (const E*)p.qt + (((size_t)b * p.Hq + h) * p.T + ic) * D;
+  const E* arow = (const E*)p.da + (((size_t)b * p.T + ic) * p.Hq + h) * D;
+  float qv[D];
+#pragma unroll
+  for (int c = 0; c < D; ++c) {
+    qv[c] = ld(qrow, c);
+    sA[t * RS + c] = ld(arow, c);
+  }
+  const size_t st = ((size_t)b * p.Hq + h) * p.T + ic;
+  const float dsum = p.dsum[st];
+  const int kt_lo = p.swa ? max(0, i0 - p.window + 1) / kVT : 0;
+  const int kt_hi = (min(i0 + kVT, p.T) - 1) / kVT;
+  auto stage = [&](int kt, bool with_v) {
+    const int j = min(kt * kVT + t, p.T - 1);
+    const E* krow = (const E*)p.kt + (((size_t)b * p.Hkv + kvh) * p.T + j) * D;
+    const E* vrow = (const E*)p.v + (((size_t)b * p.T + j) * p.Hkv + kvh) * D;
+#pragma unroll
+    for (int c = 0; c < D; ++c) {
+      sK[t * RS + c] = ld(krow, c);
+      if (with_v) sV[t * RS + c] = ld(vrow, c);
+    }
+  };
+  float lse;
+  if (p.lse_in) {
+    lse = p.lse_in[st];
+  } else {
+    float m = -INFINITY, l = 0.f;
+    for (int kt = kt_lo; kt <= kt_hi; ++kt) {
+      __syncthreads();
+      stage(kt, false);
+      __syncthreads();
+      for (int jj = 0; jj < kVT; ++jj) {
+        const int key = kt * kVT + jj;
+        if (!valu_visible(key, i, p.T, p.swa, p.window)) continue;
+        float sc = 0.f;
+#pragma unroll
+        for (int c = 0; c < D; ++c) sc = __builtin_fmaf(qv[c], sK[jj * RS + c], sc);
+        const float mn = fmaxf(m, sc);
+        l = l * expf(m - mn) + expf(sc - mn);
+        m = mn;
+      }
+    }
+    lse = m + logf(l);
+  }
+  if (valid) p.lse[st] = lse;
+  float acc[D];
+#pragma unroll
+  for (int c = 0; c < D; ++c) acc[c] = 0.f;
+  for (int kt = kt_lo; kt <= kt_hi; ++kt) {
+    __syncthreads();
+    stage(kt, true);
+    __syncthreads();
+    for (int jj = 0; jj < kVT; ++jj) {
+      const int key = kt * kVT + jj;
+      if (!valu_visible(key, i, p.T, p.swa, p.window)) continue;
+      float sc = 0.f, dp = 0.f;
+#pragma unroll
+      for (int c = 0; c < D; ++c) {
+        sc = __builtin_fmaf(qv[c], sK[jj * RS + c], sc);
+        dp = __builtin_fmaf(sA[t * RS + c], sV[jj * RS + c], dp);
+      }
+      const float ds = expf(sc - lse) * (dp - dsum);
+#pragma unroll
+      for (int c = 0; c < D; ++c) acc[c] = __builtin_fmaf(ds, sK[jj * RS + c], acc[c]);
+    }
+  }
+  if (valid) {
+    float* dst = p.dqt + (((size_t)b * p.T + i) * p.Hq + h) * D;
+#pragma unroll
+    for (int c = 0; c < D; ++c) dst[c] = acc[c] * p.scale;
+  }
+}
+
+// grid (key tiles, Hkv, B), kVT threads; dynamic LDS: Q~ and dA rows of a query tile, the
+// lane's own K~ and V rows (padded), the tile's lse and D
+template <int D, typename E>
+__global__ __launch_bounds__(kVT) void valu_bwd_dkdv_kernel(const VArgs p) {
+  constexpr int RS = D + 1;
+  extern __shared__ float vsm[];
+  float* sQ = vsm;
+  float* sA = sQ + kVT * RS;
+  float* sK = sA + kVT * RS;
+  float* sV = sK + kVT * RS;
+  float* sL = sV + kVT * RS;
+  float* sD = sL + kVT;
+  const int t = threadIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int k0 = blockIdx.x * kVT, j = k0 + t;
+  const int jc = min(j, p.T - 1);
+  {
+    const E* krow = (const E*)p.kt + (((size_t)b * p.Hkv + kvh) * p.T + jc) * D;
+    const E* vrow = (const E*)p.v + (((size_t)b * p.T + jc) * p.Hkv + kvh) * D;
+#pragma unroll
+    for (int c = 0; c < D; ++c) {
+      sK[t * RS + c] = ld(krow, c);
+      sV[t * RS + c] = ld(vrow, c);
+    }
+  }
+  float dk[D], dv[D];
+#pragma unroll
+  for (int c = 0; c < D; ++c) {
+    dk[c] = 0.f;
+    dv[c] = 0.f;
+  }
+  const int q_last = p.swa ? min(p.T - 1, k0 + kVT - 1 + p.window - 1) : p.T - 1;
+  for (int hh = 0; hh < p.group; ++hh) {
+    const int h = kvh * p.group + hh;
+    for (int qt = k0 / kVT; qt * kVT <= q_last; ++qt) {
+      const int ic = min(qt * kVT + t, p.T - 1);
+      const E* qrow = (const E*)p.qt + (((size_t)b * p.Hq + h) * p.T + ic) * D;
+      const E* arow = (const E*)p.da + (((size_t)b * p.T + ic) * p.Hq + h) * D;
+      __syncthreads();
+#pragma unroll
+      for (int c = 0; c < D; ++c) {
+        sQ[t * RS + c] = ld(qrow, c);
+        sA[t * RS + c] = ld(arow, c);
+      }
+      sL[t] = p.lse[((size_t)b * p.Hq + h) * p.T + ic];
+      sD[t] = p.dsum[((size_t)b * p.Hq + h) * p.T + ic];
+      __syncthreads();
+      for (int r = 0; r < kVT; ++r) {
+        const int i = qt * kVT + r;
+        if (!valu_visible(j, i, p.T, p.swa, p.window)) continue;
+        float sc = 0.f, dp = 0.f;
+#pragma unroll
+        for (int c = 0; c < D; ++c) {
+          sc = __builtin_fmaf(sQ[r * RS + c], sK[t * RS + c], sc);
+          dp = __builtin_fmaf(sA[r * RS + c], sV[t * RS + c], dp);
+        }
+        const float pr = expf(sc - sL[r]);
+        const float ds = pr * (dp - sD[r]);
+#pragma unroll
+        for (int c = 0; c < D; ++c) {
+          dv[c] = __builtin_fmaf(pr, sA[r * RS + c], dv[c]);
+          dk[c] = __builtin_fmaf(ds, sQ[r * RS + c], dk[c]);
+        }
+      }
+    }
+  }
+  if (j < p.T) {
+    const size_t o = (((size_t)b * p.T + j) * p.Hkv + kvh) * D;
+#pragma unroll
+    for (int c = 0; c < D; ++c) {
+      ((E*)p.dv)[o + c] = (E)dv[c];
+      p.dkt[o + c] = dk[c];
+    }
+  }
+}
+
+// Workspace of the vector-ALU path (Q~, K~ and dA in the tensors' element type), within
+// the bytes backward_workspace_bytes gives for the MFMA path of the same shape.
+WsLayout valu_ws_layout(int B, int T, int Hq, int Hkv, int d, int esz) {
+  WsLayout L{};
+  size_t o = 0;
+  const size_t nq = (size_t)B * T * Hq, nk = (size_t)B * T * Hkv;
+  L.qt = o;   o += align256(nq * d * esz);
+  L.kt = o;   o += align256(nk * d * esz);
+  L.da = o;   o += align256(nq * d * esz);
+  L.dsum = o; o += align256(nq * 4);
+  L.lse = o;  o += align256(nq * 4);
+  L.dqt = o;  o += align256(nq * d * 4);
+  L.dkt = o;  o += align256(nk * d * 4);
+  L.nq_blk = kNormBlocks;
+  L.nk_blk = kNormBlocks;
+  L.part = o; o += align256((size_t)(L.nq_blk + L.nk_blk) * d * 4);
+  L.total = o;
+  return L;
+}
+
+template <int D, typename E>
+hipError_t valu_backward_t(const BackwardArgs& a, hipStream_t s) {
+  const WsLayout L = valu_ws_layout(a.B, a.T, a.Hq, a.Hkv, D, (int)sizeof(E));
+  char* ws = (char*)a.ws;
+  NormRopeArgs n;
+  n.pos = nullptr;
+  n.B = a.B;
+  n.T = a.T;
+  n.d = D;
+  n.rdim = a.rdim;
+  n.pos_offset = a.pos_offset;
+  n.is_bf16 = std::is_same<E, bf16>::value;
+  n.eps = a.eps;
+  n.fr = a.fr;
+  n.x = a.q;
+  n.w = a.wq;
+  n.y = ws + L.qt;
+  n.out_scale = a.scale;   // Q~ carries the (natural-log) softmax scale
+  n.H = a.Hq;
+  n.ysb = (int64_t)a.Hq * a.T * D;
+  n.yst = D;
+  n.ysh = (int64_t)a.T * D;
+  hipError_t e = launch_qknorm_rope(n, s);
+  if (e != hipSuccess) return e;
+  n.x = a.k;
+  n.w = a.wk;
+  n.y = ws + L.kt;
+  n.out_scale = 1.0f;
+  n.H = a.Hkv;
+  n.ysb = (int64_t)a.Hkv * a.T * D;
+  n.ysh = (int64_t)a.T * D;
+  e = launch_qknorm_rope(n, s);
+  if (e != hipSuccess) return e;
+
+  VArgs p;
+  p.out = a.out;
+  p.dout = a.dout;
+  p.g = a.g;
+  p.v = a.v;
+  p.qt = ws + L.qt;
+  p.kt = ws + L.kt;
+  p.da = a.g ? (void*)(ws + L.da) : const_cast<void*>(a.dout);
+  p.dsum = (float*)(ws + L.dsum);
+  p.lse = (float*)(ws + L.lse);
+  p.lse_in = a.lse;
+  p.dqt = (float*)(ws + L.dqt);
+  p.dkt = (float*)(ws + L.dkt);
+  p.dv = a.dv;
+  p.dg = a.dg;
+  p.B = a.B;
+  p.T = a.T;
+  p.Hq = a.Hq;
+  p.Hkv = a.Hkv;
+  p.window = a.window;
+  p.swa = a.swa;
+  p.group = a.Hq / a.Hkv;
+  p.scale = a.scale;
+  const int64_t rows = (int64_t)a.B * a.T * a.Hq;
+  hipLaunchKernelGGL((valu_bwd_prep_kernel<D, E>), dim3((unsigned)((rows + kT - 1) / kT)),
+                     dim3(kT), 0, s, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned n_t = (unsigned)((a.T + kVT - 1) / kVT);
+  e = launch_big(valu_bwd_dq_kernel<D, E>, dim3(n_t, a.Hq, a.B), dim3(kVT),
+                 3 * kVT * (D + 1) * 4, s, p);
+  if (e != hipSuccess) return e;
+  e = launch_big(valu_bwd_dkdv_kernel<D, E>, dim3(n_t, a.Hkv, a.B), dim3(kVT),
+                 (4 * kVT * (D + 1) + 2 * kVT) * 4, s, p);
+  if (e != hipSuccess) return e;
+
+  NArgs nb;
+  nb.B = a.B;
+  nb.T = a.T;
+  nb.rdim = a.rdim;
+  nb.pos_offset = a.pos_offset;
+  nb.eps = a.eps;
+  nb.fr = a.fr;
+  float* part = (float*)(ws + L.part);
+  nb.x = a.q;
+  nb.w = a.wq;
+  nb.dxt = p.dqt;
+  nb.dx = a.dq;
+  nb.part = part;
+  nb.H = a.Hq;
+  hipLaunchKernelGGL((bwd_norm_rope_kernel<D, E>), dim3(L.nq_blk), dim3(kT), 0, s, nb);
+  nb.x = a.k;
+  nb.w = a.wk;
+  nb.dxt = p.dkt;
+  nb.dx = a.dk;
+  nb.part = part + (size_t)L.nq_blk * D;
+  nb.H = a.Hkv;
+  hipLaunchKernelGGL((bwd_norm_rope_kernel<D, E>), dim3(L.nk_blk), dim3(kT), 0, s, nb);
+  hipLaunchKernelGGL(bwd_dw_reduce_kernel<D>, dim3(D), dim3(kT), 0, s, (const float*)part,
+                     L.nq_blk, a.dwq);
+  hipLaunchKernelGGL(bwd_dw_reduce_kernel<D>, dim3(D), dim3(kT), 0, s,
+                     (const float*)(part + (size_t)L.nq_blk * D), L.nk_blk, a.dwk);
   return hipGetLastError();
 }
 
@@ -977,17 +1336,17 @@ hipError_t backward_t(const BackwardArgs& a, hipStream_t s) {
   nb.eps = a.eps;
   nb.fr = a.fr;
   float* part = (float*)(ws + L.part);
-  nb.x = (const bf16*)a.q;
+  nb.x = a.q;
   nb.w = a.wq;
   nb.dxt = p.dqt;
-  nb.dx = (bf16*)a.dq;
+  nb.dx = a.dq;
   nb.part = part;
   nb.H = a.Hq;
   hipLaunchKernelGGL(bwd_norm_rope_kernel<D>, dim3(L.nq_blk), dim3(kT), 0, s, nb);
-  nb.x = (const bf16*)a.k;
+  nb.x = a.k;
   nb.w = a.wk;
   nb.dxt = p.dkt;
-  nb.dx = (bf16*)a.dk;
+  nb.dx = a.dk;
   nb.part = part + (size_t)L.nq_blk * D;
   nb.H = a.Hkv;
   hipLaunchKernelGGL(bwd_norm_rope_kernel<D>, dim3(L.nk_blk), dim3(kT), 0, s, nb);
@@ -1001,10 +1360,19 @@ hipError_t backward_t(const BackwardArgs& a, hipStream_t s) {
 }  // namespace
 
 size_t backward_workspace_bytes(int B, int T, int Hq, int Hkv, int d) {
-  return ws_layout(B, T, Hq, Hkv, d).total;
+  // the MFMA path's layout, or the vector-ALU path's with fp32 rows if that is larger
+  const size_t m = ws_layout(B, T, Hq, Hkv, d).total;
+  const size_t v = valu_ws_layout(B, T, Hq, Hkv, d, 4).total;
+  return m > v ? m : v;
 }
 
+bool backward_mfma_supported(int group) { return group == 1 || group == 2 || group == 4 || group == 8; }
+
 hipError_t launch_prefill_backward(const BackwardArgs& a, hipStream_t s) {
+  if (a.f32)
+    return a.d == 128 ? valu_backward_t<128, float>(a, s) : valu_backward_t<64, float>(a, s);
+  if (!backward_mfma_supported(a.Hq / a.Hkv))
+    return a.d == 128 ? valu_backward_t<128, bf16>(a, s) : valu_backward_t<64, bf16>(a, s);
   return a.d == 128 ? backward_t<128>(a, s) : backward_t<64>(a, s);
 }
 

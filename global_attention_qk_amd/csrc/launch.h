@@ -83,7 +83,9 @@ struct NormRopeArgs {
 };
 hipError_t launch_qknorm_rope(const NormRopeArgs& a, hipStream_t s);
 
-// Backward pass of a prefill call (bf16, d 64 or 128): gradients of sum(dout * out).
+// Backward pass of a prefill call (d 64 or 128): gradients of sum(dout * out). bf16 with
+// head groups 1, 2, 4, 8 on the MFMA kernels; fp32 and other head groups on vector-ALU
+// kernels.
 struct BackwardArgs {
   const void* q;
   const void* k;
@@ -104,6 +106,7 @@ struct BackwardArgs {
   int B, T, Hq, Hkv, d, window, rdim, pos_offset, swa;
   float eps, scale;
   RopeFreq fr;
+  int f32;             // fp32 tensors (the vector-ALU kernels), else bf16
 };
 size_t backward_workspace_bytes(int B, int T, int Hq, int Hkv, int d);
 hipError_t launch_prefill_backward(const BackwardArgs& a, hipStream_t s);

@@ -150,9 +150,11 @@ size_t zgattn_global_prefill_varlen_workspace_bytes(const zgattn_desc* desc, int
  * (as written by zgattn_global_prefill; device fp32 [B, Hq, T]) or NULL, in which case the
  * log-sum-exp is recomputed by an extra pass over the keys; the SWA form always recomputes
  * it (its rows see at most `window` keys). dq, dg: [B, T, Hq, d]; dk, dv: [B, T, Hkv, d]
- * (bf16, written, not accumulated); dwq, dwk: fp32 [d] (written). workspace (device, >=
- * zgattn_prefill_backward_workspace_bytes(desc) bytes) holds the transformed q~/k~, the
- * row statistics and the fp32 gradients of q~ and k~. bf16 only; head groups 1, 2, 4, 8.
+ * (the tensors' dtype, written, not accumulated); dwq, dwk: fp32 [d] (written). workspace
+ * (device, >= zgattn_prefill_backward_workspace_bytes(desc) bytes, the same for bf16 and
+ * fp32) holds the transformed q~/k~, the row statistics and the fp32 gradients of q~ and
+ * k~. bf16 with head groups 1, 2, 4, 8 runs on MFMA kernels; fp32 tensors and other head
+ * groups run on vector-ALU kernels (fp32 arithmetic), which also take the forward's `lse`.
  */
 size_t zgattn_prefill_backward_workspace_bytes(const zgattn_desc* desc);
 int zgattn_swa_prefill_backward(const zgattn_desc* desc, const void* q, const void* k,

@@ -134,6 +134,13 @@ static void prefill_checks() {
   CHECK(stub::last_backward.lse == (const float*)P(14));
   CHECK(zgattn_global_prefill_backward(&d, P(1), P(2), P(3), W(), W(), P(5), (const float*)((char*)P(14) + 1), P(8), P(9), P(10), P(11), dw, dw, P(13), bneed, nullptr) == ZGATTN_EINVAL);
   CHECK(zgattn_swa_prefill_backward(&d, P(1), P(2), P(3), nullptr, W(), W(), P(5), P(8), P(9), P(10), P(11), P(12), dw, dw, P(13), bneed, nullptr) == ZGATTN_ENULL);
+  CHECK(stub::last_backward.f32 == 0);
+  // fp32 tensors and other head groups are accepted (the library picks the kernels)
+  CHECK(zgattn_prefill_backward_workspace_bytes(&f) > 0);
+  CHECK(zgattn_swa_prefill_backward(&f, P(1), P(2), P(3), P(4), W(), W(), P(5), P(8), P(9), P(10), P(11), P(12), dw, dw, P(13), zgattn_prefill_backward_workspace_bytes(&f), nullptr) == ZGATTN_OK);
+  CHECK(stub::last_backward.f32 == 1 && stub::last_backward.swa == 1);
+  CHECK(zgattn_global_prefill_backward(&g16, P(1), P(2), P(3), W(), W(), P(5), nullptr, P(8), P(9), P(10), P(11), dw, dw, P(13), zgattn_prefill_backward_workspace_bytes(&g16), nullptr) == ZGATTN_OK);
+  CHECK(stub::last_backward.f32 == 0 && stub::last_backward.Hq == 32 && stub::last_backward.Hkv == 2);
 }
 
 static void decode_checks() {

@@ -221,8 +221,17 @@ def test_backward_checks():
     assert call(dg=None) == -2
     assert call(dout=None) == -2
     assert call(dout=ctypes.c_void_p(4100)) == -1
-    assert call(d=_d(batch=2, seq_len=300, n_q_heads=8, n_kv_heads=2, dtype=L.F32)) == -4
-    assert call(d=_d(batch=2, seq_len=300, n_q_heads=48, n_kv_heads=3)) == -4
+    # fp32 tensors and head groups off the MFMA kernels take the vector-ALU backward: the
+    # same checks, the same workspace size (the larger of the two paths' layouts)
+    df = _d(batch=2, seq_len=300, n_q_heads=8, n_kv_heads=2, dtype=L.F32)
+    assert lib.zgattn_prefill_backward_workspace_bytes(ctypes.byref(df)) == need
+    assert call(d=df, nb=need - 1) == -5
+    assert call(d=df, g=None) == -2
+    dg16 = _d(batch=2, seq_len=300, n_q_heads=48, n_kv_heads=3)
+    need16 = lib.zgattn_prefill_backward_workspace_bytes(ctypes.byref(dg16))
+    assert need16 > need
+    assert call(d=dg16, nb=need16 - 1) == -5
+    assert call(d=dg16, ws=None, nb=need16) == -5
     assert call(d=_d(batch=2, seq_len=0, n_q_heads=8, n_kv_heads=2)) == 0
     st = lib.zgattn_global_prefill_backward(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                             None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, need,

@@ -1,8 +1,10 @@
 """Backward pass (zgattn_*_prefill_backward) against the fp64 oracle's gradients (GPU).
 
 Gradients of sum(dout * out) with dout ~ N(0, 1). Tolerance: max-abs error within 2e-2 of
-max(1, max |reference|) per tensor: the products run on bf16 operands (Q~, K~, V, dA, P and
-dS rounded to bf16, fp32 accumulation) and the inputs' bf16 rounding bounds the rest.
+max(1, max |reference|) per tensor for bf16 tensors: the products run on bf16 operands (Q~,
+K~, V, dA, P and dS rounded to bf16, fp32 accumulation) and the inputs' bf16 rounding bounds
+the rest. fp32 tensors (the vector-ALU backward, fp32 throughout): 1e-4 of the same scale,
+room for fp32 rounding summed over a thousand keys.
 """
 
 import numpy as np
@@ -15,20 +17,23 @@ from workloads import host_tensor, norm_weight
 pytestmark = pytest.mark.gpu
 
 REL = 2e-2
+REL_F32 = 1e-4
 
 
-def _check(B, T, Hq, Hkv, d, window, seed, pos_offset=0, fwd_lse=False):
+def _check(B, T, Hq, Hkv, d, window, seed, pos_offset=0, fwd_lse=False, dtype="bf16",
+           rdim=None):
     need_gpu()
     import torch
     import global_attention_qk_amd as zg
-    q = host_tensor((B, T, Hq, d), seed, "bf16")
-    k = host_tensor((B, T, Hkv, d), seed + 1, "bf16")
-    v = host_tensor((B, T, Hkv, d), seed + 2, "bf16")
-    g = host_tensor((B, T, Hq, d), seed + 3, "bf16", 2 ** 0.5) if window else None
-    do = host_tensor((B, T, Hq, d), seed + 4, "bf16")
+    q = host_tensor((B, T, Hq, d), seed, dtype)
+    k = host_tensor((B, T, Hkv, d), seed + 1, dtype)
+    v = host_tensor((B, T, Hkv, d), seed + 2, dtype)
+    g = host_tensor((B, T, Hq, d), seed + 3, dtype, 2 ** 0.5) if window else None
+    do = host_tensor((B, T, Hq, d), seed + 4, dtype)
     wq = torch.from_numpy(norm_weight(d, seed + 5))
     wk = torch.from_numpy(norm_weight(d, seed + 6))
-    r = zg.rotary_dim_for(d)
+    r = zg.rotary_dim_for(d) if rdim is None else rdim
+    rel = REL_F32 if dtype == "f32" else REL
     cq, ck, cv, cdo, cwq, cwk = (t.cuda() for t in (q, k, v, do, wq, wk))
     cg = g.cuda() if g is not None else None
     if window:
@@ -61,8 +66,9 @@ def _check(B, T, Hq, Hkv, d, window, seed, pos_offset=0, fwd_lse=False):
     for name, t in got.items():
         want = ref[name]
         err = float(np.max(np.abs(host64(t) - want)))
-        lim = REL * max(1.0, float(np.max(np.abs(want))))
-        say("backward", (B, T, Hq, Hkv, d, window), name, f"err={err:.3e} lim={lim:.3e}")
+        lim = rel * max(1.0, float(np.max(np.abs(want))))
+        say("backward", (B, T, Hq, Hkv, d, window, dtype, r), name,
+            f"err={err:.3e} lim={lim:.3e}")
         assert err <= lim, (name, err, lim)
 
 
@@ -106,6 +112,32 @@ def test_backward_ragged_top_tile(window, lse):
     # query tile, a run of fully visible tiles and the diagonal tiles; B = 2, 4 query heads
     # per KV head
     _check(2, 1000, 8, 2, 128, window, 2000, fwd_lse=lse)
+
+
+@pytest.mark.parametrize("window", [None, 128, 37])
+def test_backward_f32(window):
+    # fp32 tensors: the vector-ALU backward (forward on the vector-ALU prefill kernel),
+    # several 64-row tiles, a ragged tail, 4 query heads per KV head
+    _check(2, 300, 8, 2, 128, window, 2500, dtype="f32")
+
+
+def test_backward_f32_head_dim_64_offset():
+    _check(1, 200, 6, 2, 64, None, 2510, pos_offset=3000, dtype="f32")
+    _check(1, 200, 6, 2, 64, 80, 2520, pos_offset=3000, dtype="f32")
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(6, 2), (3, 1), (32, 2)])
+def test_backward_bf16_other_head_groups(Hq, Hkv):
+    # head groups 3 and 16: bf16 tensors on the vector-ALU backward
+    _check(1, 260, Hq, Hkv, 128, None, 2600 + Hq)
+    _check(1, 260, Hq, Hkv, 64, 100, 2610 + Hq)
+
+
+def test_backward_bf16_rotary_above_64():
+    # a rotary dim the MFMA forward does not take (vector-ALU forward); the MFMA backward
+    # handles any rotary dim
+    _check(1, 200, 8, 2, 128, None, 2700, rdim=96)
+    _check(1, 200, 8, 2, 128, 64, 2710, rdim=128)
 
 
 def test_backward_forward_lse_head_dim_64_offset():
