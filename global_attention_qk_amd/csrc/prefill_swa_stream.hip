@@ -67,7 +67,8 @@ constexpr int kOffRaw = kOffV + kRing * kVBlkB;       // two raw K buffers
 constexpr int kOffTrig = kOffRaw + 2 * kRawB;         // three trig tables
 constexpr int kOffW = kOffTrig + kTrigBufs * kTrigB;  // wq * qscale, wk
 constexpr int kOffFr = kOffW + 2 * kD * 4;            // RoPE frequencies (hi, lo)
-constexpr int kSmem = kOffFr + 2 * 32 * 4;
+constexpr int kOffRn = kOffFr + 2 * 32 * 4;           // 1/rms of the tile's key rows
+constexpr int kSmem = kOffRn + kStep * 4;
 static_assert(kSmem <= 160 * 1024, "LDS budget");
 
 struct SArgs {
@@ -255,42 +256,58 @@ __device__ __forceinline__ void swa_stream_body(const SArgs& p, const float sini
     const int tl = opaque(tid);
     *(u32x4*)(raw_buf(t) + krow_off(tl >> 4, tl & 15)) = kr;
   };
-  // RMSNorm + partial RoPE of staged tile t into its ring block: 16 lanes per key, lane
-  // kc writes dims 8 kc .. + 7 (rotated where < 42, the partner read from the raw row).
+  // RMSNorm + partial RoPE of staged tile t into its ring block, in two branch-free passes
+  // over the four key rows of this wave (rows 4 w .. 4 w + 3 in both passes, so the
+  // second pass sees the first one's LDS writes in order, with no barrier):
+  //   1. 16 lanes per key, lane kc: dims 8 kc .. + 7 normalised and weighted,
+  //      x w / rms, the row's 1/rms kept in LDS;
+  //   2. one lane per rotated pair (4 keys x 21 pairs = 84 jobs, two rounds): both
+  //      members of the pair from the raw row, rotated, overwriting what pass 1 wrote.
   auto transform_k = [&](int t) {
     const char* raw = raw_buf(t);
     const float2* tr = trig_buf(t);
-    const int tl = opaque(tid);
-    const int krow = tl >> 4, kc = tl & 15;
-    const u32x4 r0 = *(const u32x4*)(raw + krow_off(krow, kc));
-    float x[8];
-    float ss = 0.f;
+    char* blk = smem + kOffK + ring_slot(t) * kKBlkB;
+    float* sRn = (float*)(smem + kOffRn);
+    {
+      const int tl = opaque(tid);
+      const int krow = tl >> 4, kc = tl & 15;
+      const u32x4 r0 = *(const u32x4*)(raw + krow_off(krow, kc));
+      const float4 w0 = *(const float4*)(sWk + 8 * kc);
+      const float4 w1 = *(const float4*)(sWk + 8 * kc + 4);
+      const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      float x[8];
+      float ss = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      x[e] = bf16_elem(r0, e);
-      ss = __builtin_fmaf(x[e], x[e], ss);
-    }
-    ss = row16_sum(ss);
-    const float rn = __builtin_amdgcn_rsqf(ss * (1.0f / kD) + p.eps);
-    const bf16* rrow = (const bf16*)(raw + krow * kKRowB);
-    bf16x8 o;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = kc * 8 + e;
-      const bool rot = d < 2 * kRH;
-      const bool first = d < kRH;
-      const int j = first ? d : d - kRH;
-      const int pd = rot ? (first ? d + kRH : d - kRH) : d;
-      float c = 1.f, s = 0.f, xp = 0.f;
-      if (rot) {
-        const float2 cs = tr[krow * kRHP + j];
-        c = cs.x;
-        s = first ? -cs.y : cs.y;
-        xp = (float)rrow[pd] * sWk[pd];
+      for (int e = 0; e < 8; ++e) {
+        x[e] = bf16_elem(r0, e);
+        ss = __builtin_fmaf(x[e], x[e], ss);
       }
-      o[e] = (bf16)((x[e] * sWk[d] * c + xp * s) * rn);
+      ss = row16_sum(ss);
+      const float rn = __builtin_amdgcn_rsqf(ss * (1.0f / kD) + p.eps);
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (bf16)(x[e] * w[e] * rn);
+      *(bf16x8*)(blk + krow_off(krow, kc)) = o;
+      if (kc == 0) sRn[krow] = rn;
     }
-    *(bf16x8*)(smem + kOffK + ring_slot(t) * kKBlkB + krow_off(krow, kc)) = o;
+    const int ln = opaque(lane);
+    const int row0 = 4 * wave;
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int job = ln + 64 * it;
+      if (job < 4 * kRH) {
+        const int kr = row0 + job / kRH;   // key row of the tile
+        const int j = job - (job / kRH) * kRH;
+        const bf16* rrow = (const bf16*)(raw + kr * kKRowB);
+        const float a = (float)rrow[j] * sWk[j];
+        const float b2 = (float)rrow[j + kRH] * sWk[j + kRH];
+        const float2 cs = tr[kr * kRHP + j];
+        const float rn = sRn[kr];
+        bf16* orow = (bf16*)(blk + kr * kKRowB);
+        orow[j] = (bf16)(__builtin_fmaf(a, cs.x, -b2 * cs.y) * rn);
+        orow[j + kRH] = (bf16)(__builtin_fmaf(b2, cs.x, a * cs.y) * rn);
+      }
+    }
   };
   // V of tile t, transposed into its ring block (keys 2 kp, 2 kp + 1 are adjacent slots,
   // so each store is one 32-bit word).
