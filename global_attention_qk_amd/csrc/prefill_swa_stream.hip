@@ -68,7 +68,9 @@ constexpr int kOffTrig = kOffRaw + 2 * kRawB;         // three trig tables
 constexpr int kOffW = kOffTrig + kTrigBufs * kTrigB;  // wq * qscale, wk
 constexpr int kOffFr = kOffW + 2 * kD * 4;            // RoPE frequencies (hi, lo)
 constexpr int kOffRn = kOffFr + 2 * 32 * 4;           // 1/rms of the tile's key rows
-constexpr int kSmem = kOffRn + kStep * 4;
+constexpr int kOffRot = kOffRn + kStep * 4;           // cos/sin of the 32 in-step offsets
+constexpr int kOffBase = kOffRot + kTrigB;            // cos/sin at two steps' first positions
+constexpr int kSmem = kOffBase + 2 * 32 * 8;
 static_assert(kSmem <= 160 * 1024, "LDS budget");
 
 struct SArgs {
@@ -240,8 +242,9 @@ __device__ __forceinline__ void swa_stream_body(const SArgs& p, const float sini
   // ---- LDS producers -----------------------------------------------------------------
   auto trig_buf = [&](int t) { return (float2*)(smem + kOffTrig + ((t + 3 * kTrigBufs) % kTrigBufs) * kTrigB); };
   auto raw_buf = [&](int t) { return smem + kOffRaw + (t & 1) * kRawB; };
-  // RoPE cos/sin of the 32 positions of tile t.
-  auto make_trig = [&](int t) {
+  // RoPE cos/sin of the 32 positions of tile t, each evaluated from its position (the
+  // prologue's tiles).
+  auto make_trig_direct = [&](int t) {
     float2* tr = trig_buf(t);
     for (int e = tid; e < kStep * kRH; e += kThreads) {
       const int pl = e / kRH, j = e - pl * kRH;
@@ -250,6 +253,30 @@ __device__ __forceinline__ void swa_stream_body(const SArgs& p, const float sini
       // load, and waiting for it would also wait for every prefetch issued before it
       rope_cos_sin(p.pos_offset + max(t * kStep + pl, 0), sFr[j], sFr[32 + j], c, s);
       tr[pl * kRHP + j] = make_float2(c, s);
+    }
+  };
+  // cos/sin at the first position of tile t (t >= 0), for the steady state's tables: the
+  // last wave, which builds the fewest table entries.
+  auto make_base = [&](int t) {
+    if (wave == kWaves - 1 && lane < kRH) {
+      float c, s;
+      rope_cos_sin(p.pos_offset + t * kStep, sFr[lane], sFr[32 + lane], c, s);
+      ((float2*)(smem + kOffBase))[(t & 1) * 32 + lane] = make_float2(c, s);
+    }
+  };
+  // The same table in the steady state (t >= 0) by angle addition: the rotation at
+  // position p0 + i is the one at p0 (make_base, a step earlier) times the one at i
+  // (the kernel's constant table of in-step offsets); both factors are evaluated from
+  // their positions, so the product is within a few ulp at any position.
+  auto make_trig = [&](int t) {
+    float2* tr = trig_buf(t);
+    const float2* base = (const float2*)(smem + kOffBase) + (t & 1) * 32;
+    const float2* rot = (const float2*)(smem + kOffRot);
+    for (int e = tid; e < kStep * kRH; e += kThreads) {
+      const int pl = e / kRH, j = e - pl * kRH;
+      const float2 b0 = base[j], r0 = rot[pl * kRHP + j];
+      tr[pl * kRHP + j] = make_float2(__builtin_fmaf(b0.x, r0.x, -b0.y * r0.y),
+                                      __builtin_fmaf(b0.y, r0.x, b0.x * r0.y));
     }
   };
   auto stage_k = [&](const u32x4& kr, int t) {
@@ -405,12 +432,15 @@ __device__ __forceinline__ void swa_stream_body(const SArgs& p, const float sini
 
   // Scores of ring block kb for this wave's 16 queries: two 16-key halves; lane group g
   // holds keys 16 kh + 4 g + r.
-  auto scores = [&](int kb, const bf16x8 (&qreg)[4], f32x4 (&sacc)[2]) {
+  // Halves outside [KH0, KH1] are not computed.
+  auto scores = [&](int kb, const bf16x8 (&qreg)[4], f32x4 (&sacc)[2], auto kh0_tag,
+                    auto kh1_tag) {
+    constexpr int KH0 = decltype(kh0_tag)::value, KH1 = decltype(kh1_tag)::value;
     const int ln = lane;
     const int nn = ln & 15, gg = ln >> 4;
     const char* sK = smem + kOffK + ring_slot(kb) * kKBlkB;
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
+    for (int kh = KH0; kh <= KH1; ++kh) {
       sacc[kh] = (f32x4){sinit, sinit, sinit, sinit};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
@@ -443,27 +473,43 @@ __device__ __forceinline__ void swa_stream_body(const SArgs& p, const float sini
   };
 
   // Fast path (128-key window, static shift, away from position 0): the five blocks
-  // unrolled; masks only on the band-edge block (visible: keys above the query's offset
-  // in its block) and the diagonal block (keys at or below it); the first block starts the
-  // accumulators from zero.
-  auto blocks_full = [&](int s, const bf16x8 (&qreg)[4]) {
+  // unrolled, specialised on which 16 positions of the step the wave holds (PH); masks
+  // only on the band-edge block (visible: keys above the query's offset in its block) and
+  // the diagonal block (keys at or below it), whose 16-key half on the far side of the
+  // wave's queries is not computed at all; the first block starts the accumulators from
+  // zero.
+  auto blocks_full = [&](int s, const bf16x8 (&qreg)[4], auto ph_tag) {
+    constexpr int PH = decltype(ph_tag)::value;
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
     const int ln = lane;
     const int nn = ln & 15, gg = ln >> 4;
-    const int qo = 16 * ph + nn;   // query offset within the step's 32 positions
+    const int qo = 16 * PH + nn;   // query offset within the step's 32 positions
     float ls = 0.f;
 #pragma unroll
     for (int jb = 0; jb < kNB; ++jb) {
       const int kb = s - (kNB - 1) + jb;
+      // 16-key halves: the band-edge block's lower half lies wholly below queries 16..31
+      // (masked), the diagonal block's upper half wholly above queries 0..15 (masked);
+      // the other half of those blocks straddles the queries and takes the mask
+      const bool edge = jb == 0, diag = jb == kNB - 1;
       f32x4 sacc[2];
-      scores(kb, qreg, sacc);
+      if (edge && PH == 1) scores(kb, qreg, sacc, I1{}, I1{});
+      else if (diag && PH == 0) scores(kb, qreg, sacc, I0{}, I0{});
+      else scores(kb, qreg, sacc, I0{}, I1{});
       float pf[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int kh = e >> 2, r = e & 3;
+        const bool skipped = (edge && PH == 1 && kh == 0) || (diag && PH == 0 && kh == 1);
+        if (skipped) {
+          pf[e] = 0.f;
+          continue;
+        }
         float pv = fast_exp2(sacc[kh][r]);
         const bool below = 16 * kh + 4 * gg + r <= qo;
-        if (jb == 0) pv = below ? 0.f : pv;
-        if (jb == kNB - 1) pv = below ? pv : 0.f;
+        if (edge && kh == PH) pv = below ? 0.f : pv;
+        if (diag && kh == PH) pv = below ? pv : 0.f;
         pf[e] = pv;
       }
       const bf16x8 pb = to_p(pf, ls);
@@ -480,7 +526,7 @@ __device__ __forceinline__ void swa_stream_body(const SArgs& p, const float sini
       const int ln = opaque(lane);
       const int nn = ln & 15, gg = ln >> 4;
       f32x4 sacc[2];
-      scores(kb, qreg, sacc);
+      scores(kb, qreg, sacc, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
       // key - query for value e: 32 kb + 16 (e / 4) + 4 g + e % 4 - q
       const int rel = kStep * kb + 4 * gg - (q_lo + nn);
       float sv[8];
@@ -549,7 +595,7 @@ __device__ __forceinline__ void swa_stream_body(const SArgs& p, const float sini
     u32x2 vr[2];
     load_k(t, kr);
     load_v(t, vr);
-    make_trig(t);
+    make_trig_direct(t);
     stage_k(kr, t);
     __syncthreads();
     transform_k(t);
@@ -559,7 +605,8 @@ __device__ __forceinline__ void swa_stream_body(const SArgs& p, const float sini
   u32x4 kr;
   u32x2 vr[2];
   load_k(s_begin + 1, kr);
-  make_trig(s_begin + 1);
+  make_trig_direct(s_begin + 1);
+  make_base(s_begin + 2);
   stage_k(kr, s_begin + 1);
   // the loads the first step consumes, issued in the order the steady state issues them
   // (Q, V, K, then G), so that the waits at the loop head are the same on both entries
@@ -589,8 +636,12 @@ __device__ __forceinline__ void swa_stream_body(const SArgs& p, const float sini
     load_k(s + 3, kr);
     transform_k(s + 1);
     make_trig(s + 2);
+    make_base(s + 3);
     if (STATIC && W == kMaxWindow && s >= kNB - 1) {
-      blocks_full(s, qreg);
+      if (ph)
+        blocks_full(s, qreg, std::integral_constant<int, 1>{});
+      else
+        blocks_full(s, qreg, std::integral_constant<int, 0>{});
     } else {
       reset_acc();
       blocks(s, qreg);
@@ -623,6 +674,12 @@ __global__ __launch_bounds__(kThreads, 1) void swa_stream_kernel(const SArgs p) 
     sFr[32 + tid] = p.fr.lo[tid];
   }
   __syncthreads();
+  for (int e = tid; e < kStep * kRH; e += kThreads) {
+    const int pl = e / kRH, j = e - pl * kRH;
+    float c, s;
+    rope_cos_sin(pl, sFr[j], sFr[32 + j], c, s);
+    ((float2*)(smem + kOffRot))[pl * kRHP + j] = make_float2(c, s);
+  }
   // |s| <= d * max|wq * qscale| * max|wk| after RMSNorm (2% margin for bf16 operands).
   float wqm = 0.f, wkm = 0.f;
   for (int c = lane; c < kD; c += 64) {
