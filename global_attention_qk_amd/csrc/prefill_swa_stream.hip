@@ -165,6 +165,34 @@ __device__ __forceinline__ float bf16_word(uint32_t w, int half) {
   return half ? bf16_hi_to_f32(w) : bf16_lo_to_f32(w);
 }
 
+// Slot stream of the fast path's five blocks for the waves holding positions 16 PH .. of
+// a step: one MFMA per slot, phases S(b) (scores of block b, 4 slots per 16-key half
+// computed) and PV(b) (8 slots) in the order S0 S1 PV0 S2 PV1 S3 PV2 S4 PV3 PV4; the
+// softmax of block b runs under phase kSmPhase[b] (after S(b), before PV(b)).
+template <int PH>
+struct FullSched {
+  static constexpr int h0(int b) { return (b == 0 && PH == 1) ? 1 : 0; }          // band edge
+  static constexpr int h1(int b) { return (b == kNB - 1 && PH == 0) ? 0 : 1; }    // diagonal
+  static constexpr int kPhases = 2 * kNB;
+  static constexpr int kind(int ph) { return (ph == 0 || ph == 1 || ph == 3 || ph == 5 || ph == 7) ? 0 : 1; }
+  static constexpr int blk(int ph) {
+    constexpr int b[kPhases] = {0, 1, 0, 2, 1, 3, 2, 4, 3, 4};
+    return b[ph];
+  }
+  static constexpr int sm_phase(int b) {
+    constexpr int q[kNB] = {1, 3, 5, 7, 8};
+    return q[b];
+  }
+  static constexpr int len(int ph) { return kind(ph) ? 8 : 4 * (h1(blk(ph)) - h0(blk(ph)) + 1); }
+  static constexpr int first(int ph) { return ph == 0 ? 0 : first(ph - 1) + len(ph - 1); }
+  static constexpr int kSlots = first(kPhases - 1) + len(kPhases - 1);
+  static constexpr int phase_of(int u) {
+    int ph = 0;
+    while (ph + 1 < kPhases && first(ph + 1) <= u) ++ph;
+    return ph;
+  }
+};
+
 // The stream of one workgroup; `sinit` starts every score accumulator: -B for the static
 // shift (so p <= 1), 0 for the online max. The norm weights and RoPE frequencies are in
 // LDS already.
@@ -472,49 +500,90 @@ __device__ __forceinline__ void swa_stream_body(const SArgs& p, const float sini
     return v;
   };
 
-  // Fast path (128-key window, static shift, away from position 0): the five blocks
-  // unrolled, specialised on which 16 positions of the step the wave holds (PH); masks
-  // only on the band-edge block (visible: keys above the query's offset in its block) and
-  // the diagonal block (keys at or below it), whose 16-key half on the far side of the
-  // wave's queries is not computed at all; the first block starts the accumulators from
-  // zero.
+  // Fast path (128-key window, static shift, away from position 0): the five blocks as
+  // one compile-time stream of MFMA slots (FullSched), specialised on which 16 positions
+  // of the step the wave holds (PH). Each slot issues one product, reads the LDS operand
+  // of the slot two ahead, and carries a piece of the softmax of the block before, so
+  // that neither the operand reads nor the products' results are waited for right away.
+  // Masks only on the band-edge block (visible: keys above the query's offset in its
+  // block) and the diagonal block (keys at or below it), whose 16-key half on the far
+  // side of the wave's queries is not computed at all; the first block starts the
+  // accumulators from zero.
   auto blocks_full = [&](int s, const bf16x8 (&qreg)[4], auto ph_tag) {
     constexpr int PH = decltype(ph_tag)::value;
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
+    using FS = FullSched<PH>;
+    constexpr int NS = FS::kSlots;
     const int ln = lane;
     const int nn = ln & 15, gg = ln >> 4;
     const int qo = 16 * PH + nn;   // query offset within the step's 32 positions
-    float ls = 0.f;
+    // per-lane operand offsets of a block (ring-slot base added per block)
+    const char* kbase0 = smem + kOffK;
+    const char* vbase0 = smem + kOffV;
+    int kslot[kNB];
 #pragma unroll
-    for (int jb = 0; jb < kNB; ++jb) {
-      const int kb = s - (kNB - 1) + jb;
-      // 16-key halves: the band-edge block's lower half lies wholly below queries 16..31
-      // (masked), the diagonal block's upper half wholly above queries 0..15 (masked);
-      // the other half of those blocks straddles the queries and takes the mask
-      const bool edge = jb == 0, diag = jb == kNB - 1;
-      f32x4 sacc[2];
-      if (edge && PH == 1) scores(kb, qreg, sacc, I1{}, I1{});
-      else if (diag && PH == 0) scores(kb, qreg, sacc, I0{}, I0{});
-      else scores(kb, qreg, sacc, I0{}, I1{});
-      float pf[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int kh = e >> 2, r = e & 3;
-        const bool skipped = (edge && PH == 1 && kh == 0) || (diag && PH == 0 && kh == 1);
-        if (skipped) {
-          pf[e] = 0.f;
-          continue;
-        }
-        float pv = fast_exp2(sacc[kh][r]);
-        const bool below = 16 * kh + 4 * gg + r <= qo;
-        if (edge && kh == PH) pv = below ? 0.f : pv;
-        if (diag && kh == PH) pv = below ? pv : 0.f;
-        pf[e] = pv;
+    for (int b = 0; b < kNB; ++b) kslot[b] = ring_slot(s - (kNB - 1) + b);
+    auto read_op = [&](auto uc) -> bf16x8 {
+      constexpr int u = decltype(uc)::value;
+      constexpr int ph = FS::phase_of(u), i = u - FS::first(ph), b = FS::blk(ph);
+      if constexpr (FS::kind(ph) == 0) {
+        constexpr int kh = FS::h0(b) + i / 4, ks = i % 4;
+        return *(const bf16x8*)(kbase0 + kslot[b] * kKBlkB + krow_off(16 * kh + nn, 4 * gg + ks));
+      } else {
+        return *(const bf16x8*)(vbase0 + kslot[b] * kVBlkB + vblk_off(16 * i + nn, gg));
       }
-      const bf16x8 pb = to_p(pf, ls);
-      pv_block(kb, pb, jb == 0);
-    }
+    };
+    f32x4 sacc[kNB][2];
+    float pf[kNB][8];
+    bf16x8 pb[kNB];
+    bf16x8 ops[NS];
+    float ls = 0.f;
+    ops[0] = read_op(std::integral_constant<int, 0>{});
+    if constexpr (NS > 1) ops[1] = read_op(std::integral_constant<int, 1>{});
+    static_for<NS>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      constexpr int ph = FS::phase_of(u), i = u - FS::first(ph), b = FS::blk(ph);
+      if constexpr (u + 2 < NS) ops[u + 2] = read_op(std::integral_constant<int, u + 2>{});
+      if constexpr (FS::kind(ph) == 0) {
+        constexpr int kh = FS::h0(b) + i / 4, ks = i % 4;
+        if constexpr (ks == 0) sacc[b][kh] = (f32x4){sinit, sinit, sinit, sinit};
+        sacc[b][kh] = mfma16(ops[u], qreg[ks], sacc[b][kh]);
+      } else {
+        oacc[i] = mfma16(ops[u], pb[b], b == 0 ? (f32x4){0.f, 0.f, 0.f, 0.f} : oacc[i]);
+      }
+      // softmax piece of block sb under this phase: its computed values spread evenly
+      // over the phase's slots, each pair converted (and summed) after its second value
+      static_for<kNB>([&](auto sbc) {
+        constexpr int sb = decltype(sbc)::value;
+        if constexpr (FS::sm_phase(sb) == ph) {
+          constexpr int e0 = 4 * FS::h0(sb), nv = 4 * (FS::h1(sb) - FS::h0(sb) + 1);
+          constexpr int L = FS::len(ph);
+          static_for<nv>([&](auto vc) {
+            constexpr int v = decltype(vc)::value;
+            if constexpr (v * L / nv == i) {
+              constexpr int e = e0 + v, kh = e >> 2, r = e & 3;
+              float x = fast_exp2(sacc[sb][kh][r]);
+              const bool below = 16 * kh + 4 * gg + r <= qo;
+              if constexpr (sb == 0 && kh == PH) x = below ? 0.f : x;
+              if constexpr (sb == kNB - 1 && kh == PH) x = below ? x : 0.f;
+              pf[sb][e] = x;
+              if constexpr (e & 1) {
+                const bf16x2 pr = {(bf16)pf[sb][e - 1], (bf16)x};
+                pb[sb][e - 1] = pr[0];
+                pb[sb][e] = pr[1];
+                ls = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2, ls, false);
+              }
+              if constexpr (v == 0) {
+                // values of skipped halves
+#pragma unroll
+                for (int z = 0; z < 8; ++z)
+                  if (z < e0 || z >= e0 + nv) pb[sb][z] = (bf16)0.f;
+              }
+            }
+          });
+        }
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
     l_run = ls;
   };
   // General path: any window <= 128, blocks before position 0, and the online variant.
