@@ -207,10 +207,10 @@ __device__ __forceinline__ void transform_row(const bf16* raw, bf16* dst, const 
   }
 }
 
-// One query tile (blockIdx-independent: `lin` names the tile).
-// `sinit` starts every score accumulator: -B (the static shift) or 0 (online variant).
-template <int D, bool SWA, bool KPRE, bool STATIC, int NW>
-__device__ __forceinline__ void prefill_tile(const KArgs& p, const int lin, const float sinit) {
+// One query tile (blockIdx-independent: `lin` names the tile). Below, `sinit` starts every
+// score accumulator: -B (the static shift) or 0 (online variant).
+template <int D, bool SWA, bool KPRE, int NW>
+__device__ __forceinline__ void prefill_tile(const KArgs& p, const int lin) {
   using S = Smem<D>;
   constexpr int kThreads = NW * 64;
   constexpr int QB = kRows / 32 / NW;  // 32-row query blocks per wave
@@ -239,16 +239,20 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p, const int lin, cons
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  for (int i = tid; i < D; i += kThreads) {
-    sWq[i] = p.wq[i];
-    sWk[i] = p.wk[i];
+  // The norm weights and RoPE steps are loaded first and stored to LDS only after the Q
+  // tile's loads are issued below, so that both travel in one memory round trip (loads
+  // complete in issue order: storing the weights waits for them alone).
+  static_assert(kThreads >= D && kThreads >= kMaxHalfMfma, "one weight per thread");
+  float wq_l = 0.f, wk_l = 0.f, fr_hi = 0.f, fr_lo = 0.f;
+  if (tid < D) {
+    wq_l = p.wq[tid];
+    wk_l = p.wk[tid];
   }
   // (a lane-dependent index into the kernel arguments would be a memory load per use)
-  for (int i = tid; i < kMaxHalfMfma; i += kThreads) {
-    sFr[i] = p.fr.hi[i];
-    sFr[kMaxHalfMfma + i] = p.fr.lo[i];
+  if (tid < kMaxHalfMfma) {
+    fr_hi = p.fr.hi[tid];
+    fr_lo = p.fr.lo[tid];
   }
-  __syncthreads();
 
   // Heavy query tiles first (global layers). Workgroup i runs on XCD i % 8 (round-robin
   // dispatch); when the (batch, kv-head) pairs divide evenly, each XCD takes its pairs one
@@ -290,15 +294,15 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p, const int lin, cons
   // dc = t % DC (kThreads is a multiple of DC) of rows qrow[it], so its 8 weights and the
   // RoPE partners of its 8 dims are fixed; the DC lanes holding one row sum its squares
   // with shuffles. All loads are issued before the first LDS write.
+  constexpr int QIT = kRows * DC / kThreads;
+  static_assert(QIT * kThreads == kRows * DC && kThreads % DC == 0, "Q chunks per thread");
+  u32x4 qv[QIT];
+  int qrow[QIT], qpi[QIT];
   {
-    constexpr int QIT = kRows * DC / kThreads;
-    static_assert(QIT * kThreads == kRows * DC && kThreads % DC == 0, "Q chunks per thread");
     const int g = p.group;
     const int chunks_per_pos = g * DC;
     const int dc = tid % DC;
     const bf16* qbase = p.q + (seq0 * p.Hq + (size_t)kvh * g) * D;
-    u32x4 qv[QIT];
-    int qrow[QIT], qpi[QIT];
 #pragma unroll
     for (int it = 0; it < QIT; ++it) {
       const int c = tid + it * kThreads;
@@ -309,6 +313,33 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p, const int lin, cons
       qrow[it] = hg * p.bmp + pi;
       qpi[it] = pi;
     }
+  }
+  if (tid < D) {
+    sWq[tid] = wq_l;
+    sWk[tid] = wk_l;
+  }
+  if (tid < kMaxHalfMfma) {
+    sFr[tid] = fr_hi;
+    sFr[kMaxHalfMfma + tid] = fr_lo;
+  }
+  __syncthreads();   // weights and RoPE steps are in LDS
+  // Softmax form: after RMSNorm every score obeys |s| <= B = |qscale| d max|wq| max|wk|
+  // (2 % margin for the bf16 operands). The bound is the same for every workgroup, so they
+  // all take the same form: the static shift (score accumulators start at -B, p <= 1)
+  // while B <= kStaticShiftMax, else the online max.
+  float bound;
+  {
+    float wqm = 0.f, wkm = 0.f;
+    for (int c = lane; c < D; c += 64) {
+      wqm = fmaxf(wqm, fabsf(sWq[c]));
+      wkm = fmaxf(wkm, fabsf(sWk[c]));
+    }
+    bound = fabsf(p.qscale) * (float)D * wave_max(wqm) * wave_max(wkm) * 1.02f;
+  }
+  auto rest = [&](auto static_tag, const float sinit) {
+  constexpr bool STATIC = decltype(static_tag)::value;
+  {
+    const int dc = tid % DC;
     for (int e = tid; e < p.bmp * half; e += kThreads) {
       const int pi = e / half, j = e - pi * half;
       float c, s;
@@ -1076,34 +1107,21 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p, const int lin, cons
       *(u32x4*)(p.out + ((seq0 + pos) * p.Hq + h) * D + dc * 8) = v;
     }
   }
+  };
+  if (bound <= kStaticShiftMax)
+    rest(std::true_type{}, -bound);
+  else
+    rest(std::false_type{}, 0.f);
+
 }
 
 // Score bound (uniform over the grid): after RMSNorm, ||q^|| <= sqrt(d) max|wq| and
 // ||k^|| <= sqrt(d) max|wk|, so every log2-domain score obeys
 // |s| <= qscale * d * max|wq| * max|wk| (2% margin for the bf16 rounding of q~ and k~).
-template <int D>
-__device__ __forceinline__ float score_bound(const KArgs& p) {
-  const int lane = threadIdx.x & 63;
-  float wqm = 0.f, wkm = 0.f;
-  for (int c = lane; c < D; c += 64) {
-    wqm = fmaxf(wqm, fabsf(p.wq[c]));
-    wkm = fmaxf(wkm, fabsf(p.wk[c]));
-  }
-  wqm = wave_max(wqm);
-  wkm = wave_max(wkm);
-  return fabsf(p.qscale) * (float)D * wqm * wkm * 1.02f;
-}
-
-// One launch, one query tile per workgroup: the bound is the same for every workgroup, so
-// they all take the same variant (static shift when the bound allows it, else the online
-// max).
+// One launch, one query tile per workgroup (the softmax form is chosen inside).
 template <int D, bool SWA, bool KPRE, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p) {
-  const float bound = score_bound<D>(p);
-  if (bound <= kStaticShiftMax)
-    prefill_tile<D, SWA, KPRE, true, NW>(p, blockIdx.x, -bound);
-  else
-    prefill_tile<D, SWA, KPRE, false, NW>(p, blockIdx.x, 0.f);
+  prefill_tile<D, SWA, KPRE, NW>(p, blockIdx.x);
 }
 
 template <int D, bool SWA, bool KPRE, int NW = kWavesPerBlock>

@@ -41,7 +41,7 @@ def _kernels(asm, name):
             body = []
             for l2 in lines[i + 1:]:
                 s = l2.strip()
-                if "s_endpgm" in s:
+                if s.startswith(".Lfunc_end"):   # the kernel's last instruction is above
                     break
                 if s and not s.startswith(";") and not s.startswith("."):
                     body.append(s)
@@ -82,7 +82,7 @@ def _early_reads(body):
                 tgt = s.split()[1]
                 if tgt in labels:
                     succ.append(labels[tgt])
-            if op != "s_branch":
+            if op not in ("s_branch", "s_endpgm"):   # an early exit ends its path
                 succ.append(i + 1)
             for j in succ:
                 old = entry[j]
