@@ -6,7 +6,8 @@
 // (the last `window` tokens including the query for SWA, the whole prefix for global),
 // times V, then the elementwise sigmoid gate for SWA.
 //
-// Work decomposition (one workgroup = 256 query rows):
+// Work decomposition (one workgroup = 256 query rows at a time; global layers of dense
+// batches launch one workgroup per CU, each walking several query tiles in turn):
 //   * The rows are all g = Hq/Hkv query heads of one KV head at 256/g consecutive
 //     positions, so every K/V tile staged in LDS serves the whole head group.
 //   * Global layers with K~ / V tiles from the workspace: 4 wave64s, one per SIMD, each
@@ -69,6 +70,14 @@ constexpr int kDmaBufs = ZG_DMA_BUFS;
 #define ZG_DMA_PHASE 3
 #endif
 constexpr int kDmaPhase = ZG_DMA_PHASE;
+// Persistent global launches (one workgroup per CU walking several query tiles).
+#ifndef ZG_PERSISTENT
+#define ZG_PERSISTENT 1
+#endif
+// Load the next query tile's Q rows under the current tile's epilogue.
+#ifndef ZG_PREFETCH_Q
+#define ZG_PREFETCH_Q 1
+#endif
 constexpr int kBN = 64;           // keys per tile
 constexpr int kXcds = 8;          // accelerator complex dies (one L2 each)
 constexpr int kMaxHalfMfma = 32;  // rotary_dim <= 64 on this path
@@ -210,7 +219,7 @@ __device__ __forceinline__ void transform_row(const bf16* raw, bf16* dst, const 
 // One query tile (blockIdx-independent: `lin` names the tile). Below, `sinit` starts every
 // score accumulator: -B (the static shift) or 0 (online variant).
 template <int D, bool SWA, bool KPRE, int NW>
-__device__ __forceinline__ void prefill_tile(const KArgs& p, const int lin) {
+__device__ __forceinline__ void prefill_tile(const KArgs& p) {
   using S = Smem<D>;
   constexpr int kThreads = NW * 64;
   constexpr int QB = kRows / 32 / NW;  // 32-row query blocks per wave
@@ -254,66 +263,94 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p, const int lin) {
     fr_lo = p.fr.lo[tid];
   }
 
-  // Heavy query tiles first (global layers). Workgroup i runs on XCD i % 8 (round-robin
-  // dispatch); when the (batch, kv-head) pairs divide evenly, each XCD takes its pairs one
-  // after another, so that its L2 holds the K~ / V tiles of one or two pairs at a time.
-  int hb, tile_rank;
-  if (p.n_hb % kXcds == 0) {
-    const int x = lin % kXcds, slot = lin / kXcds;
-    hb = (slot / p.n_qtiles) * kXcds + x;
-    tile_rank = slot % p.n_qtiles;
-  } else {
-    hb = lin % p.n_hb;
-    tile_rank = lin / p.n_hb;
-  }
-  const int b = hb / p.Hkv;        // batch element, or document of a packed batch
-  const int kvh = hb % p.Hkv;
-  // Sequence of this workgroup: `seq0` is its first row in the [B*T] (or packed) token
-  // order, T its length; K~ rows and V tiles start at kt_row0 / vt_tile0 of the workspace.
-  int T = p.T, n_qtiles = p.n_qtiles;
-  size_t seq0 = (size_t)b * p.T;
-  size_t kt_row0 = ((size_t)b * p.Hkv + kvh) * p.T;
-  size_t vt_tile0 = ((size_t)b * p.Hkv + kvh) * ((p.T + kBN - 1) / kBN);
-  if (p.cu) {
-    int start, len;
-    doc_range(p.cu, b, p.T, p.max_len, start, len);
-    T = len;
-    n_qtiles = (len + p.bmp - 1) / p.bmp;
-    if (tile_rank >= n_qtiles) return;   // the whole workgroup, before any later barrier
-    seq0 = start;
-    kt_row0 = (size_t)kvh * p.T + start;
-    vt_tile0 = (size_t)kvh * p.vt_slots + doc_tile_base(start, b);
-  }
-  const int qt = SWA ? tile_rank : (n_qtiles - 1 - tile_rank);
-  const int i0 = qt * p.bmp;
+  // Query tiles of the workgroup, heaviest first (global layers). A launch of n_blocks
+  // workgroups gives each one tile; a persistent launch (fewer workgroups, dense batches)
+  // deals the tiles out in snake order: round k hands the next gridDim.x tiles of the
+  // list to the workgroups forwards on even rounds and backwards on odd ones, so that a
+  // heavy tile is paired with a light one and every workgroup gets about the same number
+  // of key tiles. Workgroup i runs on XCD i % 8 (round-robin dispatch); when the
+  // (batch, kv-head) pairs divide by 8, each XCD takes its pairs one after another, so
+  // that its L2 holds the K~ / V tiles of one or two pairs at a time.
+  auto item_lin = [&](int k) -> int {
+    const int G = gridDim.x, j = blockIdx.x;
+    if (p.n_hb % kXcds == 0) {
+      const int per = G / kXcds, x = j % kXcds, w = j / kXcds;
+      return (k * per + ((k & 1) ? per - 1 - w : w)) * kXcds + x;
+    }
+    return k * G + ((k & 1) ? G - 1 - j : j);
+  };
+  // One query tile: sequence `seq0` (its first row in the [B*T] or packed token order) of
+  // length T, KV head kvh, first position i0; K~ rows and V tiles start at kt_row0 /
+  // vt_tile0 of the workspace. `skip`: past the end of a shorter packed document.
+  struct Item {
+    int b, kvh, T, i0;
+    size_t seq0, kt_row0, vt_tile0;
+    bool skip;
+  };
+  auto decode = [&](int lin) -> Item {
+    int hb, tile_rank;
+    if (p.n_hb % kXcds == 0) {
+      const int x = lin % kXcds, slot = lin / kXcds;
+      hb = (slot / p.n_qtiles) * kXcds + x;
+      tile_rank = slot % p.n_qtiles;
+    } else {
+      hb = lin % p.n_hb;
+      tile_rank = lin / p.n_hb;
+    }
+    Item it;
+    it.b = hb / p.Hkv;        // batch element, or document of a packed batch
+    it.kvh = hb % p.Hkv;
+    it.T = p.T;
+    int n_qtiles = p.n_qtiles;
+    it.seq0 = (size_t)it.b * p.T;
+    it.kt_row0 = ((size_t)it.b * p.Hkv + it.kvh) * p.T;
+    it.vt_tile0 = ((size_t)it.b * p.Hkv + it.kvh) * ((p.T + kBN - 1) / kBN);
+    it.skip = false;
+    if (p.cu) {
+      int start, len;
+      doc_range(p.cu, it.b, p.T, p.max_len, start, len);
+      it.T = len;
+      n_qtiles = (len + p.bmp - 1) / p.bmp;
+      it.skip = tile_rank >= n_qtiles;
+      it.seq0 = start;
+      it.kt_row0 = (size_t)it.kvh * p.T + start;
+      it.vt_tile0 = (size_t)it.kvh * p.vt_slots + doc_tile_base(start, it.b);
+    }
+    const int qt = SWA ? tile_rank : (n_qtiles - 1 - tile_rank);
+    it.i0 = qt * p.bmp;
+    return it;
+  };
   const int half = p.rdim >> 1;
   const int bpp = p.bmp >> 5;  // 32-row blocks per head in the tile
 
   // ---- Phase 1: Q tile -> LDS, QK-norm + RoPE + scale in place ----------------------
   // The tile is bmp * group = kRows rows of DC 16-byte chunks. Thread t always holds chunk
-  // dc = t % DC (kThreads is a multiple of DC) of rows qrow[it], so its 8 weights and the
+  // dc = t % DC (kThreads is a multiple of DC) of rows q_row(i), so its 8 weights and the
   // RoPE partners of its 8 dims are fixed; the DC lanes holding one row sum its squares
   // with shuffles. All loads are issued before the first LDS write.
   constexpr int QIT = kRows * DC / kThreads;
   static_assert(QIT * kThreads == kRows * DC && kThreads % DC == 0, "Q chunks per thread");
+  auto q_pi = [&](int i, int t) { return (t + i * kThreads) / (p.group * DC); };
+  auto q_row = [&](int i, int t) {
+    const int c = t + i * kThreads, cpp = p.group * DC, pi = c / cpp;
+    return (c - pi * cpp) / DC * p.bmp + pi;
+  };
   u32x4 qv[QIT];
-  int qrow[QIT], qpi[QIT];
-  {
-    const int g = p.group;
-    const int chunks_per_pos = g * DC;
+  auto load_q = [&](const Item& it, const int tid) {
     const int dc = tid % DC;
-    const bf16* qbase = p.q + (seq0 * p.Hq + (size_t)kvh * g) * D;
+    const bf16* qbase = p.q + (it.seq0 * p.Hq + (size_t)it.kvh * p.group) * D;
 #pragma unroll
-    for (int it = 0; it < QIT; ++it) {
-      const int c = tid + it * kThreads;
-      const int pi = c / chunks_per_pos;
-      const int hg = (c - pi * chunks_per_pos) / DC;
-      const int pos = min(i0 + pi, T - 1);   // rows past the end read a valid row, then zero
-      qv[it] = *(const u32x4*)(qbase + (size_t)pos * p.Hq * D + hg * D + dc * 8);
-      qrow[it] = hg * p.bmp + pi;
-      qpi[it] = pi;
+    for (int i = 0; i < QIT; ++i) {
+      const int c = tid + i * kThreads, cpp = p.group * DC;
+      const int pi = c / cpp, hg = (c - pi * cpp) / DC;
+      const int pos = min(it.i0 + pi, it.T - 1);   // rows past the end read a valid row, then zero
+      qv[i] = *(const u32x4*)(qbase + (size_t)pos * p.Hq * D + hg * D + dc * 8);
     }
-  }
+  };
+  int k_item = 0, cur_lin = item_lin(0);
+  Item cur = decode(cur_lin);
+  if (cur.skip) return;   // the whole workgroup, before any barrier
+  load_q(cur, tid);
   if (tid < D) {
     sWq[tid] = wq_l;
     sWk[tid] = wk_l;
@@ -338,6 +375,19 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p, const int lin) {
   }
   auto rest = [&](auto static_tag, const float sinit) {
   constexpr bool STATIC = decltype(static_tag)::value;
+  for (;;) {
+  // Per-lane values are re-derived for every tile from a copy of the thread index that the
+  // compiler cannot see through, so that nothing computed from them is hoisted out of this
+  // loop and held in registers across the key loop.
+  int tid_v = threadIdx.x;
+  asm volatile("" : "+v"(tid_v));
+  const int tid = tid_v, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int b = cur.b, kvh = cur.kvh, T = cur.T, i0 = cur.i0;
+  const size_t seq0 = cur.seq0, kt_row0 = cur.kt_row0, vt_tile0 = cur.vt_tile0;
+  if (k_item > 0) __syncthreads();   // every wave's output rows have left the Q region
+#if !ZG_PREFETCH_Q
+  if (k_item > 0) load_q(cur, tid);
+#endif
   {
     const int dc = tid % DC;
     for (int e = tid; e < p.bmp * half; e += kThreads) {
@@ -349,8 +399,8 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p, const int lin) {
 #pragma unroll
     for (int it = 0; it < QIT; ++it) {
       const u32x4 zero = {0u, 0u, 0u, 0u};
-      if (i0 + qpi[it] >= T) qv[it] = zero;
-      *(u32x4*)(sQ + qrow[it] * RW + dc * 8) = qv[it];
+      if (i0 + q_pi(it, tid) >= T) qv[it] = zero;
+      *(u32x4*)(sQ + q_row(it, tid) * RW + dc * 8) = qv[it];
     }
     if (p.rdim == 2 * kModelHalf<D>) {
       // The model's rotary dim: one thread per tile row. The row comes from LDS into
@@ -442,8 +492,8 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p, const int lin) {
         for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
         ss = group_sum<DC>(ss);
         const float rs = __builtin_amdgcn_rsqf(ss * (1.0f / D) + p.eps) * p.qscale;
-        const bf16* row = sQ + qrow[it] * RW;
-        const float2* trig = sQtrig + qpi[it] * kQTrigStride;
+        const bf16* row = sQ + q_row(it, tid) * RW;
+        const float2* trig = sQtrig + q_pi(it, tid) * kQTrigStride;
         float y[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -461,7 +511,7 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p, const int lin) {
       }
       __syncthreads();   // every partner read of the raw rows is done
 #pragma unroll
-      for (int it = 0; it < QIT; ++it) *(u32x4*)(sQ + qrow[it] * RW + dc * 8) = res[it];
+      for (int it = 0; it < QIT; ++it) *(u32x4*)(sQ + q_row(it, tid) * RW + dc * 8) = res[it];
 
     }
   }
@@ -1049,6 +1099,14 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p, const int lin) {
     for (; i < n_tiles; ++i) step(i, std::integral_constant<bool, true>{});
   }
 
+  // The next query tile's Q rows load under this tile's epilogue (persistent launch).
+  const int nlin = item_lin(k_item + 1);
+  const bool more = nlin < p.n_blocks;
+  const Item nxt = decode(more ? nlin : cur_lin);
+#if ZG_PREFETCH_Q
+  if (more) load_q(nxt, tid);
+#endif
+
   // ---- Epilogue: O = acc / l (* sigmoid(G)), bf16 store ------------------------------
   // Each wave stages its QB * 32 rows in its own slice of the (now idle) Q region, then
   // stores whole 16-byte chunks of contiguous rows (a lane of the accumulator layout
@@ -1107,6 +1165,11 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p, const int lin) {
       *(u32x4*)(p.out + ((seq0 + pos) * p.Hq + h) * D + dc * 8) = v;
     }
   }
+  if (!more) break;
+  cur = nxt;
+  cur_lin = nlin;
+  ++k_item;
+  }
   };
   if (bound <= kStaticShiftMax)
     rest(std::true_type{}, -bound);
@@ -1118,20 +1181,21 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p, const int lin) {
 // Score bound (uniform over the grid): after RMSNorm, ||q^|| <= sqrt(d) max|wq| and
 // ||k^|| <= sqrt(d) max|wk|, so every log2-domain score obeys
 // |s| <= qscale * d * max|wq| * max|wk| (2% margin for the bf16 rounding of q~ and k~).
-// One launch, one query tile per workgroup (the softmax form is chosen inside).
+// One launch: a query tile per workgroup, or several per workgroup when the grid is
+// smaller than the tile count (the softmax form is chosen inside).
 template <int D, bool SWA, bool KPRE, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(const KArgs p) {
-  prefill_tile<D, SWA, KPRE, NW>(p, blockIdx.x);
+  prefill_tile<D, SWA, KPRE, NW>(p);
 }
 
 template <int D, bool SWA, bool KPRE, int NW = kWavesPerBlock>
-hipError_t launch_t(const KArgs& ka, int n_blocks, hipStream_t s) {
+hipError_t launch_t(const KArgs& ka, int grid, hipStream_t s) {
   constexpr int smem = Smem<D>::kTotal;
   constexpr int kThreads = NW * 64;
   auto kern = prefill_bf16_kernel<D, SWA, KPRE, NW>;
   hipError_t e = ensure_dynamic_smem((const void*)kern, smem);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(n_blocks), dim3(kThreads), smem, s, ka);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), smem, s, ka);
   return hipGetLastError();
 }
 
@@ -1295,14 +1359,26 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
   ka.lse = (a.swa || a.cu) ? nullptr : a.lse;
   if (swa_stream_supported(a)) return launch_swa_stream(a, s);
   const bool kpre = (a.kt != nullptr);
-  if (a.d == 128) {
-    if (a.swa) return launch_t<128, true, false>(ka, n_blocks, s);
-    return kpre ? launch_t<128, false, true, ZG_GLOBAL_WAVES>(ka, n_blocks, s)
-                : launch_t<128, false, false>(ka, n_blocks, s);
+  // Global layers of dense batches with K~ / V tiles from the workspace run persistent:
+  // one workgroup per CU (a multiple of 8 when the tiles are dealt out per XCD), each
+  // walking its share of the query tiles, so that a tile's Q load overlaps the previous
+  // tile's epilogue. Everything else: one workgroup per query tile.
+  int grid = n_blocks;
+  if (ZG_PERSISTENT && kpre && !a.swa && a.cu == nullptr) {
+    int cus = 0;
+    hipError_t e = device_cu_count(&cus);
+    if (e != hipSuccess) return e;
+    if (ka.n_hb % kXcds == 0) cus -= cus % kXcds;
+    if (cus > 0 && cus < n_blocks) grid = cus;
   }
-  if (a.swa) return launch_t<64, true, false>(ka, n_blocks, s);
-  return kpre ? launch_t<64, false, true, ZG_GLOBAL_WAVES>(ka, n_blocks, s)
-              : launch_t<64, false, false>(ka, n_blocks, s);
+  if (a.d == 128) {
+    if (a.swa) return launch_t<128, true, false>(ka, grid, s);
+    return kpre ? launch_t<128, false, true, ZG_GLOBAL_WAVES>(ka, grid, s)
+                : launch_t<128, false, false>(ka, grid, s);
+  }
+  if (a.swa) return launch_t<64, true, false>(ka, grid, s);
+  return kpre ? launch_t<64, false, true, ZG_GLOBAL_WAVES>(ka, grid, s)
+              : launch_t<64, false, false>(ka, grid, s);
 }
 
 }  // namespace zg
