@@ -163,6 +163,15 @@ __device__ __forceinline__ void set_prio() {
   if (ZG_PREFILL_SETPRIO) __builtin_amdgcn_s_setprio(P);
 }
 
+// A barrier for LDS reuse: the workgroup's LDS accesses before it complete before any
+// after it, while global loads and stores stay in flight (__syncthreads also waits for
+// every store the wave has issued).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Keep a value in AGPRs from here on (so that loop-carried accumulators never take a
 // mixed register class).
 __device__ __forceinline__ void pin_agpr(f32x16& v) { asm volatile("" : "+a"(v)); }
@@ -242,25 +251,26 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p) {
   float* sWk = sWq + D;
   float* sFr = sWk + D;   // [0, 32): phase step heads, [32, 64): tails
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31;
-  const int hi = lane >> 5;
+  // Global layers with K~ from the workspace may walk several query tiles (persistent
+  // launch); the other forms always take one.
+  constexpr bool PERSIST = KPRE && !SWA;
+  const int tid0 = threadIdx.x;
+  const int lane0 = tid0 & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);
 
   // The norm weights and RoPE steps are loaded first and stored to LDS only after the Q
   // tile's loads are issued below, so that both travel in one memory round trip (loads
   // complete in issue order: storing the weights waits for them alone).
   static_assert(kThreads >= D && kThreads >= kMaxHalfMfma, "one weight per thread");
   float wq_l = 0.f, wk_l = 0.f, fr_hi = 0.f, fr_lo = 0.f;
-  if (tid < D) {
-    wq_l = p.wq[tid];
-    wk_l = p.wk[tid];
+  if (tid0 < D) {
+    wq_l = p.wq[tid0];
+    wk_l = p.wk[tid0];
   }
   // (a lane-dependent index into the kernel arguments would be a memory load per use)
-  if (tid < kMaxHalfMfma) {
-    fr_hi = p.fr.hi[tid];
-    fr_lo = p.fr.lo[tid];
+  if (tid0 < kMaxHalfMfma) {
+    fr_hi = p.fr.hi[tid0];
+    fr_lo = p.fr.lo[tid0];
   }
 
   // Query tiles of the workgroup, heaviest first (global layers). A launch of n_blocks
@@ -350,14 +360,14 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p) {
   int k_item = 0, cur_lin = item_lin(0);
   Item cur = decode(cur_lin);
   if (cur.skip) return;   // the whole workgroup, before any barrier
-  load_q(cur, tid);
-  if (tid < D) {
-    sWq[tid] = wq_l;
-    sWk[tid] = wk_l;
+  load_q(cur, tid0);
+  if (tid0 < D) {
+    sWq[tid0] = wq_l;
+    sWk[tid0] = wk_l;
   }
-  if (tid < kMaxHalfMfma) {
-    sFr[tid] = fr_hi;
-    sFr[kMaxHalfMfma + tid] = fr_lo;
+  if (tid0 < kMaxHalfMfma) {
+    sFr[tid0] = fr_hi;
+    sFr[kMaxHalfMfma + tid0] = fr_lo;
   }
   __syncthreads();   // weights and RoPE steps are in LDS
   // Softmax form: after RMSNorm every score obeys |s| <= B = |qscale| d max|wq| max|wk|
@@ -367,7 +377,7 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p) {
   float bound;
   {
     float wqm = 0.f, wkm = 0.f;
-    for (int c = lane; c < D; c += 64) {
+    for (int c = lane0; c < D; c += 64) {
       wqm = fmaxf(wqm, fabsf(sWq[c]));
       wkm = fmaxf(wkm, fabsf(sWk[c]));
     }
@@ -375,16 +385,16 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p) {
   }
   auto rest = [&](auto static_tag, const float sinit) {
   constexpr bool STATIC = decltype(static_tag)::value;
+  int tid_c = tid0;
   for (;;) {
-  // Per-lane values are re-derived for every tile from a copy of the thread index that the
-  // compiler cannot see through, so that nothing computed from them is hoisted out of this
-  // loop and held in registers across the key loop.
-  int tid_v = threadIdx.x;
-  asm volatile("" : "+v"(tid_v));
-  const int tid = tid_v, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  // Persistent: per-lane values are re-derived for every tile from the lane index read
+  // afresh (an assembly mbcnt the compiler cannot hoist), so that nothing computed from
+  // them is held in registers across the key loop.
+  if constexpr (PERSIST) asm volatile("" : "+v"(tid_c));
+  const int tid = tid_c, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int b = cur.b, kvh = cur.kvh, T = cur.T, i0 = cur.i0;
   const size_t seq0 = cur.seq0, kt_row0 = cur.kt_row0, vt_tile0 = cur.vt_tile0;
-  if (k_item > 0) __syncthreads();   // every wave's output rows have left the Q region
+  if (k_item > 0) lds_barrier();   // every wave's output rows have left the Q region
 #if !ZG_PREFETCH_Q
   if (k_item > 0) load_q(cur, tid);
 #endif
@@ -1101,7 +1111,7 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p) {
 
   // The next query tile's Q rows load under this tile's epilogue (persistent launch).
   const int nlin = item_lin(k_item + 1);
-  const bool more = nlin < p.n_blocks;
+  const bool more = PERSIST && nlin < p.n_blocks;
   const Item nxt = decode(more ? nlin : cur_lin);
 #if ZG_PREFETCH_Q
   if (more) load_q(nxt, tid);
