@@ -74,10 +74,6 @@ constexpr int kDmaPhase = ZG_DMA_PHASE;
 #ifndef ZG_PERSISTENT
 #define ZG_PERSISTENT 1
 #endif
-// Load the next query tile's Q rows under the current tile's epilogue.
-#ifndef ZG_PREFETCH_Q
-#define ZG_PREFETCH_Q 1
-#endif
 constexpr int kBN = 64;           // keys per tile
 constexpr int kXcds = 8;          // accelerator complex dies (one L2 each)
 constexpr int kMaxHalfMfma = 32;  // rotary_dim <= 64 on this path
@@ -387,17 +383,14 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p) {
   constexpr bool STATIC = decltype(static_tag)::value;
   int tid_c = tid0;
   for (;;) {
-  // Persistent: per-lane values are re-derived for every tile from the lane index read
-  // afresh (an assembly mbcnt the compiler cannot hoist), so that nothing computed from
-  // them is held in registers across the key loop.
+  // Persistent: the thread index passes through an empty assembly statement at the top
+  // of every tile, so that the compiler cannot hoist what it derives from it (offsets,
+  // row indices) out of this loop and hold it in registers across the key loop.
   if constexpr (PERSIST) asm volatile("" : "+v"(tid_c));
   const int tid = tid_c, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int b = cur.b, kvh = cur.kvh, T = cur.T, i0 = cur.i0;
   const size_t seq0 = cur.seq0, kt_row0 = cur.kt_row0, vt_tile0 = cur.vt_tile0;
   if (k_item > 0) lds_barrier();   // every wave's output rows have left the Q region
-#if !ZG_PREFETCH_Q
-  if (k_item > 0) load_q(cur, tid);
-#endif
   {
     const int dc = tid % DC;
     for (int e = tid; e < p.bmp * half; e += kThreads) {
@@ -1113,9 +1106,7 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p) {
   const int nlin = item_lin(k_item + 1);
   const bool more = PERSIST && nlin < p.n_blocks;
   const Item nxt = decode(more ? nlin : cur_lin);
-#if ZG_PREFETCH_Q
   if (more) load_q(nxt, tid);
-#endif
 
   // ---- Epilogue: O = acc / l (* sigmoid(G)), bf16 store ------------------------------
   // Each wave stages its QB * 32 rows in its own slice of the (now idle) Q region, then
