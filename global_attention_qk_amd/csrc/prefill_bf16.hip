@@ -106,7 +106,12 @@ struct Smem {
   static constexpr int kFr = 2 * kMaxHalfMfma * 4;  // RoPE phase steps (head, tail)
   static constexpr int kMain = kLoop > kDLoop ? kLoop : kDLoop;
   static constexpr int kUnion = (kQ + kQtrig) > kMain ? (kQ + kQtrig) : kMain;
-  static constexpr int kTotal = kUnion + kW + kFr;
+  // Persistent global path: RoPE of the in-tile offsets 0 .. kBN-1 (one table per
+  // workgroup) and of each tile's first position, combined by angle addition.
+  static constexpr int kOffT = kBN * kMaxHalfMfma * 8;
+  static constexpr int kBaseT = kMaxHalfMfma * 8;
+  static constexpr int kTotal = kUnion + kW + kFr + kOffT + kBaseT;
+  static_assert(kTotal <= 160 * 1024, "LDS budget of a CU");
 };
 
 struct KArgs {
@@ -246,6 +251,8 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p) {
   float* sWq = (float*)(smem + S::kUnion);
   float* sWk = sWq + D;
   float* sFr = sWk + D;   // [0, 32): phase step heads, [32, 64): tails
+  float2* sOffT = (float2*)(smem + S::kUnion + S::kW + S::kFr);  // [offset][pair]
+  float2* sBaseT = (float2*)((char*)sOffT + S::kOffT);           // [pair]
 
   // Global layers with K~ from the workspace may walk several query tiles (persistent
   // launch); the other forms always take one.
@@ -379,6 +386,19 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p) {
     }
     bound = fabsf(p.qscale) * (float)D * wave_max(wqm) * wave_max(wkm) * 1.02f;
   }
+  // Persistent launches with at most 64 positions per tile build each tile's RoPE table
+  // by angle addition: cos/sin(b + o) from the exact angles of the tile's first position
+  // b and of the offsets o = 0 .. 63 (the offsets once per workgroup), 4 FMAs per entry
+  // in place of a reduced sine and cosine.
+  const bool trig_add = PERSIST && p.bmp <= kBN;
+  if (trig_add) {
+    for (int e = tid0; e < p.bmp * half; e += kThreads) {
+      const int o = e / half, j = e - o * half;
+      float c, s;
+      rope_cos_sin(o, sFr[j], sFr[kMaxHalfMfma + j], c, s);
+      sOffT[o * kMaxHalfMfma + j] = make_float2(c, s);
+    }
+  }
   auto rest = [&](auto static_tag, const float sinit) {
   constexpr bool STATIC = decltype(static_tag)::value;
   int tid_c = tid0;
@@ -390,13 +410,28 @@ __device__ __forceinline__ void prefill_tile(const KArgs& p) {
   const int tid = tid_c, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int b = cur.b, kvh = cur.kvh, T = cur.T, i0 = cur.i0;
   const size_t seq0 = cur.seq0, kt_row0 = cur.kt_row0, vt_tile0 = cur.vt_tile0;
-  if (k_item > 0) lds_barrier();   // every wave's output rows have left the Q region
+  if (trig_add) {
+    if (tid < half) {
+      float c, s;
+      rope_cos_sin(p.pos_offset + i0, sFr[tid], sFr[kMaxHalfMfma + tid], c, s);
+      sBaseT[tid] = make_float2(c, s);
+    }
+    lds_barrier();   // the angle tables are in LDS; the output rows have left the Q region
+  } else if (k_item > 0) {
+    lds_barrier();   // every wave's output rows have left the Q region
+  }
   {
     const int dc = tid % DC;
     for (int e = tid; e < p.bmp * half; e += kThreads) {
       const int pi = e / half, j = e - pi * half;
       float c, s;
-      rope_cos_sin(p.pos_offset + i0 + pi, sFr[j], sFr[kMaxHalfMfma + j], c, s);
+      if (trig_add) {
+        const float2 b = sBaseT[j], o = sOffT[pi * kMaxHalfMfma + j];
+        c = __builtin_fmaf(b.x, o.x, -b.y * o.y);
+        s = __builtin_fmaf(b.y, o.x, b.x * o.y);
+      } else {
+        rope_cos_sin(p.pos_offset + i0 + pi, sFr[j], sFr[kMaxHalfMfma + j], c, s);
+      }
       sQtrig[pi * kQTrigStride + j] = make_float2(c, s);
     }
 #pragma unroll
